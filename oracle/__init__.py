@@ -1,0 +1,432 @@
+"""CPU ORACLE -- test infrastructure only.
+
+Plain, slow, obviously-correct CPU implementation of the residual-compression
+path (the C functions in ``oracle.c``, driven from here). Only ``tests/``, the
+smoke check and the benchmark's ``cpu_baseline`` leg may import it. It shares no
+code with the GPU library: the packed byte layout below is written out here
+independently of the library's own layout code.
+
+Method source: the paper-notes page "Accelerating Parallel Diffusion Model
+Serving with Residual Compression" (CompactFusion), sections Method / Overall
+framework, Key designs (Residual compression, Error feedback, Low-rank strategy
+for extreme compression, System co-design), Main experiment table and
+Limitations (warm-up). See ``oracle.c`` for the per-function citations and the
+readings taken where the page is silent.
+
+Parity status: every scheme is pinned by the CPU tests (closed forms, brute
+force, library routines, invariants); the low-rank factors themselves are
+compared by tolerance only (their bits are not fixed by any definition).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# Compile flags: IEEE single/double semantics, no contraction into FMA.
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math"]
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        lib.orc_bf16_bits.restype = ctypes.c_uint16
+        lib.orc_bf16_bits.argtypes = [ctypes.c_float]
+        lib.orc_bf16_round_array.argtypes = [i64, vp, vp]
+        lib.orc_residual.argtypes = [i64, vp, vp, vp]
+        lib.orc_ef_update.argtypes = [i64, vp, vp, vp, vp]
+        lib.orc_accumulate.argtypes = [i64, vp, vp]
+        lib.orc_ef_update_f64.argtypes = [i64, vp, vp, vp, vp]
+        lib.orc_accumulate_f64.argtypes = [i64, vp, vp]
+        lib.orc_q1_encode.argtypes = [i64, i32, vp, vp, vp]
+        lib.orc_q1_decode.argtypes = [i64, i32, vp, vp, vp]
+        lib.orc_q2_encode.argtypes = [i64, i32, vp, vp, vp, vp]
+        lib.orc_q2_decode.argtypes = [i64, i32, vp, vp, vp, vp]
+        lib.orc_nm_encode.argtypes = [i64, vp, vp, vp]
+        lib.orc_nm_decode.argtypes = [i64, vp, vp, vp]
+        lib.orc_lr_encode.restype = i32
+        lib.orc_lr_encode.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.orc_lr_decode.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+        lib.orc_lr_factors.restype = i32
+        lib.orc_lr_factors.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
+        _lib = lib
+    return _lib
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(x):
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+# ------------------------------------------------------------ elementwise
+def bf16_round(x) -> np.ndarray:
+    x = _f32(x)
+    out = np.empty_like(x)
+    _load().orc_bf16_round_array(x.size, _p(x), _p(out))
+    return out
+
+
+def bf16_bits(x) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (oracle's own rounding)."""
+    return (bf16_round(x).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_value(bits) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def residual(a, ahat) -> np.ndarray:
+    a, ahat = _f32(a), _f32(ahat)
+    r = np.empty_like(a)
+    _load().orc_residual(a.size, _p(a), _p(ahat), _p(r))
+    return r
+
+
+def ef_update(r, c, ahat):
+    """(e, ahat_new) with e = r - c, ahat_new = ahat + c (fp32, or fp64 c)."""
+    r = _f32(r)
+    e = np.empty_like(r)
+    ahat = _f32(ahat).copy()
+    if np.asarray(c).dtype == np.float64:
+        c = np.ascontiguousarray(c, np.float64)
+        _load().orc_ef_update_f64(r.size, _p(r), _p(c), _p(e), _p(ahat))
+    else:
+        c = _f32(c)
+        _load().orc_ef_update(r.size, _p(r), _p(c), _p(e), _p(ahat))
+    return e, ahat
+
+
+def accumulate(c, ahat) -> np.ndarray:
+    ahat = _f32(ahat).copy()
+    if np.asarray(c).dtype == np.float64:
+        c = np.ascontiguousarray(c, np.float64)
+        _load().orc_accumulate_f64(ahat.size, _p(c), _p(ahat))
+    else:
+        c = _f32(c)
+        _load().orc_accumulate(ahat.size, _p(c), _p(ahat))
+    return ahat
+
+
+# ------------------------------------------------------------ schemes
+def q1_encode(r, group=64):
+    r = _f32(r)
+    assert r.size % group == 0 and group % 8 == 0
+    bits = np.zeros(r.size // 8, np.uint8)
+    scale = np.empty(r.size // group, np.float32)
+    _load().orc_q1_encode(r.size, group, _p(r), _p(bits), _p(scale))
+    return bits, scale
+
+
+def q1_decode(bits, scale, count, group=64):
+    c = np.empty(count, np.float32)
+    _load().orc_q1_decode(count, group, _p(np.ascontiguousarray(bits, np.uint8)), _p(_f32(scale)),
+                          _p(c))
+    return c
+
+
+def q2_encode(r, group=128):
+    r = _f32(r)
+    assert r.size % group == 0 and group % 4 == 0
+    codes = np.zeros(r.size // 4, np.uint8)
+    mn = np.empty(r.size // group, np.float32)
+    d = np.empty(r.size // group, np.float32)
+    _load().orc_q2_encode(r.size, group, _p(r), _p(codes), _p(mn), _p(d))
+    return codes, mn, d
+
+
+def q2_decode(codes, mn, d, count, group=128):
+    c = np.empty(count, np.float32)
+    _load().orc_q2_decode(count, group, _p(np.ascontiguousarray(codes, np.uint8)), _p(_f32(mn)),
+                          _p(_f32(d)), _p(c))
+    return c
+
+
+def nm_encode(r):
+    r = _f32(r)
+    assert r.size % 16 == 0
+    vals = np.empty(2 * (r.size // 16), np.uint16)
+    idx = np.empty(r.size // 16, np.uint8)
+    _load().orc_nm_encode(r.size, _p(r), _p(vals), _p(idx))
+    return vals, idx
+
+
+def nm_decode(vals, idx, count):
+    c = np.empty(count, np.float32)
+    _load().orc_nm_decode(count, _p(np.ascontiguousarray(vals, np.uint16)),
+                          _p(np.ascontiguousarray(idx, np.uint8)), _p(c))
+    return c
+
+
+def lr_encode(r, q0, rank, iters, return_factors=False):
+    """r: fp32 [n, m]; q0: fp32 [m, rank]. Returns (qu, qv, su, sv[, U, V], ndead)."""
+    r = _f32(r)
+    n, m = r.shape
+    q0 = _f32(q0)
+    assert q0.shape == (m, rank)
+    qu = np.empty((n, rank), np.int8)
+    qv = np.empty((m, rank), np.int8)
+    su = np.empty(rank, np.float32)
+    sv = np.empty(rank, np.float32)
+    U = np.empty((n, rank), np.float64) if return_factors else None
+    V = np.empty((m, rank), np.float64) if return_factors else None
+    nd = _load().orc_lr_encode(n, m, rank, iters, _p(r), _p(q0), _p(qu), _p(qv), _p(su), _p(sv),
+                               _p(U), _p(V))
+    if return_factors:
+        return qu, qv, su, sv, U, V, nd
+    return qu, qv, su, sv, nd
+
+
+def lr_decode(qu, qv, su, sv):
+    n, k = qu.shape
+    m = qv.shape[0]
+    c = np.empty((n, m), np.float64)
+    _load().orc_lr_decode(n, m, k, _p(np.ascontiguousarray(qu, np.int8)),
+                          _p(np.ascontiguousarray(qv, np.int8)), _p(_f32(su)), _p(_f32(sv)), _p(c))
+    return c
+
+
+def lr_factors(r, q0, rank, iters):
+    """Unquantised factors (U [n,k], V [m,k]) of the subspace iteration."""
+    r = _f32(r)
+    n, m = r.shape
+    U = np.empty((n, rank), np.float64)
+    V = np.empty((m, rank), np.float64)
+    nd = _load().orc_lr_factors(n, m, rank, iters, _p(r), _p(_f32(q0)), _p(U), _p(V))
+    return U, V, nd
+
+
+# ------------------------------------------------------------ packed layout
+# Per tensor, sections in this order, each starting at a multiple of 256 bytes;
+# tensors follow each other, each tensor's block a multiple of 256 bytes.
+#   q1: sign bits [N/8]            | scales f32 [N/G]
+#   q2: 2-bit codes [N/4]          | (mn f32, d f32) pairs [N/G]
+#   nm: (v_i0, v_i1) bf16 pairs [N/16] | index bytes i0 | i1<<4 [N/16]
+#   lr: U nibbles [n*k/2] | V nibbles [m*k/2] | s_U f32 [k] | s_V f32 [k]
+#       nibble t of a row-major [rows x k] INT4 matrix = element t; even t in
+#       the low nibble; two's complement.
+ALIGN = 256
+
+
+def _al(x):
+    return (x + ALIGN - 1) // ALIGN * ALIGN
+
+
+def section_sizes(scheme, n, m, group=None, rank=None):
+    N = n * m
+    if scheme == "q1":
+        return [N // 8, 4 * (N // group)]
+    if scheme == "q2":
+        return [N // 4, 8 * (N // group)]
+    if scheme == "nm":
+        return [4 * (N // 16), N // 16]
+    if scheme == "lr":
+        return [n * rank // 2, m * rank // 2, 4 * rank, 4 * rank]
+    raise ValueError(scheme)
+
+
+def tensor_bytes(scheme, n, m, group=None, rank=None):
+    return sum(_al(s) for s in section_sizes(scheme, n, m, group, rank))
+
+
+def _place(sections, scheme, n, m, group, rank):
+    buf = np.zeros(tensor_bytes(scheme, n, m, group, rank), np.uint8)
+    off = 0
+    for raw, size in zip(sections, section_sizes(scheme, n, m, group, rank)):
+        raw = np.ascontiguousarray(raw).view(np.uint8).ravel()
+        assert raw.size == size, (raw.size, size)
+        buf[off:off + size] = raw
+        off += _al(size)
+    return buf
+
+
+def _split(buf, scheme, n, m, group, rank):
+    out, off = [], 0
+    for size in section_sizes(scheme, n, m, group, rank):
+        out.append(buf[off:off + size])
+        off += _al(size)
+    return out
+
+
+def _pack_int4(q):
+    q = np.asarray(q, np.int8).ravel()
+    nib = (q.astype(np.int16) & 0xF).astype(np.uint8)
+    return (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)
+
+
+def _unpack_int4(b, count):
+    b = np.asarray(b, np.uint8)
+    lo = (b & 0xF).astype(np.int16)
+    hi = (b >> 4).astype(np.int16)
+    q = np.empty(2 * b.size, np.int16)
+    q[0::2], q[1::2] = lo, hi
+    q = np.where(q >= 8, q - 16, q)
+    return q[:count].astype(np.int8)
+
+
+# ------------------------------------------------------------ one tensor
+def compress_tensor(scheme, a, ahat, *, group=None, rank=None, iters=None, q0=None):
+    """One sender step on one tensor.
+
+    a: library-view activations as fp32 values [n, m]; ahat: fp32 [n, m].
+    Returns dict(packed, c, e, ahat, r) where ahat is the new sender state.
+    """
+    a = _f32(a)
+    n, m = a.shape
+    r = residual(a, ahat)
+    flat = r.ravel()
+    if scheme == "q1":
+        bits, scale = q1_encode(flat, group)
+        c = q1_decode(bits, scale, flat.size, group)
+        packed = _place([bits, scale], scheme, n, m, group, rank)
+    elif scheme == "q2":
+        codes, mn, d = q2_encode(flat, group)
+        c = q2_decode(codes, mn, d, flat.size, group)
+        meta = np.stack([mn, d], axis=1)
+        packed = _place([codes, meta], scheme, n, m, group, rank)
+    elif scheme == "nm":
+        vals, idx = nm_encode(flat)
+        c = nm_decode(vals, idx, flat.size)
+        packed = _place([vals, idx], scheme, n, m, group, rank)
+    elif scheme == "lr":
+        qu, qv, su, sv, _ = lr_encode(r, q0, rank, iters)
+        c = lr_decode(qu, qv, su, sv).ravel()
+        packed = _place([_pack_int4(qu), _pack_int4(qv), su, sv], scheme, n, m, group, rank)
+    elif scheme == "identity":
+        c = flat.copy()
+        packed = None
+    else:
+        raise ValueError(scheme)
+    e, ahat_new = ef_update(flat, c, ahat.ravel())
+    return dict(packed=packed, c=c.reshape(n, m), e=e.reshape(n, m), ahat=ahat_new.reshape(n, m),
+                r=r)
+
+
+def decode_tensor(scheme, packed, n, m, *, group=None, rank=None):
+    """Decode one tensor's packed bytes to C(r) (fp32, or fp64 for lr)."""
+    secs = _split(np.asarray(packed, np.uint8), scheme, n, m, group, rank)
+    N = n * m
+    if scheme == "q1":
+        return q1_decode(secs[0], secs[1].view(np.float32), N, group).reshape(n, m)
+    if scheme == "q2":
+        meta = secs[1].view(np.float32).reshape(-1, 2)
+        return q2_decode(secs[0], meta[:, 0].copy(), meta[:, 1].copy(), N, group).reshape(n, m)
+    if scheme == "nm":
+        return nm_decode(secs[0].view(np.uint16), secs[1], N).reshape(n, m)
+    if scheme == "lr":
+        qu = _unpack_int4(secs[0], n * rank).reshape(n, rank)
+        qv = _unpack_int4(secs[1], m * rank).reshape(m, rank)
+        return lr_decode(qu, qv, secs[2].view(np.float32), secs[3].view(np.float32))
+    raise ValueError(scheme)
+
+
+def decompress_tensor(scheme, packed, ahat_r, *, group=None, rank=None):
+    n, m = ahat_r.shape
+    c = decode_tensor(scheme, packed, n, m, group=group, rank=rank)
+    return accumulate(c.ravel(), ahat_r.ravel()).reshape(n, m)
+
+
+def unpack_fields(scheme, packed, n, m, *, group=None, rank=None):
+    """Named views of one tensor's packed sections (for exact comparisons)."""
+    secs = _split(np.asarray(packed, np.uint8), scheme, n, m, group, rank)
+    if scheme == "q1":
+        return dict(bits=secs[0], scale=secs[1].view(np.float32))
+    if scheme == "q2":
+        meta = secs[1].view(np.float32).reshape(-1, 2)
+        return dict(codes=secs[0], mn=meta[:, 0], d=meta[:, 1])
+    if scheme == "nm":
+        return dict(vals=secs[0].view(np.uint16), idx=secs[1])
+    if scheme == "lr":
+        return dict(qu=_unpack_int4(secs[0], n * rank).reshape(n, rank),
+                    qv=_unpack_int4(secs[1], m * rank).reshape(m, rank),
+                    su=secs[2].view(np.float32), sv=secs[3].view(np.float32))
+    raise ValueError(scheme)
+
+
+# ------------------------------------------------------------ trajectories
+def compress_values(scheme, x, *, group=None, rank=None, iters=None, q0=None):
+    """C(x) for a fp32 matrix x [n, m] (fp32, or fp64 for lr)."""
+    x = _f32(x)
+    flat = x.ravel()
+    if scheme == "q1":
+        return q1_decode(*q1_encode(flat, group), flat.size, group).reshape(x.shape)
+    if scheme == "q2":
+        return q2_decode(*q2_encode(flat, group), flat.size, group).reshape(x.shape)
+    if scheme == "nm":
+        return nm_decode(*nm_encode(flat), flat.size).reshape(x.shape)
+    if scheme == "lr":
+        qu, qv, su, sv, _ = lr_encode(x, q0, rank, iters)
+        return lr_decode(qu, qv, su, sv)
+    if scheme == "identity":
+        return x.copy()
+    raise ValueError(scheme)
+
+
+def run_trajectory(mode, scheme, frames, **kw):
+    """Free-running sequence of one tensor through the scheme.
+
+    frames: list of fp32 [n, m] activations a_0..a_{T-1} (a_0 is sent in full,
+    the warm-up step in the Limitations section). Modes:
+      closed  -- the normative loop: r = a_t - ahat_{t-1}; ahat += C(r); e = r - C(r)
+      open    -- error feedback written against the previous activation:
+                 r = (a_t - a_{t-1}) + e_{t-1}
+      noef    -- r = a_t - a_{t-1}, the dropped part is discarded
+      literal -- r = a_t - ahat_{t-1} + e_{t-1} (counts the carried error twice)
+      direct  -- no residual: ahat_t = C(a_t)
+    Returns a list of ahat_t (fp32 [n, m]) for t = 0..T-1.
+    """
+    a0 = _f32(frames[0])
+    ahat = a0.copy()
+    e = np.zeros_like(a0)
+    out = [ahat.copy()]
+    prev = a0
+    for t in range(1, len(frames)):
+        a = _f32(frames[t])
+        if mode == "direct":
+            c = compress_values(scheme, a, **kw)
+            ahat = c.astype(np.float32) if c.dtype == np.float64 else c
+            out.append(ahat.copy())
+            continue
+        if mode == "closed":
+            r = residual(a, ahat)
+        elif mode == "open":
+            r = (residual(a, prev) + e).astype(np.float32)
+        elif mode == "noef":
+            r = residual(a, prev)
+        elif mode == "literal":
+            r = (residual(a, ahat) + e).astype(np.float32)
+        else:
+            raise ValueError(mode)
+        c = compress_values(scheme, r, **kw)
+        e_new, ahat = ef_update(r.ravel(), c.ravel(), ahat.ravel())
+        ahat = ahat.reshape(a.shape)
+        e = e_new.reshape(a.shape) if mode != "noef" else np.zeros_like(a)
+        prev = a
+        out.append(ahat.copy())
+    return out
