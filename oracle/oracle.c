@@ -130,7 +130,9 @@ void orc_q1_decode(int64_t count, int group, const uint8_t* bits, const float* s
 /* 2-bit uniform quantisation with group min/max (Main experiment table,
  * "2bit (8x)"; four levels mn + q*d, q = 0..3, d = (mx - mn)/3).
  * Readings (all fp32, one rounding per operation):
- *   d   = (mx - mn) / 3
+ *   mn  = group minimum, a zero stored as +0 (the page fixes no sign of zero;
+ *         no decoded value depends on it)
+ *   d   = (mx - mn) / 3, a zero stored as +0
  *   if d < FLT_MIN (constant or denormal-range group): q = 0 everywhere
  *   else inv = 1/d, t = (r - mn) * inv, q = min(3, round-half-even(t))
  *   decode c = fma(q, d, mn) (one rounding).
@@ -145,8 +147,10 @@ void orc_q2_encode(int64_t count, int group, const float* r, uint8_t* codes, flo
       if (x[i] < mn) mn = x[i];
       if (x[i] > mx) mx = x[i];
     }
+    /* a zero minimum or step is stored as +0 (x + 0 turns -0 into +0) */
+    mn = mn + 0.0f;
     const float range = mx - mn;
-    const float d = range / 3.0f;
+    const float d = range / 3.0f + 0.0f;
     mn_out[g] = mn;
     d_out[g] = d;
     if (!(d >= FLT_MIN)) continue; /* all codes 0 */
