@@ -1,0 +1,53 @@
+// Internal interface between the C ABI (plan.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace rc {
+
+// Per-tensor packed layout: up to 4 sections, each at a multiple of 256 bytes
+// inside the tensor's block; blocks of consecutive tensors are tstride apart.
+struct Layout {
+  int64_t rows = 0, cols = 0;
+  int64_t n = 0;        // elements per tensor (rows * cols)
+  int64_t tstride = 0;  // packed bytes per tensor (multiple of 256)
+  int64_t sec_off[4] = {0, 0, 0, 0};
+  int64_t sec_len[4] = {0, 0, 0, 0};
+  int nsec = 0;
+};
+
+// Q1 (bits = 1) and Q2 (bits = 2) group quantisation, group in {32, 64, 128}.
+hipError_t launch_q_compress(int bits, int group, bool bf16_input, const void* a, float* ahat,
+                             float* e, uint8_t* packed, int batch, const Layout& L, hipStream_t s);
+hipError_t launch_q_decompress(int bits, int group, const uint8_t* packed, float* ahat, int batch,
+                               const Layout& L, hipStream_t s);
+
+// 2:16 block sparsifier.
+hipError_t launch_nm_compress(bool bf16_input, const void* a, float* ahat, float* e,
+                              uint8_t* packed, int batch, const Layout& L, hipStream_t s);
+hipError_t launch_nm_decompress(const uint8_t* packed, float* ahat, int batch, const Layout& L,
+                                hipStream_t s);
+
+// Low-rank workspace, carved out of one device allocation by the plan.
+// ntiles = ceil(rows / 64); rows_pad = 64 * ntiles.
+struct LowRankWork {
+  int rank = 0, iters = 0;
+  int64_t ntiles = 0, rows_pad = 0;
+  uint16_t* R = nullptr;     // bf16 residual [batch][rows][cols]
+  float* P = nullptr;        // fp32 panel [batch][rows][rank]
+  uint16_t* Pbt = nullptr;   // bf16 orthonormal panel, transposed [batch][rank][rows_pad]
+  float* Qt = nullptr;       // fp32 Q^T [batch][rank][cols]
+  uint16_t* Q0t = nullptr;   // bf16 start matrix, transposed [batch][rank][cols]
+  uint16_t* Qtb = nullptr;   // bf16 Q^T for the next product [batch][rank][cols]
+  float* gpart = nullptr;    // per-64-row-tile Gram partials [batch][ntiles][rank][rank]
+  float* chol = nullptr;     // Cholesky factor + dead flags [batch][rank][rank + 1]
+};
+
+hipError_t launch_lr_compress(bool bf16_input, const void* a, float* ahat, float* e,
+                              uint8_t* packed, int batch, const Layout& L, const LowRankWork& w,
+                              hipStream_t s);
+hipError_t launch_lr_decompress(const uint8_t* packed, float* ahat, int batch, const Layout& L,
+                                int rank, hipStream_t s);
+
+}  // namespace rc

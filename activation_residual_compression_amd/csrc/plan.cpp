@@ -1,0 +1,265 @@
+// C ABI of librescomp: plan validation, packed-layout arithmetic, workspace,
+// and dispatch to the kernels. Host code only; every step of the path runs in
+// the HIP kernels launched from here.
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "../../include/librescomp.h"
+#include "launch.hpp"
+
+struct rc_plan {
+  rc_shape_t shape;
+  rc_dtype_t dtype;
+  rc_scheme_t scheme;
+  rc_params_t params;  // q0 cleared after upload
+  rc::Layout layout;
+  size_t packed_bytes = 0;
+  int device = 0;
+  // low rank
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  rc::LowRankWork lr;
+};
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+rc_status_t make_layout(const rc_shape_t& sh, rc_scheme_t scheme, const rc_params_t& p,
+                        rc::Layout* L) {
+  L->rows = sh.rows;
+  L->cols = sh.cols;
+  L->n = (int64_t)sh.rows * sh.cols;
+  const int64_t N = L->n;
+  int64_t len[4] = {0, 0, 0, 0};
+  int nsec = 0;
+  switch (scheme) {
+    case RC_Q1: len[0] = N / 8; len[1] = 4 * (N / p.group); nsec = 2; break;
+    case RC_Q2: len[0] = N / 4; len[1] = 8 * (N / p.group); nsec = 2; break;
+    case RC_NM: len[0] = 4 * (N / 16); len[1] = N / 16; nsec = 2; break;
+    case RC_LOWRANK:
+      len[0] = (int64_t)sh.rows * p.rank / 2;
+      len[1] = (int64_t)sh.cols * p.rank / 2;
+      len[2] = 4 * (int64_t)p.rank;
+      len[3] = 4 * (int64_t)p.rank;
+      nsec = 4;
+      break;
+    default: return RC_ERR_INVALID_ARG;
+  }
+  int64_t off = 0;
+  for (int s = 0; s < nsec; ++s) {
+    L->sec_off[s] = off;
+    L->sec_len[s] = len[s];
+    off += align_up(len[s]);
+  }
+  L->nsec = nsec;
+  L->tstride = off;
+  return RC_OK;
+}
+
+rc_status_t validate(const rc_shape_t& sh, rc_dtype_t dtype, rc_scheme_t scheme,
+                     const rc_params_t* p) {
+  if (!p) return RC_ERR_INVALID_ARG;
+  if (sh.batch < 1 || sh.rows < 1 || sh.cols < 1) return RC_ERR_INVALID_ARG;
+  if (sh.batch > 65535) return RC_ERR_UNSUPPORTED;  // one grid row per tensor
+  if ((int64_t)sh.batch * sh.rows * sh.cols >= kMaxElems) return RC_ERR_UNSUPPORTED;
+  if (dtype != RC_BF16 && dtype != RC_F32) return RC_ERR_INVALID_ARG;
+  if (p->flags != 0) return RC_ERR_INVALID_ARG;
+  switch (scheme) {
+    case RC_Q1:
+    case RC_Q2:
+      if (p->group != 32 && p->group != 64 && p->group != 128) {
+        return (p->group > 0 && p->group % 8 == 0) ? RC_ERR_UNSUPPORTED : RC_ERR_INVALID_ARG;
+      }
+      if (sh.cols % p->group) return RC_ERR_INVALID_ARG;
+      return RC_OK;
+    case RC_NM:
+      if (p->nm_keep < 1 || p->nm_block < 2 || p->nm_keep >= p->nm_block) return RC_ERR_INVALID_ARG;
+      if (p->nm_keep != 2 || p->nm_block != 16) return RC_ERR_UNSUPPORTED;
+      if (sh.cols % 16) return RC_ERR_INVALID_ARG;
+      return RC_OK;
+    case RC_LOWRANK:
+      if (p->rank < 1 || p->iters < 1 || p->iters > 16 || !p->q0) return RC_ERR_INVALID_ARG;
+      if (p->rank % 16 || p->rank > 64) return RC_ERR_UNSUPPORTED;
+      if (p->rank > sh.rows || p->rank > sh.cols) return RC_ERR_INVALID_ARG;
+      if (sh.cols % 64) return RC_ERR_INVALID_ARG;
+      return RC_OK;
+  }
+  return RC_ERR_INVALID_ARG;
+}
+
+// bf16 round-to-nearest-even of a host fp32 value (Q0 upload).
+uint16_t host_bf16(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+rc_status_t setup_lowrank(rc_plan* pl, const float* q0) {
+  const int64_t B = pl->shape.batch, n = pl->shape.rows, m = pl->shape.cols, k = pl->params.rank;
+  // carve the workspace: every piece 256-byte aligned
+  struct Piece { void** dst; int64_t bytes; };
+  rc::LowRankWork& w = pl->lr;
+  w.rank = (int)k;
+  w.iters = pl->params.iters;
+  w.ntiles = (n + 63) / 64;
+  w.rows_pad = 64 * w.ntiles;
+  Piece pieces[] = {
+      {(void**)&w.R, B * n * m * 2},
+      {(void**)&w.P, B * n * k * 4},
+      {(void**)&w.Pbt, B * k * w.rows_pad * 2},
+      {(void**)&w.Qt, B * k * m * 4},
+      {(void**)&w.Q0t, B * k * m * 2},
+      {(void**)&w.Qtb, B * k * m * 2},
+      {(void**)&w.gpart, B * w.ntiles * k * k * 4},
+      {(void**)&w.chol, B * k * (k + 1) * 4},
+  };
+  int64_t total = 0;
+  for (auto& pc : pieces) total += align_up(pc.bytes);
+  hipError_t err = hipGetDevice(&pl->device);
+  if (err != hipSuccess) return RC_ERR_HIP;
+  err = hipMalloc(&pl->ws, (size_t)total);
+  if (err != hipSuccess) { pl->ws = nullptr; return RC_ERR_HIP; }
+  pl->ws_bytes = (size_t)total;
+  int64_t off = 0;
+  for (auto& pc : pieces) {
+    *pc.dst = (char*)pl->ws + off;
+    off += align_up(pc.bytes);
+  }
+  // Q0 [B][m][k] fp32 (host) -> bf16 Q0^T [B][k][m] (device), uploaded once.
+  std::vector<uint16_t> t((size_t)(B * k * m));
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t c = 0; c < m; ++c)
+      for (int64_t j = 0; j < k; ++j) t[(size_t)((b * k + j) * m + c)] = host_bf16(q0[(b * m + c) * k + j]);
+  err = hipMemcpy(w.Q0t, t.data(), t.size() * 2, hipMemcpyHostToDevice);
+  if (err != hipSuccess) return RC_ERR_HIP;
+  return RC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rc_status_t rc_plan_create(rc_shape_t shape, rc_dtype_t dtype, rc_scheme_t scheme,
+                           const rc_params_t* params, rc_plan_t* out) {
+  if (!out) return RC_ERR_INVALID_ARG;
+  *out = nullptr;
+  rc_status_t st = validate(shape, dtype, scheme, params);
+  if (st != RC_OK) return st;
+  rc_plan* pl = new (std::nothrow) rc_plan();
+  if (!pl) return RC_ERR_HIP;
+  pl->shape = shape;
+  pl->dtype = dtype;
+  pl->scheme = scheme;
+  pl->params = *params;
+  pl->params.q0 = nullptr;
+  st = make_layout(shape, scheme, *params, &pl->layout);
+  if (st != RC_OK) { delete pl; return st; }
+  pl->packed_bytes = (size_t)(pl->layout.tstride * shape.batch);
+  if (scheme == RC_LOWRANK) {
+    st = setup_lowrank(pl, params->q0);
+    if (st != RC_OK) { rc_plan_destroy(pl); return st; }
+  }
+  *out = pl;
+  return RC_OK;
+}
+
+rc_status_t rc_compress(rc_plan_t pl, hipStream_t stream, const void* a_t, const rc_state_t* state,
+                        void* packed_out) {
+  if (!pl || !a_t || !state || !state->ahat || !state->e || !packed_out) return RC_ERR_INVALID_ARG;
+  if (!aligned16(a_t) || !aligned16(state->ahat) || !aligned16(state->e) || !aligned16(packed_out))
+    return RC_ERR_ALIGNMENT;
+  const bool bf16 = pl->dtype == RC_BF16;
+  uint8_t* packed = static_cast<uint8_t*>(packed_out);
+  hipError_t err = hipSuccess;
+  switch (pl->scheme) {
+    case RC_Q1:
+    case RC_Q2:
+      err = rc::launch_q_compress(pl->scheme == RC_Q1 ? 1 : 2, pl->params.group, bf16, a_t,
+                                  state->ahat, state->e, packed, pl->shape.batch, pl->layout, stream);
+      break;
+    case RC_NM:
+      err = rc::launch_nm_compress(bf16, a_t, state->ahat, state->e, packed, pl->shape.batch,
+                                   pl->layout, stream);
+      break;
+    case RC_LOWRANK:
+      err = rc::launch_lr_compress(bf16, a_t, state->ahat, state->e, packed, pl->shape.batch,
+                                   pl->layout, pl->lr, stream);
+      break;
+  }
+  return err == hipSuccess ? RC_OK : RC_ERR_HIP;
+}
+
+rc_status_t rc_decompress(rc_plan_t pl, hipStream_t stream, const void* packed_in,
+                          float* recon_state) {
+  if (!pl || !packed_in || !recon_state) return RC_ERR_INVALID_ARG;
+  if (!aligned16(packed_in) || !aligned16(recon_state)) return RC_ERR_ALIGNMENT;
+  const uint8_t* packed = static_cast<const uint8_t*>(packed_in);
+  hipError_t err = hipSuccess;
+  switch (pl->scheme) {
+    case RC_Q1:
+    case RC_Q2:
+      err = rc::launch_q_decompress(pl->scheme == RC_Q1 ? 1 : 2, pl->params.group, packed,
+                                    recon_state, pl->shape.batch, pl->layout, stream);
+      break;
+    case RC_NM:
+      err = rc::launch_nm_decompress(packed, recon_state, pl->shape.batch, pl->layout, stream);
+      break;
+    case RC_LOWRANK:
+      err = rc::launch_lr_decompress(packed, recon_state, pl->shape.batch, pl->layout,
+                                     pl->params.rank, stream);
+      break;
+  }
+  return err == hipSuccess ? RC_OK : RC_ERR_HIP;
+}
+
+rc_status_t rc_plan_destroy(rc_plan_t pl) {
+  if (!pl) return RC_OK;
+  rc_status_t st = RC_OK;
+  if (pl->ws) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) st = RC_ERR_HIP;
+    if (cur != pl->device && hipSetDevice(pl->device) != hipSuccess) st = RC_ERR_HIP;
+    if (hipFree(pl->ws) != hipSuccess) st = RC_ERR_HIP;
+    if (cur != pl->device) (void)hipSetDevice(cur);
+  }
+  delete pl;
+  return st;
+}
+
+size_t rc_packed_bytes(rc_plan_t pl) { return pl ? pl->packed_bytes : 0; }
+
+size_t rc_tensor_packed_bytes(rc_plan_t pl) { return pl ? (size_t)pl->layout.tstride : 0; }
+
+size_t rc_workspace_bytes(rc_plan_t pl) { return pl ? pl->ws_bytes : 0; }
+
+// Diagnostics (not part of the public header): device pointers of the
+// low-rank workspace pieces, in the order R, P, Pbt, Qt, Q0t, Qtb, gpart, chol.
+int rcx_lowrank_workspace(rc_plan_t pl, void** ptrs, int count) {
+  if (!pl || pl->scheme != RC_LOWRANK || !ptrs || count < 8) return -1;
+  const rc::LowRankWork& w = pl->lr;
+  void* v[8] = {w.R, w.P, w.Pbt, w.Qt, w.Q0t, w.Qtb, w.gpart, w.chol};
+  for (int i = 0; i < 8; ++i) ptrs[i] = v[i];
+  return (int)w.rows_pad;
+}
+
+const char* rc_status_string(rc_status_t s) {
+  switch (s) {
+    case RC_OK: return "RC_OK: success";
+    case RC_ERR_INVALID_ARG: return "RC_ERR_INVALID_ARG: null pointer, bad shape or bad parameter";
+    case RC_ERR_UNSUPPORTED: return "RC_ERR_UNSUPPORTED: valid request not implemented by librescomp";
+    case RC_ERR_ALIGNMENT: return "RC_ERR_ALIGNMENT: tensor pointer not 16-byte aligned";
+    case RC_ERR_HIP: return "RC_ERR_HIP: HIP runtime call or kernel launch failed";
+  }
+  return "unknown rc_status_t";
+}
+
+}  // extern "C"

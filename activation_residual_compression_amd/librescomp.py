@@ -1,0 +1,208 @@
+"""ctypes binding of the librescomp C ABI (``include/librescomp.h``).
+
+Argument marshalling only: every step of the compression path runs in the HIP
+kernels of ``librescomp.so``. Functions keep the C names; a non-RC_OK status
+raises :class:`RcError`. Tensor arguments may be torch tensors (their
+``data_ptr()`` is passed), raw integer device addresses, or numpy arrays for the
+host-side start matrix ``q0``. Streams may be a ``torch.cuda.Stream``, a raw
+``hipStream_t`` integer, or None for torch's current stream.
+
+The library must be built first (``__graft_entry__.build()`` or
+``python -m activation_residual_compression_amd.build``); importing this module
+without it raises, so nothing can silently fall back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "librescomp.so")
+
+RC_OK, RC_ERR_INVALID_ARG, RC_ERR_UNSUPPORTED, RC_ERR_ALIGNMENT, RC_ERR_HIP = 0, 1, 2, 3, 4
+RC_BF16, RC_F32 = 0, 1
+RC_Q1, RC_Q2, RC_NM, RC_LOWRANK = 0, 1, 2, 3
+
+SCHEMES = {"q1": RC_Q1, "q2": RC_Q2, "nm": RC_NM, "lr": RC_LOWRANK}
+DTYPES = {"bf16": RC_BF16, "f32": RC_F32}
+
+
+class rc_shape_t(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
+class rc_params_t(ctypes.Structure):
+    _fields_ = [("group", ctypes.c_int32), ("nm_keep", ctypes.c_int32),
+                ("nm_block", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("iters", ctypes.c_int32), ("q0", ctypes.c_void_p), ("flags", ctypes.c_uint32)]
+
+
+class rc_state_t(ctypes.Structure):
+    _fields_ = [("ahat", ctypes.c_void_p), ("e", ctypes.c_void_p)]
+
+
+class RcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s" % (where, rc_status_string(status)))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "librescomp.so is not built (expected at %s); run __graft_entry__.build() "
+            "or python -m activation_residual_compression_amd.build" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    st = ctypes.c_int
+    lib.rc_plan_create.restype = st
+    lib.rc_plan_create.argtypes = [rc_shape_t, ctypes.c_int, ctypes.c_int,
+                                   ctypes.POINTER(rc_params_t), ctypes.POINTER(vp)]
+    lib.rc_compress.restype = st
+    lib.rc_compress.argtypes = [vp, vp, vp, ctypes.POINTER(rc_state_t), vp]
+    lib.rc_decompress.restype = st
+    lib.rc_decompress.argtypes = [vp, vp, vp, vp]
+    lib.rc_plan_destroy.restype = st
+    lib.rc_plan_destroy.argtypes = [vp]
+    for f in ("rc_packed_bytes", "rc_tensor_packed_bytes", "rc_workspace_bytes"):
+        getattr(lib, f).restype = sz
+        getattr(lib, f).argtypes = [vp]
+    lib.rc_status_string.restype = ctypes.c_char_p
+    lib.rc_status_string.argtypes = [ctypes.c_int]
+    lib.rcx_lowrank_workspace.restype = ctypes.c_int
+    lib.rcx_lowrank_workspace.argtypes = [vp, ctypes.POINTER(vp), ctypes.c_int]
+    return lib
+
+
+_lib = _load()
+lib = _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if hasattr(x, "ctypes"):  # numpy (host)
+        return x.ctypes.data
+    raise TypeError("cannot take a device pointer of %r" % type(x))
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != RC_OK:
+        raise RcError(status, where)
+
+
+# ------------------------------------------------------------------ C names
+def rc_status_string(status: int) -> str:
+    return _lib.rc_status_string(int(status)).decode()
+
+
+def rc_plan_create(shape, dtype, scheme, params: rc_params_t):
+    """shape: rc_shape_t or (batch, rows, cols); dtype/scheme: enum ints or names."""
+    if not isinstance(shape, rc_shape_t):
+        shape = rc_shape_t(*shape)
+    dtype = DTYPES.get(dtype, dtype)
+    scheme = SCHEMES.get(scheme, scheme)
+    plan = ctypes.c_void_p()
+    _check(_lib.rc_plan_create(shape, int(dtype), int(scheme), ctypes.byref(params),
+                               ctypes.byref(plan)), "rc_plan_create")
+    return plan
+
+
+def rc_compress(plan, stream, a_t, state: rc_state_t, packed_out):
+    _check(_lib.rc_compress(plan, _stream(stream), _ptr(a_t), ctypes.byref(state), _ptr(packed_out)),
+           "rc_compress")
+
+
+def rc_decompress(plan, stream, packed_in, recon_state):
+    _check(_lib.rc_decompress(plan, _stream(stream), _ptr(packed_in), _ptr(recon_state)),
+           "rc_decompress")
+
+
+def rc_plan_destroy(plan):
+    _check(_lib.rc_plan_destroy(plan), "rc_plan_destroy")
+
+
+def rc_packed_bytes(plan) -> int:
+    return int(_lib.rc_packed_bytes(plan))
+
+
+def rc_tensor_packed_bytes(plan) -> int:
+    return int(_lib.rc_tensor_packed_bytes(plan))
+
+
+def rc_workspace_bytes(plan) -> int:
+    return int(_lib.rc_workspace_bytes(plan))
+
+
+def make_params(scheme, *, group=0, nm_keep=0, nm_block=0, rank=0, iters=0, q0=None, flags=0):
+    """rc_params_t for a scheme; q0 (host fp32 [batch][cols][rank]) is referenced, not copied,
+    so keep it alive until rc_plan_create returns."""
+    p = rc_params_t(int(group), int(nm_keep), int(nm_block), int(rank), int(iters), _ptr(q0),
+                    int(flags))
+    p._q0_ref = q0
+    return p
+
+
+# ------------------------------------------------------------------ convenience
+class Plan:
+    """Owns one rc_plan_t; a thin wrapper over the C calls above."""
+
+    def __init__(self, shape, dtype, scheme, **params):
+        self.shape = tuple(shape)
+        self.dtype = dtype
+        self.scheme = scheme
+        q0 = params.get("q0")
+        if q0 is not None:
+            import numpy as np
+            q0 = np.ascontiguousarray(q0, dtype=np.float32)
+            params["q0"] = q0
+        self._params = make_params(scheme, **params)
+        self.handle = rc_plan_create(self.shape, dtype, scheme, self._params)
+        self.packed_bytes = rc_packed_bytes(self.handle)
+        self.tensor_packed_bytes = rc_tensor_packed_bytes(self.handle)
+        self.workspace_bytes = rc_workspace_bytes(self.handle)
+
+    def compress(self, a_t, ahat, e, packed_out, stream=None):
+        st = rc_state_t(_ptr(ahat), _ptr(e))
+        rc_compress(self.handle, stream, a_t, st, packed_out)
+
+    def decompress(self, packed_in, recon_state, stream=None):
+        rc_decompress(self.handle, stream, packed_in, recon_state)
+
+    def lowrank_workspace(self):
+        """Device pointers (R, P, Pbt, Qt, Q0t, Qtb, gpart, chol) and rows_pad (diagnostics)."""
+        arr = (ctypes.c_void_p * 8)()
+        rp = _lib.rcx_lowrank_workspace(self.handle, arr, 8)
+        if rp < 0:
+            raise ValueError("not a low-rank plan")
+        return [int(v or 0) for v in arr], rp
+
+    def close(self):
+        if self.handle is not None:
+            rc_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

@@ -53,6 +53,16 @@ static inline double sm_normal(uint64_t key, uint64_t i) {
   return (i & 1) ? rad * sin(ang) : rad * cos(ang);
 }
 
+/* Both normals of pair p (elements 2p and 2p+1) from one Box-Muller draw. */
+static inline void sm_normal_pair(uint64_t key, uint64_t p, double* z0, double* z1) {
+  const double u1 = sm_uniform(key, 2 * p);
+  const double u2 = sm_uniform(key, 2 * p + 1);
+  const double rad = sqrt(-2.0 * log(u1));
+  const double ang = 6.283185307179586476925286766559 * u2;
+  *z0 = rad * cos(ang);
+  *z1 = rad * sin(ang);
+}
+
 /* Stream key for (seed, role, tensor, step). */
 uint64_t sg_key(uint64_t seed, uint64_t role, uint64_t tensor, uint64_t step) {
   uint64_t k = sm_at(seed, role);
@@ -119,9 +129,16 @@ void sg_walk_init(uint64_t seed, int tensor, int n, int m, double sigma_s, float
 void sg_walk_step(uint64_t seed, int tensor, int t, int n, int m, double step_sigma, const float* sc,
                   float* a) {
   const uint64_t k = sg_key(seed, ROLE_STEP, tensor, t);
+  const int64_t N = (int64_t)n * m;
 #pragma omp parallel for schedule(static)
-  for (int64_t idx = 0; idx < (int64_t)n * m; ++idx)
-    a[idx] = (float)((double)a[idx] + step_sigma * sm_normal(k, idx) * (double)sc[idx % m]);
+  for (int64_t p = 0; p < (N + 1) / 2; ++p) {
+    double z[2];
+    sm_normal_pair(k, p, &z[0], &z[1]);
+    for (int q = 0; q < 2; ++q) {
+      const int64_t idx = 2 * p + q;
+      if (idx < N) a[idx] = (float)((double)a[idx] + step_sigma * z[q] * (double)sc[idx % m]);
+    }
+  }
 }
 
 /* ------------------------------------------------------------------------ */
@@ -167,13 +184,20 @@ void sg_flux_step(uint64_t seed, int tensor, int t, int n, int m, double sigma, 
   const uint64_t k = sg_key(seed, ROLE_STEP, tensor, t);
   const double amp = sigma / sqrt(2.0);
   const double inv_sqrt_r = 1.0 / sqrt((double)rank_drift);
+  const int64_t N = (int64_t)n * m;
 #pragma omp parallel for schedule(static)
-  for (int64_t idx = 0; idx < (int64_t)n * m; ++idx) {
-    const int64_t i = idx / m, j = idx % m;
-    double d = 0.0;
-    for (int q = 0; q < rank_drift; ++q) d += (double)A[i * rank_drift + q] * (double)B[j * rank_drift + q];
-    d *= inv_sqrt_r;
-    a[idx] = (float)((double)a[idx] + amp * (sm_normal(k, idx) + d) * (double)sc[j]);
+  for (int64_t p = 0; p < (N + 1) / 2; ++p) {
+    double z[2];
+    sm_normal_pair(k, p, &z[0], &z[1]);
+    for (int q = 0; q < 2; ++q) {
+      const int64_t idx = 2 * p + q;
+      if (idx >= N) break;
+      const int64_t i = idx / m, j = idx % m;
+      double d = 0.0;
+      for (int r = 0; r < rank_drift; ++r) d += (double)A[i * rank_drift + r] * (double)B[j * rank_drift + r];
+      d *= inv_sqrt_r;
+      a[idx] = (float)((double)a[idx] + amp * (z[q] + d) * (double)sc[j]);
+    }
   }
 }
 

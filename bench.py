@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Throughput of the residual-compression hot path on one MI355X.
+
+One step = rc_compress + rc_decompress over the whole batch of a workload (the
+sender's fused residual / compress / error-feedback pass and the receiver's
+decode-and-accumulate pass), with every input already resident in HBM. Default
+workload: the FLUX-like share, 57 bf16 tensors of 1152 x 3072, 2-bit groups of
+128. The other workloads (2:16, video-like 1-bit, both low-rank settings) are
+measured the same way and reported under "workloads".
+
+Prints ONE JSON line. `value` = input-activation GB/s of the default workload
+(bf16 bytes of a_t per step / wall time per step over the timed steps).
+`roofline` = the dominant kernel (the sender kernel) against HBM: algorithmic
+bytes per launch / its mean duration from HIP events on the launch stream.
+`cpu_baseline` = the single-threaded CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def algorithmic_bytes(scheme, n_elem, in_bytes, group=None, rank=None, rows=None, cols=None, iters=None,
+                      batch=None):
+    """Bytes each kernel family must move at minimum, per call (all tensors)."""
+    N = n_elem
+    if scheme == "q1":
+        meta = N / 8 + 4 * N / group
+    elif scheme == "q2":
+        meta = N / 4 + 8 * N / group
+    elif scheme == "nm":
+        meta = 5 * N / 16
+    else:
+        meta = None
+    if meta is not None:
+        return dict(compress=N * (in_bytes + 12) + meta, decompress=meta + 8 * N)
+    # low rank: residual + first product (a, ahat in; R out), later products re-read R,
+    # reconstruct reads a, ahat and writes ahat, e; receiver reads/writes its state.
+    factors = batch * (rows + cols) * rank // 2 + batch * 8 * rank
+    compress = N * (in_bytes + 4 + 2) + N * 2 * (2 * iters - 1) + N * (in_bytes + 12) + factors
+    return dict(compress=compress, decompress=factors + 8 * N)
+
+
+def lr_flops(rows, cols, rank, iters, batch):
+    """bf16 MFMA flops of the two tall-skinny products per iteration."""
+    return batch * iters * 2 * (2.0 * rows * cols * rank)
+
+
+_FRAMES = {}  # host frames per workload sequence, shared by the schemes measured on it
+
+
+def measure(config, steps, warmup, max_frames, log):
+    import numpy as np
+    import torch
+
+    from activation_residual_compression_amd import librescomp as rc
+    from activation_residual_compression_amd import synth
+
+    spec = synth.CONFIGS[config]
+    wl = synth.make(config)
+    nframes = max(2, min(1 + warmup + steps, wl.steps, max_frames))
+    dev = torch.device("cuda:0")
+    B, n, m = wl.nb, wl.n, wl.m
+    tdtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    host = _FRAMES.setdefault(wl.name, [])
+    if len(host) < nframes:
+        log("[bench] %s: generating %d frames of %dx%dx%d %s" % (config, nframes, B, n, m, wl.dtype))
+        for _ in range(len(host)):
+            wl.next()
+        while len(host) < nframes:
+            host.append(wl.next()[1])
+    frames = []
+    for a in host[:nframes]:
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if wl.dtype == "bf16" else \
+            torch.from_numpy(a)
+        frames.append(t.to(dev))
+    kw = {k: spec[k] for k in ("group", "nm_keep", "nm_block", "rank", "iters") if k in spec}
+    if spec["scheme"] == "lr":
+        kw["q0"] = wl.q0(spec["rank"])
+    plan = rc.Plan((B, n, m), wl.dtype, spec["scheme"], **kw)
+    ahat = frames[0].float().contiguous()
+    recon = ahat.clone()
+    e = torch.zeros_like(ahat)
+    packed = torch.empty(plan.packed_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    seq = [frames[1 + i % (nframes - 1)] for i in range(warmup + steps)]
+    for i in range(warmup):
+        plan.compress(seq[i], ahat, e, packed, stream)
+        plan.decompress(packed, recon, stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        plan.compress(seq[warmup + i], ahat, e, packed, stream)
+        ev[i][1].record(stream)
+        plan.decompress(packed, recon, stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    c_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)) / steps
+    d_ms = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)) / steps
+    same = bool(torch.equal(ahat, recon))
+    in_bytes = 2 if wl.dtype == "bf16" else 4
+    N = B * n * m
+    alg = algorithmic_bytes(spec["scheme"], N, in_bytes, group=spec.get("group"), rank=spec.get("rank"),
+                            rows=n, cols=m, iters=spec.get("iters"), batch=B)
+    out = dict(config=config, scheme=spec["scheme"], shape=[B, n, m], dtype=wl.dtype,
+               frames=nframes, steps=steps, ms_per_step=ms_step, compress_ms=c_ms,
+               decompress_ms=d_ms, input_GBps=N * in_bytes / (ms_step * 1e6),
+               compress_GBps=alg["compress"] / (c_ms * 1e6),
+               decompress_GBps=alg["decompress"] / (d_ms * 1e6),
+               alg_bytes_compress=alg["compress"], alg_bytes_decompress=alg["decompress"],
+               sender_equals_receiver=same)
+    out["hbm_frac_step"] = (alg["compress"] + alg["decompress"]) / (ms_step * 1e6) / HBM_PEAK_GBS
+    if spec["scheme"] == "lr":
+        fl = lr_flops(n, m, spec["rank"], spec["iters"], B)
+        out["tensors_per_ms"] = B / ms_step
+        out["mfma_flops"] = fl
+        out["mfma_util_whole_compress"] = fl / (c_ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    plan.close()
+    del frames, seq, ahat, recon, e, packed
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(config, budget_s, log):
+    """The oracle, untuned, single-threaded, on a bounded sample of the workload."""
+    import numpy as np
+
+    import oracle
+    from activation_residual_compression_amd import synth
+
+    spec = synth.CONFIGS[config]
+    kw = {k: spec[k] for k in ("group",) if k in spec}
+    if spec["scheme"] == "lr":
+        kw.update(rank=spec["rank"], iters=spec["iters"])
+    oracle.build(force=False)
+    tensors = [0, 1, 2, 3]
+    wl = synth.make(config, tensors=tensors)
+    _, a0 = wl.next()
+    f32 = lambda a: (a.astype(np.uint32) << 16).view(np.float32) if wl.dtype == "bf16" else a
+    ahat = [f32(a0)[i].copy() for i in range(len(tensors))]
+    recon = [x.copy() for x in ahat]
+    q0 = wl.q0(spec["rank"]) if spec["scheme"] == "lr" else None
+    done, elapsed, t = 0, 0.0, 0
+    log("[bench] cpu baseline: oracle %s" % config)
+    while elapsed < budget_s and t + 1 < wl.steps:
+        _, a = wl.next()
+        t += 1
+        af = f32(a)
+        for i in range(len(tensors)):
+            extra = dict(q0=q0[i]) if q0 is not None else {}
+            s = time.perf_counter()
+            o = oracle.compress_tensor(spec["scheme"], af[i], ahat[i], **kw, **extra)
+            recon[i] = oracle.decompress_tensor(spec["scheme"], o["packed"], recon[i],
+                                                group=kw.get("group"), rank=kw.get("rank"))
+            elapsed += time.perf_counter() - s
+            ahat[i] = o["ahat"]
+            done += 1
+            if elapsed >= budget_s:
+                break
+    in_bytes = 2 if wl.dtype == "bf16" else 4
+    gbps = done * wl.n * wl.m * in_bytes / elapsed / 1e9
+    return dict(value=gbps, unit="GB/s", cores=1, kind="oracle",
+                sample="%s: %d tensor-steps of %dx%d (tensors 0-3, steps 1-%d), compress+decompress, "
+                       "%.1f s single-threaded" % (config, done, wl.n, wl.m, t, elapsed))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="flux_q2")
+    ap.add_argument("--also", default="flux_nm,video_q1,flux_lr,video_lr",
+                    help="other workloads to measure ('' for none)")
+    ap.add_argument("--also-frames", type=int, default=4,
+                    help="distinct input frames for the other workloads (cycled)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the path has no inter-GPU step in this library "
+              "(--gpus %d / WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    log = lambda s: print(s, file=sys.stderr, flush=True)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    main_res = measure(args.workload, args.steps, args.warmup, 64, log)
+    log("[bench] %s: %.3f ms/step, %.1f GB/s input, compress %.3f ms (%.0f GB/s alg)" % (
+        args.workload, main_res["ms_per_step"], main_res["input_GBps"], main_res["compress_ms"],
+        main_res["compress_GBps"]))
+    others = {}
+    for cfg in [c for c in args.also.split(",") if c and c != args.workload]:
+        r = measure(cfg, args.steps, args.warmup, args.also_frames, log)
+        log("[bench] %s: %.3f ms/step, %.1f GB/s input" % (cfg, r["ms_per_step"], r["input_GBps"]))
+        others[cfg] = r
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload, args.cpu_budget, log)
+
+    ach = main_res["compress_GBps"]
+    line = {
+        "metric": "compress+decompress GB/s of activations per GPU (% HBM peak); low-rank MFMA util",
+        "value": main_res["input_GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: %d bf16 tensors [%d x %d] per step, scheme %s" % (
+            args.workload, *main_res["shape"], main_res["scheme"]),
+            "steps_per_sequence": 28, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "sender kernel (rc_compress)"},
+        "hbm_frac_step": main_res["hbm_frac_step"],
+        "cpu_baseline": cpu,
+        "workloads": {args.workload: main_res, **others},
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

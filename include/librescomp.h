@@ -1,0 +1,136 @@
+/*
+ * librescomp -- residual compression with error feedback for parallel
+ * diffusion inference, as HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one described on the paper-notes page "Accelerating
+ * Parallel Diffusion Model Serving with Residual Compression" (CompactFusion):
+ *   - Overall framework: instead of an activation a_t, a GPU sends C(r) for the
+ *     residual r = a_t - ahat_{t-1} against the reconstruction ahat that the
+ *     receiver holds; the receiver sets ahat_t = ahat_{t-1} + C(r).
+ *   - Key designs / Error feedback: the part C dropped, e_t = r - C(r), stays on
+ *     the sender. The sender keeps a bit-identical copy of the receiver's ahat,
+ *     so a_t - ahat_t = e_t after every step and the next residual carries e_t.
+ *   - Compressors C: 1-bit and 2-bit group quantisation (Main experiment table,
+ *     16x / 8x), a 2:16 block sparsifier (Key designs / System co-design), and a
+ *     rank-k factorisation by subspace iteration with INT4 factors (Key designs /
+ *     Low-rank strategy for extreme compression).
+ *   - Limitations: step 0 has no history and is sent in full. That warm-up is
+ *     the caller's: send a_0, set sender ahat = receiver ahat = float(a_0) and
+ *     e = 0 (plain device copies); every later step uses rc_compress on the
+ *     sender and rc_decompress on each receiver.
+ *
+ * Conventions for every call:
+ *   - Tensors are [batch][rows][cols], row-major, contiguous; groups and blocks
+ *     run along cols. a_t is bf16 or fp32 (rc_dtype_t); ahat, e and the receiver
+ *     state are fp32.
+ *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *     aligned. The library never allocates or frees them.
+ *   - Calls are asynchronous on the given HIP stream and never synchronise the
+ *     host. Calls on one plan must be serialised on one stream (the low-rank
+ *     scheme keeps per-plan device workspace).
+ *   - On any error nothing is launched and no buffer is touched; the return
+ *     value says why. RC_ERR_HIP reports a failed kernel launch.
+ *   - Inputs holding NaN or Inf give unspecified (but memory-safe) results.
+ */
+#ifndef LIBRESCOMP_H
+#define LIBRESCOMP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct rc_plan* rc_plan_t; /* opaque; created and owned by the library */
+
+typedef enum {
+  RC_OK = 0,
+  RC_ERR_INVALID_ARG = 1, /* null pointer, bad shape, bad parameter value */
+  RC_ERR_UNSUPPORTED = 2, /* valid request this library does not implement */
+  RC_ERR_ALIGNMENT = 3,   /* a tensor pointer is not 16-byte aligned */
+  RC_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+} rc_status_t;
+
+typedef enum { RC_BF16 = 0, RC_F32 = 1 } rc_dtype_t; /* dtype of a_t */
+
+typedef enum {
+  RC_Q1 = 0,      /* 1-bit signs + per-group fp32 mean|r|                 */
+  RC_Q2 = 1,      /* 2-bit uniform levels + per-group fp32 (min, step)   */
+  RC_NM = 2,      /* keep 2 of every 16, bf16 values + 4-bit indices     */
+  RC_LOWRANK = 3, /* rank-k subspace iteration, INT4 factors             */
+} rc_scheme_t;
+
+typedef struct {
+  int32_t batch; /* tensors per call (e.g. 57 transformer blocks)  */
+  int32_t rows;  /* tokens of this GPU's share                      */
+  int32_t cols;  /* hidden size                                     */
+} rc_shape_t;
+
+typedef struct {
+  int32_t group;    /* RC_Q1 / RC_Q2: group size along cols: 32, 64 or 128       */
+  int32_t nm_keep;  /* RC_NM: kept per block, must be 2                           */
+  int32_t nm_block; /* RC_NM: block size, must be 16                              */
+  int32_t rank;     /* RC_LOWRANK: 16, 32, 48 or 64                               */
+  int32_t iters;    /* RC_LOWRANK: subspace iterations, 1..16                     */
+  const float* q0;  /* RC_LOWRANK: HOST fp32 [batch][cols][rank] start matrices;  */
+                    /*   copied at plan creation and reused every step           */
+  uint32_t flags;   /* must be 0                                                  */
+} rc_params_t;
+
+typedef struct {
+  float* ahat; /* sender's copy of the receiver reconstruction, fp32 [batch][rows][cols] */
+  float* e;    /* error-feedback buffer, fp32 [batch][rows][cols] (written every step)  */
+} rc_state_t;
+
+/* Validate the request and build a plan. For RC_LOWRANK this allocates the
+ * device workspace (rc_workspace_bytes) on the current device and uploads q0.
+ * Cols must be a multiple of the group (Q1/Q2), of 16 (NM) or of 64 (LR);
+ * rows*cols*batch must stay below 2^40. */
+rc_status_t rc_plan_create(rc_shape_t shape, rc_dtype_t dtype, rc_scheme_t scheme,
+                           const rc_params_t* params, rc_plan_t* out);
+
+/* Sender step (Overall framework + Error feedback): for every tensor,
+ *   r = a_t - ahat;  packed_out <- encode(C(r));  e = r - C(r);  ahat += C(r)
+ * where C(r) is decoded from the packed bytes exactly as rc_decompress decodes
+ * them, so a receiver that applies packed_out stays bit-identical to ahat.
+ * a_t: [batch][rows][cols] of the plan's dtype. state->ahat is read and
+ * updated in place, state->e is written. packed_out: rc_packed_bytes(plan)
+ * bytes, written completely (padding included). */
+rc_status_t rc_compress(rc_plan_t plan, hipStream_t stream, const void* a_t, const rc_state_t* state,
+                        void* packed_out);
+
+/* Receiver step (Overall framework): recon_state += decode(packed_in) for every
+ * tensor. recon_state: fp32 [batch][rows][cols], updated in place. */
+rc_status_t rc_decompress(rc_plan_t plan, hipStream_t stream, const void* packed_in,
+                          float* recon_state);
+
+/* Free the plan and its workspace. Waits for nothing: the caller must make sure
+ * no launched work still uses the plan. NULL is accepted. */
+rc_status_t rc_plan_destroy(rc_plan_t plan);
+
+/* Bytes of one call's packed stream (all batch tensors), and of one tensor's
+ * slice of it. Layout, per tensor, each section starting at a multiple of 256
+ * bytes, tensors back to back (N = rows*cols, G = group):
+ *   Q1: sign bits [N/8] (element k = bit k%8 of byte k/8) | scale f32 [N/G]
+ *   Q2: codes [N/4] (element k = bits 2(k%4)..+1 of byte k/4) | {mn, step} f32 pairs [N/G]
+ *   NM: {v_i0, v_i1} bf16 pairs [N/16] | index byte i0 | i1<<4 [N/16], i0 < i1
+ *   LR: U nibbles [rows*rank/2] | V nibbles [cols*rank/2] | sU f32 [rank] | sV f32 [rank]
+ *       (row-major INT4, element t in nibble t, even t low, two's complement)
+ * Returns 0 for a NULL plan. */
+size_t rc_packed_bytes(rc_plan_t plan);
+size_t rc_tensor_packed_bytes(rc_plan_t plan);
+
+/* Device workspace owned by the plan (0 unless RC_LOWRANK). */
+size_t rc_workspace_bytes(rc_plan_t plan);
+
+/* Static description of a status code. */
+const char* rc_status_string(rc_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBRESCOMP_H */

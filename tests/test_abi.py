@@ -1,0 +1,116 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+public header declares, validates arguments before touching the device, and its
+packed-layout sizes agree with the oracle's independently written layout."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "librescomp.h")
+
+
+@pytest.fixture(scope="module")
+def rc():
+    from activation_residual_compression_amd import librescomp
+    return librescomp
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rc_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(rc):
+    names = declared_functions()
+    assert {"rc_plan_create", "rc_compress", "rc_decompress", "rc_plan_destroy"} <= set(names)
+    lib = ctypes.CDLL(rc.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(rc):
+    for s in range(5):
+        assert rc.rc_status_string(s).startswith("RC_")
+    assert "unknown" in rc.rc_status_string(99)
+
+
+@pytest.mark.parametrize("scheme,kw,bad", [
+    ("q1", dict(group=64), dict(group=0)),
+    ("q1", dict(group=64), dict(group=48)),          # unsupported group
+    ("q2", dict(group=128), dict(group=7)),
+    ("nm", dict(nm_keep=2, nm_block=16), dict(nm_keep=4)),
+    ("nm", dict(nm_keep=2, nm_block=16), dict(nm_block=1)),
+    ("lr", dict(rank=32, iters=2), dict(q0=None)),
+    ("lr", dict(rank=32, iters=2), dict(rank=24)),
+    ("lr", dict(rank=32, iters=2), dict(iters=0)),
+])
+def test_plan_validation(rc, scheme, kw, bad):
+    kw = dict(kw)
+    if scheme == "lr":
+        kw["q0"] = np.zeros((2, 256, 32), np.float32)
+    kw.update(bad)
+    with pytest.raises(rc.RcError) as ei:
+        rc.Plan((2, 128, 256), "bf16", scheme, **kw)
+    assert ei.value.status in (rc.RC_ERR_INVALID_ARG, rc.RC_ERR_UNSUPPORTED)
+
+
+def test_shape_validation(rc):
+    for shape in [(0, 8, 64), (1, 0, 64), (1, 8, 0), (1, 8, 96)]:
+        with pytest.raises(rc.RcError) as ei:
+            rc.Plan(shape, "bf16", "q2", group=128)
+        assert ei.value.status == rc.RC_ERR_INVALID_ARG
+    with pytest.raises(rc.RcError):
+        rc.Plan((1, 8, 64), 7, "q1", group=64)
+    with pytest.raises(rc.RcError) as ei:
+        rc.Plan((1, 8, 64), "f32", "q1", group=64, flags=1)
+    assert ei.value.status == rc.RC_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("scheme,kw,shape", [
+    ("q1", dict(group=64), (57, 1152, 3072)),
+    ("q1", dict(group=64), (30, 4444, 1920)),
+    ("q1", dict(group=32), (3, 7, 96)),
+    ("q2", dict(group=128), (57, 1152, 3072)),
+    ("q2", dict(group=64), (2, 5, 192)),
+    ("nm", dict(nm_keep=2, nm_block=16), (57, 1152, 3072)),
+    ("nm", dict(nm_keep=2, nm_block=16), (1, 3, 16)),
+])
+def test_packed_sizes_match_oracle_layout(rc, scheme, kw, shape):
+    with rc.Plan(shape, "bf16", scheme, **kw) as p:
+        b, n, m = shape
+        want = oracle.tensor_bytes(scheme, n, m, group=kw.get("group"))
+        assert p.tensor_packed_bytes == want
+        assert p.packed_bytes == b * want
+        assert p.workspace_bytes == 0
+
+
+def test_lowrank_packed_size_formula():
+    # the plan needs a device for its workspace; the byte count is the oracle's
+    assert sum(oracle.section_sizes("lr", 1152, 3072, rank=32)) == 67840
+    assert oracle.tensor_bytes("lr", 1152, 3072, rank=32) == 68096   # sections padded to 256 B
+    assert oracle.tensor_bytes("lr", 4444, 1920, rank=48) == 153344
+
+
+def test_compress_rejects_bad_pointers_without_launching(rc):
+    with rc.Plan((1, 8, 64), "f32", "q1", group=64) as p:
+        st = rc.rc_state_t(4096, 8192)
+        with pytest.raises(rc.RcError) as ei:
+            rc.rc_compress(p.handle, 0, 0, st, 4096)
+        assert ei.value.status == rc.RC_ERR_INVALID_ARG
+        with pytest.raises(rc.RcError) as ei:
+            rc.rc_compress(p.handle, 0, 4100, st, 4096)
+        assert ei.value.status == rc.RC_ERR_ALIGNMENT
+        with pytest.raises(rc.RcError) as ei:
+            rc.rc_decompress(p.handle, 0, 4096, 4104)
+        assert ei.value.status == rc.RC_ERR_ALIGNMENT
+        with pytest.raises(rc.RcError) as ei:
+            rc.rc_decompress(None, 0, 4096, 4096)
+        assert ei.value.status == rc.RC_ERR_INVALID_ARG
+    assert rc.rc_packed_bytes(None) == 0 and rc.rc_workspace_bytes(None) == 0
+    rc.rc_plan_destroy(None)

@@ -1,0 +1,135 @@
+"""GPU parity of the 1-bit, 2-bit and 2:16 paths against the CPU oracle.
+
+Every step is teacher-forced (the oracle starts from the GPU's previous ahat)
+and must match bit for bit: packed bytes (codes, scales, indices, values and
+padding), e_t and ahat_t; the receiver state must equal the sender's. Shapes
+span several kernel tiles with ragged tails; edge cases cover zero residuals,
+signed zeros, subnormal residuals, ties, constant groups, both input dtypes,
+and the full-size workloads (sampled tensors checked in full).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_harness import GpuRun, check_exact_step, lib_view_f32, oracle, say, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _kw(scheme, group):
+    if scheme == "nm":
+        return dict(nm_keep=2, nm_block=16), {}
+    return dict(group=group), dict(group=group)
+
+
+def _run_sequence(wl, scheme, group, tensors_checked=None, steps=None):
+    plan_kw, orc_kw = _kw(scheme, group)
+    run = GpuRun((wl.nb, wl.n, wl.m), wl.dtype, scheme, **plan_kw)
+    try:
+        _, a0 = wl.next()
+        run.warmup(a0)
+        ahat_prev = lib_view_f32(a0, wl.dtype).copy()
+        nsteps = wl.steps if steps is None else steps
+        for t in range(1, nsteps):
+            _, a = wl.next()
+            say("[gpu] %s step %d" % (scheme, t))
+            run.step(a)
+            packed, e, ahat, recon = run.fetch()
+            af = lib_view_f32(a, wl.dtype)
+            for b in (range(wl.nb) if tensors_checked is None else tensors_checked):
+                check_exact_step(run, b, af[b], ahat_prev[b], packed, e, ahat, recon, orc_kw)
+            ahat_prev = ahat
+    finally:
+        run.close()
+
+
+def test_tiny_fp32_q1_every_step():
+    """The tiny configuration: one fp32 256x64 matrix, 10 steps, 1-bit, group 64."""
+    _run_sequence(synth.make("tiny_q1"), "q1", 64)
+
+
+@pytest.mark.parametrize("scheme", ["q1", "q2"])
+@pytest.mark.parametrize("group", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quant_ragged_shapes(scheme, group, dtype):
+    if dtype == "bf16":
+        wl = synth.FluxWorkload(batch=3, n=37, m=384, steps=4)
+    else:
+        wl = synth.WalkWorkload(batch=3, n=37, m=384, steps=4)
+    _run_sequence(wl, scheme, group)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_nm_ragged_shapes(dtype):
+    if dtype == "bf16":
+        wl = synth.FluxWorkload(batch=3, n=41, m=208, steps=4)
+    else:
+        wl = synth.WalkWorkload(batch=3, n=41, m=208, steps=4)
+    _run_sequence(wl, "nm", None)
+
+
+def _crafted(n, m, seed):
+    """fp32 activations and a state whose residuals hold zeros of both signs,
+    subnormals, exact ties, constant groups and equal-magnitude blocks (rows
+    0-5 have ahat = 0, so r = a there exactly)."""
+    rng = np.random.default_rng(seed)
+    ahat = rng.standard_normal((n, m)).astype(np.float32)
+    a = rng.standard_normal((n, m)).astype(np.float32)
+    ahat[:6] = 0.0
+    a[0, :] = 0.0                                           # zero row
+    a[1, :64] = np.where(np.arange(64) % 2 == 0, 0.0, -0.0)  # -0 - (+0) = -0: signed zeros
+    a[2, :] = (rng.standard_normal(m) * 1e-39).astype(np.float32)   # subnormal residuals
+    a[3, :128] = 0.7                                        # constant group
+    a[4, :16] = 0.5                                         # all-equal 16-block (N:M ties)
+    a[4, 16:32] = np.array([1, -3, 3, 0, -3, 2, 0, 3, 1, 1, 0, -3, 2, 2, 0, 1], np.float32)
+    a[5, :128] = 0.0
+    a[5, 1], a[5, 2], a[5, 3], a[5, 4] = 3.0, 0.5, 1.5, 2.5  # 2-bit ties t = 0.5, 1.5, 2.5
+    return a, ahat
+
+
+@pytest.mark.parametrize("scheme,group", [("q1", 64), ("q2", 128), ("q1", 32), ("q2", 64), ("nm", None)])
+def test_crafted_edge_cases(scheme, group):
+    n, m = 6, 256
+    a, ahat = _crafted(n, m, seed=3)
+    plan_kw, orc_kw = _kw(scheme, group)
+    run = GpuRun((1, n, m), "f32", scheme, **plan_kw)
+    try:
+        run.set_state(ahat[None])
+        say("[gpu] crafted %s" % scheme)
+        run.step(a[None])
+        packed, e, ahat_g, recon = run.fetch()
+        o = check_exact_step(run, 0, a, ahat, packed, e, ahat_g, recon, orc_kw)
+        assert np.all(o["e"][0] == 0.0) and np.array_equal(o["ahat"][0], ahat[0])
+        assert np.isfinite(e).all() and np.isfinite(ahat_g).all()
+    finally:
+        run.close()
+
+
+@pytest.mark.parametrize("scheme,group", [("q1", 64), ("q2", 128), ("nm", None)])
+def test_zero_residual_everywhere(scheme, group):
+    wl = synth.FluxWorkload(batch=2, n=33, m=256, steps=1)
+    _, a0 = wl.next()
+    plan_kw, orc_kw = _kw(scheme, group)
+    run = GpuRun((2, 33, 256), "bf16", scheme, **plan_kw)
+    try:
+        run.warmup(a0)
+        run.step(a0)   # a_t == ahat: r = 0
+        packed, e, ahat, recon = run.fetch()
+        af = lib_view_f32(a0, "bf16")
+        for b in range(2):
+            check_exact_step(run, b, af[b], af[b], packed, e, ahat, recon, orc_kw)
+        assert not np.any(e) and np.array_equal(ahat, af)
+    finally:
+        run.close()
+
+
+@pytest.mark.parametrize("config", ["flux_q2", "flux_nm", "video_q1"])
+def test_full_size_sampled_tensors(config):
+    """Full batch at the evaluated sizes, 2 compressed steps; first, middle and
+    last tensor checked in full against the oracle."""
+    spec = synth.CONFIGS[config]
+    wl = synth.make(config, steps=3)
+    group = spec.get("group")
+    mid = wl.nb // 2
+    _run_sequence(wl, spec["scheme"], group, tensors_checked=[0, mid, wl.nb - 1])
+    torch.cuda.empty_cache()
