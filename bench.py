@@ -87,7 +87,7 @@ def measure(config, steps, warmup, max_frames, log):
     if spec["scheme"] == "lr":
         kw["q0"] = wl.q0(spec["rank"])
     plan = rc.Plan((B, n, m), wl.dtype, spec["scheme"], **kw)
-    ahat = frames[0].float().contiguous()
+    ahat = frames[0].float().clone()
     recon = ahat.clone()
     e = torch.zeros_like(ahat)
     packed = torch.empty(plan.packed_bytes, dtype=torch.uint8, device=dev)
