@@ -30,10 +30,12 @@ hipError_t launch_nm_decompress(const uint8_t* packed, float* ahat, int batch, c
                                 hipStream_t s);
 
 // Low-rank workspace, carved out of one device allocation by the plan.
-// ntiles = ceil(rows / 64); rows_pad = 64 * ntiles.
+// ntiles = ceil(rows / 64); rows_pad = 64 * ntiles; the R^T P product splits
+// the rows into nsplit chunks of split_rows (a multiple of 32).
 struct LowRankWork {
   int rank = 0, iters = 0;
   int64_t ntiles = 0, rows_pad = 0;
+  int nsplit = 1, split_rows = 0;
   uint16_t* R = nullptr;     // bf16 residual [batch][rows][cols]
   float* P = nullptr;        // fp32 panel [batch][rows][rank]
   uint16_t* Pbt = nullptr;   // bf16 orthonormal panel, transposed [batch][rank][rows_pad]
@@ -41,7 +43,10 @@ struct LowRankWork {
   uint16_t* Q0t = nullptr;   // bf16 start matrix, transposed [batch][rank][cols]
   uint16_t* Qtb = nullptr;   // bf16 Q^T for the next product [batch][rank][cols]
   float* gpart = nullptr;    // per-64-row-tile Gram partials [batch][ntiles][rank][rank]
+  float* gsum = nullptr;     // summed Gram matrices [batch][rank][rank]
   float* chol = nullptr;     // Cholesky factor + dead flags [batch][rank][rank + 1]
+  float* qpart = nullptr;    // R^T P partials [batch][nsplit][rank][cols]
+  uint32_t* amax = nullptr;  // column absmax bits of U and V [batch][2][rank]
 };
 
 hipError_t launch_lr_compress(bool bf16_input, const void* a, float* ahat, float* e,

@@ -9,22 +9,29 @@
 // their reconstruction.
 //
 // Per tensor (n = rows, m = cols, k = rank), with Q0 given:
-//   R = bf16(a_t - ahat)                                (fused into the 1st product)
+//   R = bf16(a_t - ahat)                          (fused into the first product)
 //   repeat iters times:
-//     P = R * bf16(Q)          bf16 MFMA, fp32 accumulate       [lr_rq_kernel]
-//     P = CQR(CQR(P))          CholeskyQR2 of the n x k panel   [lr_chol_kernel, lr_solve_kernel]
-//     Q = R^T * bf16(P)        bf16 MFMA via an LDS transpose   [lr_rtp_kernel]
-//   U = P, V = Q; per-column absmax INT4                       [lr_int4_kernel]
-//   c = Uq Vq^T (fp32 FMA chain, k ascending), e = r - c, ahat += c  [lr_recon_kernel]
-// CQR(P): G = P^T P (fp32 MFMA on 64-row tiles, partials summed in tile order),
-// G = L L^T (one wave, left-looking), P <- P L^{-T} (one lane per row). A pivot
-// <= 2^-23 * max(trace G, k * FLT_MIN) marks a dead column, whose P column is
-// zeroed, so zero or rank-deficient residuals never produce NaN.
+//     P = R * bf16(Q)        bf16 MFMA, fp32 accumulate            [lr_rq_kernel]
+//     P = CQR(CQR(P))        CholeskyQR2 of the n x k panel        [lr_gram_reduce_kernel,
+//                                                                    lr_chol_kernel, lr_solve_kernel]
+//     Q = R^T * bf16(P)      bf16 MFMA, R transposed through LDS   [lr_rtp_kernel, lr_qfinish_kernel]
+//   U = P, V = Q; per-column absmax INT4                          [lr_int4_kernel]
+//   c = Uq Vq^T (fp32 MFMA), e = r - c, ahat += c                 [lr_recon_kernel]
+// CQR(P): G = P^T P (fp32 MFMA on 64-row tiles, tile partials summed in tile
+// order), G = L L^T (one wave, left-looking), P <- P L^{-T} (one lane per row).
+// A pivot <= 2^-23 * max(trace G, k * FLT_MIN) marks a dead column, whose P
+// column is zeroed, so zero or rank-deficient residuals never produce NaN.
 //
-// All MFMA operand layouts follow the gfx950 register layout of
-// v_mfma_f32_16x16x32_bf16 (A: lane l holds A[l%16][8(l/16) .. +7], B: lane l
-// holds B[8(l/16) .. +7][l%16], D: lane l holds D[4(l/16) + t][l%16]) and of
-// v_mfma_f32_16x16x4_f32 (A[l%16][l/16], B[l/16][l%16], same D).
+// MFMA register layouts (gfx950):
+//   v_mfma_f32_16x16x32_bf16: A lane l holds A[l%16][8(l/16) .. +7],
+//     B lane l holds B[8(l/16) .. +7][l%16], D lane l holds D[4(l/16) + t][l%16];
+//   v_mfma_f32_16x16x4_f32: A[l%16][l/16], B[l/16][l%16], same D.
+// ds_read_b64_tr_b16: within each 16-lane group, lanes 4k..4k+3 point at four
+// consecutive 16-bit elements of "row k" (16 elements per row), and lane t of
+// the group receives element t of rows 0..3 (a 4 x 16 transpose).
+// A contraction index may be permuted freely as long as both operands use the
+// same permutation; the kernels use that to give each lane longer contiguous
+// runs of memory.
 #include <float.h>
 
 #include "device_common.hpp"
@@ -33,6 +40,8 @@
 namespace rc {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
@@ -48,7 +57,6 @@ constexpr int kTile = 64;  // rows per panel tile
 // Gram partial of a 64 x K tile held in LDS (row stride LD): G[a][b] for the
 // upper tile pairs (16-column blocks ta <= tb), fp32 MFMA over the 64 rows in
 // order, written to out[K][K] (entries of lower tile pairs are left untouched).
-// Waves of the block share the tile pairs.
 template <int K, int LD>
 __device__ __forceinline__ void tile_gram(const float* T, float* out, int nwaves) {
   constexpr int NT = K / 16;
@@ -68,25 +76,44 @@ __device__ __forceinline__ void tile_gram(const float* T, float* out, int nwaves
     }
 }
 
+__device__ __forceinline__ void load16_bf16(const uint16_t* p, F8& lo, F8& hi) {
+  load8<uint16_t>(p, lo);
+  load8<uint16_t>(p + 8, hi);
+}
+__device__ __forceinline__ u32x4 pack_r(const F8& x, const F8& h) {
+  u32x4 v;
+  v.x = bf16_rne(x.v[0] - h.v[0]) | (bf16_rne(x.v[1] - h.v[1]) << 16);
+  v.y = bf16_rne(x.v[2] - h.v[2]) | (bf16_rne(x.v[3] - h.v[3]) << 16);
+  v.z = bf16_rne(x.v[4] - h.v[4]) | (bf16_rne(x.v[5] - h.v[5]) << 16);
+  v.w = bf16_rne(x.v[6] - h.v[6]) | (bf16_rne(x.v[7] - h.v[7]) << 16);
+  return v;
+}
+
 // ---------------------------------------------------------------- P = R * Q
-// Block: 64 rows of one tensor; 4 waves split the K-steps (32 columns each,
-// interleaved) and their partial products are summed through LDS in a fixed
-// order. FROM_A: R is formed here from a_t and ahat and written out for the
-// later passes.
+// Block: 64 rows of one tensor (4 row fragments of 16); the 4 waves split the
+// 64-column K-steps (interleaved) and their products are summed through LDS
+// in a fixed order. In a K-step lane group g = l/16 owns columns
+// [64 ks + 16 g, +16): one 32-byte bf16 run that feeds two MFMAs (its first
+// and second 8 columns), so every row is read as whole 128-byte lines.
+// FROM_A: R is formed here from a_t and ahat and written out for later passes.
+// Block (0, b) clears the tensor's INT4 absmax slots, which the last solve and
+// the last Q sum of the iteration fill.
 template <typename IN, bool FROM_A, int K>
 __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
                                                     const float* __restrict__ ahat,
                                                     uint16_t* __restrict__ R,
                                                     const uint16_t* __restrict__ Qtb,
                                                     float* __restrict__ P, float* __restrict__ gpart,
-                                                    int n, int m, int ntiles) {
+                                                    uint32_t* __restrict__ amax, int n, int m,
+                                                    int ntiles) {
   constexpr int NT = K / 16;
   constexpr int LD = K + 1;
   __shared__ float red[2][kTile * LD];
   const int b = blockIdx.y, tile = blockIdx.x, row0 = tile * kTile;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
-  const int nks = m / 32;
+  const int nks = m / 64;
   const uint16_t* Qb = Qtb + (size_t)b * K * m;
+  if (tile == 0 && threadIdx.x < 2 * K) amax[(size_t)b * 2 * K + threadIdx.x] = 0u;
 
   f32x4 acc[4][NT];
 #pragma unroll
@@ -95,33 +122,39 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
     for (int g = 0; g < NT; ++g) acc[f][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int ks = w; ks < nks; ks += 4) {
-    const int c0 = ks * 32 + lk * 8;
-    u32x4 A[4];
+    const int c0 = ks * 64 + lk * 16;
+    u32x4 A0[4], A1[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       const int row = row0 + 16 * f + lr;
       const int rcl = row < n ? row : n - 1;
       const size_t off = ((size_t)b * n + rcl) * m + c0;
       if constexpr (FROM_A) {
-        F8 x, h;
-        load8<IN>(a + off, x);
-        load8<float>(ahat + off, h);
-        u32x4 v;
-        v.x = bf16_rne(x.v[0] - h.v[0]) | (bf16_rne(x.v[1] - h.v[1]) << 16);
-        v.y = bf16_rne(x.v[2] - h.v[2]) | (bf16_rne(x.v[3] - h.v[3]) << 16);
-        v.z = bf16_rne(x.v[4] - h.v[4]) | (bf16_rne(x.v[5] - h.v[5]) << 16);
-        v.w = bf16_rne(x.v[6] - h.v[6]) | (bf16_rne(x.v[7] - h.v[7]) << 16);
-        if (row < n) *reinterpret_cast<u32x4*>(R + off) = v;
-        A[f] = v;
+        F8 x0, x1, h0, h1;
+        load8<IN>(a + off, x0);
+        load8<IN>(a + off + 8, x1);
+        load8<float>(ahat + off, h0);
+        load8<float>(ahat + off + 8, h1);
+        A0[f] = pack_r(x0, h0);
+        A1[f] = pack_r(x1, h1);
+        if (row < n) {
+          reinterpret_cast<u32x4*>(R + off)[0] = A0[f];
+          reinterpret_cast<u32x4*>(R + off)[1] = A1[f];
+        }
       } else {
-        A[f] = *reinterpret_cast<const u32x4*>(R + off);
+        A0[f] = reinterpret_cast<const u32x4*>(R + off)[0];
+        A1[f] = reinterpret_cast<const u32x4*>(R + off)[1];
       }
     }
 #pragma unroll
     for (int g = 0; g < NT; ++g) {
-      const u32x4 Bv = *reinterpret_cast<const u32x4*>(Qb + (size_t)(16 * g + lr) * m + c0);
+      const u32x4* q = reinterpret_cast<const u32x4*>(Qb + (size_t)(16 * g + lr) * m + c0);
+      const u32x4 B0 = q[0], B1 = q[1];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) acc[f][g] = mfma_bf16(A[f], Bv, acc[f][g]);
+      for (int f = 0; f < 4; ++f) {
+        acc[f][g] = mfma_bf16(A0[f], B0, acc[f][g]);
+        acc[f][g] = mfma_bf16(A1[f], B1, acc[f][g]);
+      }
     }
   }
 
@@ -168,68 +201,81 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
   tile_gram<K, LD>(T, gpart + ((size_t)b * ntiles + tile) * K * K, 4);
 }
 
-// ---------------------------------------------------------------- Cholesky
-// One block per tensor: sum the tile partials of G in tile order, then the
-// left-looking Cholesky on one wave (lane i owns row i), with the dead-column
-// rule. Output chol[K][K+1]: L (lower triangle; L[j][j] = 1 for dead j) and,
-// in column K, 1.0 for dead columns.
+// ---------------------------------------------------------------- Gram sum
+// gsum[b] = sum of the tile partials, in tile order (four interleaved running
+// sums, combined as (s0 + s1) + (s2 + s3)); one lane per entry.
 template <int K>
-__global__ __launch_bounds__(256) void lr_chol_kernel(const float* __restrict__ gpart,
-                                                      float* __restrict__ chol, int ntiles) {
+__global__ __launch_bounds__(256) void lr_gram_reduce_kernel(const float* __restrict__ gpart,
+                                                             float* __restrict__ gsum, int ntiles) {
+  const int b = blockIdx.y;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= K * K) return;
+  const float* gp = gpart + (size_t)b * ntiles * K * K + idx;
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  int p = 0;
+  for (; p + 4 <= ntiles; p += 4)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] += gp[(size_t)(p + q) * K * K];
+  for (int q = 0; p < ntiles; ++p, ++q) s[q] += gp[(size_t)p * K * K];
+  gsum[(size_t)b * K * K + idx] = (s[0] + s[1]) + (s[2] + s[3]);
+}
+
+// ---------------------------------------------------------------- Cholesky
+// One wave per tensor: left-looking Cholesky of G (upper triangle of gsum),
+// lane i owns row i, with the dead-column rule. Output chol[K][K+1]: L (lower
+// triangle; L[j][j] = 1 for dead j) and, in column K, 1.0 for dead columns.
+template <int K>
+__global__ __launch_bounds__(64) void lr_chol_kernel(const float* __restrict__ gsum,
+                                                     float* __restrict__ chol) {
   constexpr int LD = K + 1;
   __shared__ float G[K * LD];
   __shared__ float L[K * LD];
   const int b = blockIdx.x;
-  const float* gp = gpart + (size_t)b * ntiles * K * K;
-  for (int idx = threadIdx.x; idx < K * K; idx += blockDim.x) {
+  const int lane = threadIdx.x;
+  const float* gs = gsum + (size_t)b * K * K;
+  for (int idx = lane; idx < K * K; idx += 64) {
     const int i = idx / K, j = idx % K;
-    if (i > j) continue;
-    float s = 0.f;
-    for (int p = 0; p < ntiles; ++p) s += gp[(size_t)p * K * K + idx];
-    G[i * LD + j] = s;
-    G[j * LD + i] = s;
+    G[i * LD + j] = gs[i <= j ? idx : j * K + i];
   }
-  for (int idx = threadIdx.x; idx < K * LD; idx += blockDim.x) L[idx] = 0.f;
+  for (int idx = lane; idx < K * LD; idx += 64) L[idx] = 0.f;
   __syncthreads();
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    float tr = lane < K ? G[lane * LD + lane] : 0.f;
+  float tr = lane < K ? G[lane * LD + lane] : 0.f;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) tr += __shfl_xor(tr, o);
-    const float tol = ldexpf(fmaxf(tr, (float)K * FLT_MIN), -23);
-    uint64_t dead = 0;
-    for (int j = 0; j < K; ++j) {
-      float s = 0.f;
-      if (lane >= j && lane < K) {
-        s = G[lane * LD + j];
-        for (int p = 0; p < j; ++p) s -= L[lane * LD + p] * L[j * LD + p];
-      }
-      const float piv = __shfl(s, j);
-      const bool dj = !(piv > tol);
-      const float ljj = dj ? 1.0f : sqrtf(piv);
-      if (lane == j) L[j * LD + j] = ljj;
-      if (lane > j && lane < K) L[lane * LD + j] = dj ? 0.f : s / ljj;
-      if (dj) dead |= (uint64_t)1 << j;
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-      __builtin_amdgcn_wave_barrier();
+  for (int o = 32; o >= 1; o >>= 1) tr += __shfl_xor(tr, o);
+  const float tol = ldexpf(fmaxf(tr, (float)K * FLT_MIN), -23);
+  uint64_t dead = 0;
+  for (int j = 0; j < K; ++j) {
+    float s = 0.f;
+    if (lane >= j && lane < K) {
+      s = G[lane * LD + j];
+      for (int p = 0; p < j; ++p) s -= L[lane * LD + p] * L[j * LD + p];
     }
-    if (lane < K) L[lane * LD + K] = ((dead >> lane) & 1) ? 1.f : 0.f;
+    const float piv = __shfl(s, j);
+    const bool dj = !(piv > tol);
+    const float ljj = dj ? 1.0f : sqrtf(piv);
+    if (lane == j) L[j * LD + j] = ljj;
+    if (lane > j && lane < K) L[lane * LD + j] = dj ? 0.f : s / ljj;
+    if (dj) dead |= (uint64_t)1 << j;
+    __syncthreads();
   }
+  if (lane < K) L[lane * LD + K] = ((dead >> lane) & 1) ? 1.f : 0.f;
   __syncthreads();
   float* out = chol + (size_t)b * K * LD;
-  for (int idx = threadIdx.x; idx < K * LD; idx += blockDim.x) out[idx] = L[idx];
+  for (int idx = lane; idx < K * LD; idx += 64) out[idx] = L[idx];
 }
 
 // ---------------------------------------------------------------- P <- P L^-T
 // One wave per 64-row tile, one lane per row: forward substitution x L^T = p.
 // GRAM: also write the Gram partial of the solved tile (next CQR pass).
 // FINAL: also write the bf16 transposed panel used by the R^T P product
-// (rows n .. rows_pad-1 written as 0).
+// (rows n .. rows_pad-1 written as 0) and fold the column absmax of the tile
+// into amax[b][0][*] (the INT4 scales of U).
 template <int K, bool GRAM, bool FINAL>
 __global__ __launch_bounds__(64) void lr_solve_kernel(float* __restrict__ P,
                                                       const float* __restrict__ chol,
                                                       float* __restrict__ gpart,
-                                                      uint16_t* __restrict__ Pbt, int n,
+                                                      uint16_t* __restrict__ Pbt,
+                                                      uint32_t* __restrict__ amax, int n,
                                                       int ntiles, int rows_pad) {
   constexpr int LD = K + 1;
   __shared__ float Ls[K * LD];
@@ -259,42 +305,50 @@ __global__ __launch_bounds__(64) void lr_solve_kernel(float* __restrict__ P,
 #pragma unroll
     for (int j = 0; j < K; j += 4) *reinterpret_cast<f32x4*>(prow + j) = f32x4{x[j], x[j + 1], x[j + 2], x[j + 3]};
   }
+#pragma unroll
+  for (int j = 0; j < K; ++j) T[lane * LD + j] = x[j];  // x = 0 for rows past n
+  __syncthreads();
   if constexpr (FINAL) {
     if (row < rows_pad) {
       uint16_t* dst = Pbt + (size_t)b * K * rows_pad + row;
 #pragma unroll
       for (int j = 0; j < K; ++j) dst[(size_t)j * rows_pad] = valid ? (uint16_t)bf16_rne(x[j]) : (uint16_t)0;
     }
+    if (lane < K) {
+      float mx = 0.f;
+      for (int r = 0; r < kTile; ++r) mx = fmaxf(mx, fabsf(T[r * LD + lane]));
+      atomicMax(amax + (size_t)b * 2 * K + lane, __float_as_uint(mx));
+    }
   }
-  if constexpr (GRAM) {
-#pragma unroll
-    for (int j = 0; j < K; ++j) T[lane * LD + j] = x[j];  // x = 0 for rows past n
-    __syncthreads();
-    tile_gram<K, LD>(T, gpart + ((size_t)b * ntiles + tile) * K * K, 1);
-  }
+  if constexpr (GRAM) tile_gram<K, LD>(T, gpart + ((size_t)b * ntiles + tile) * K * K, 1);
 }
 
 // ---------------------------------------------------------------- Q = R^T P
-// Block: 64 columns of one tensor, all rows; each wave owns 16 columns. Per
-// step of 32 rows the R tile [32 x 64] is staged through LDS (double buffered)
-// and read back column-wise to form the MFMA A operand (A[c][i] = R[i][c]).
-// Output written transposed: Qt[j][c] (fp32, for V) and Qtb (bf16, next product).
+// Block: 64 columns x one row split of one tensor; each wave owns 16 columns.
+// Per step of 32 rows the R tile [32 x 64] is staged through LDS (double
+// buffered, one barrier per step) and read back transposed with
+// ds_read_b64_tr_b16 to form the MFMA A operand A[c][i] = R[i][c]. The split's
+// partial Q^T goes to qpart; lr_qfinish_kernel sums the splits.
 constexpr int kRtpCols = 64;
-constexpr int kRtpLd = kRtpCols + 8;  // bf16 elements per LDS row
+constexpr int kRtpLd = kRtpCols + 8;  // bf16 elements per LDS row (144 B)
 
 template <int K>
 __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict__ R,
                                                      const uint16_t* __restrict__ Pbt,
-                                                     float* __restrict__ Qt,
-                                                     uint16_t* __restrict__ Qtb, int n, int m,
-                                                     int rows_pad) {
+                                                     float* __restrict__ qpart, int n, int m,
+                                                     int rows_pad, int nsplit, int split_rows) {
   constexpr int NT = K / 16;
   __shared__ __attribute__((aligned(16))) uint16_t sR[2][32 * kRtpLd];
-  const int b = blockIdx.y, c0 = blockIdx.x * kRtpCols;
+  const int b = blockIdx.z, split = blockIdx.y, c0 = blockIdx.x * kRtpCols;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
   const int ld_row = threadIdx.x >> 3, ld_col = (threadIdx.x & 7) * 8;
+  const int i_begin = split * split_rows;
+  const int i_end = min(rows_pad, i_begin + split_rows);
   const uint16_t* Rb = R + (size_t)b * n * m;
   const uint16_t* Pb = Pbt + (size_t)b * K * rows_pad;
+  // transposed-read address of this lane inside a staged tile: group lk,
+  // row 8 lk + (lr / 4) (+4 for the second read), columns 16 w + 4 (lr % 4)
+  const int tr_off = (8 * lk + (lr >> 2)) * kRtpLd + 16 * w + 4 * (lr & 3);
 
   auto gload = [&](int i0) {
     int row = i0 + ld_row;
@@ -305,18 +359,19 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
 #pragma unroll
   for (int g = 0; g < NT; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 next = gload(0);
+  u32x4 next = gload(i_begin);
   int buf = 0;
-  for (int i0 = 0; i0 < rows_pad; i0 += 32, buf ^= 1) {
+  for (int i0 = i_begin; i0 < i_end; i0 += 32, buf ^= 1) {
     *reinterpret_cast<u32x4*>(&sR[buf][ld_row * kRtpLd + ld_col]) = next;
     __syncthreads();
-    if (i0 + 32 < rows_pad) next = gload(i0 + 32);
-    const uint16_t* base = &sR[buf][(8 * lk) * kRtpLd + 16 * w + lr];
+    if (i0 + 32 < i_end) next = gload(i0 + 32);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)&sR[buf][tr_off]);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)&sR[buf][tr_off + 4 * kRtpLd]);
     u32x4 A;
-    A.x = (uint32_t)base[0 * kRtpLd] | ((uint32_t)base[1 * kRtpLd] << 16);
-    A.y = (uint32_t)base[2 * kRtpLd] | ((uint32_t)base[3 * kRtpLd] << 16);
-    A.z = (uint32_t)base[4 * kRtpLd] | ((uint32_t)base[5 * kRtpLd] << 16);
-    A.w = (uint32_t)base[6 * kRtpLd] | ((uint32_t)base[7 * kRtpLd] << 16);
+    A.x = (uint32_t)(uint16_t)lo.x | ((uint32_t)(uint16_t)lo.y << 16);
+    A.y = (uint32_t)(uint16_t)lo.z | ((uint32_t)(uint16_t)lo.w << 16);
+    A.z = (uint32_t)(uint16_t)hi.x | ((uint32_t)(uint16_t)hi.y << 16);
+    A.w = (uint32_t)(uint16_t)hi.z | ((uint32_t)(uint16_t)hi.w << 16);
 #pragma unroll
     for (int g = 0; g < NT; ++g) {
       const u32x4 Bv = *reinterpret_cast<const u32x4*>(Pb + (size_t)(16 * g + lr) * rows_pad + i0 + 8 * lk);
@@ -325,91 +380,98 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
   }
   // D[c][j]: lane holds c = c0 + 16w + 4lk + t, j = 16g + lr
   const int c = c0 + 16 * w + 4 * lk;
+  float* qp = qpart + ((size_t)b * nsplit + split) * K * m;
 #pragma unroll
-  for (int g = 0; g < NT; ++g) {
-    const size_t o = ((size_t)b * K + 16 * g + lr) * m + c;
-    *reinterpret_cast<f32x4*>(Qt + o) = acc[g];
+  for (int g = 0; g < NT; ++g) *reinterpret_cast<f32x4*>(qp + (size_t)(16 * g + lr) * m + c) = acc[g];
+}
+
+// Sum the row splits in split order: Qt (fp32, V of the factorisation), Qtb
+// (bf16 operand of the next product), and the column absmax of V folded into
+// amax[b][1][j]. Block: one j, 1024 columns (4 per lane).
+template <int K>
+__global__ __launch_bounds__(256) void lr_qfinish_kernel(const float* __restrict__ qpart,
+                                                         float* __restrict__ Qt,
+                                                         uint16_t* __restrict__ Qtb,
+                                                         uint32_t* __restrict__ amax, int m,
+                                                         int nsplit) {
+  const int b = blockIdx.z, j = blockIdx.x;
+  const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
+  float mx = 0.f;
+  if (c < m) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < nsplit; ++sp)
+      s += *reinterpret_cast<const f32x4*>(qpart + (((size_t)b * nsplit + sp) * K + j) * m + c);
+    const size_t o = ((size_t)b * K + j) * m + c;
+    *reinterpret_cast<f32x4*>(Qt + o) = s;
     uint2 hb;
-    hb.x = bf16_rne(acc[g][0]) | (bf16_rne(acc[g][1]) << 16);
-    hb.y = bf16_rne(acc[g][2]) | (bf16_rne(acc[g][3]) << 16);
+    hb.x = bf16_rne(s.x) | (bf16_rne(s.y) << 16);
+    hb.y = bf16_rne(s.z) | (bf16_rne(s.w) << 16);
     *reinterpret_cast<uint2*>(Qtb + o) = hb;
+    mx = fmaxf(fmaxf(fabsf(s.x), fabsf(s.y)), fmaxf(fabsf(s.z), fabsf(s.w)));
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((threadIdx.x & 63) == 0) atomicMax(amax + ((size_t)b * 2 + 1) * K + j, __float_as_uint(mx));
 }
 
 // ---------------------------------------------------------------- INT4 factors
-// Block x = 0: U from P [n][K]; x = 1: V from Qt [K][m]. Per column j:
-// s_j = absmax_j / 7, q = clamp(rint_even(x / s_j), -7, 7) (0 when s_j = 0),
-// packed row-major, element t in nibble t (even t low), two's complement.
+// One lane per factor row: rows 0..n-1 are U (= P, [n][K]), rows n..n+m-1 are V
+// (= Q, stored as Qt [K][m]). Per column j: s_j = absmax_j / 7,
+// q = clamp(rint_even(x / s_j), -7, 7) (0 when s_j = 0), packed row-major,
+// element t in nibble t (even t low), two's complement. Block 0 writes the
+// scale sections and zeroes the section padding.
 template <int K>
 __global__ __launch_bounds__(256) void lr_int4_kernel(const float* __restrict__ P,
                                                       const float* __restrict__ Qt,
+                                                      const uint32_t* __restrict__ amax,
                                                       uint8_t* __restrict__ packed, Layout L) {
-  __shared__ float red[4][K];
-  __shared__ float scale[K];
+  __shared__ float sc[2 * K];
   const int b = blockIdx.y;
-  const bool isV = blockIdx.x == 1;
   const int n = (int)L.rows, m = (int)L.cols;
-  const int rows = isV ? m : n;
-  const float* Pb = P + (size_t)b * n * K;
-  const float* Qb = Qt + (size_t)b * K * m;
   uint8_t* pk = packed + (size_t)b * L.tstride;
-  uint8_t* nib = pk + (isV ? L.sec_off[1] : L.sec_off[0]);
-  float* sc = reinterpret_cast<float*>(pk + (isV ? L.sec_off[3] : L.sec_off[2]));
-  auto val = [&](int i, int j) { return isV ? Qb[(size_t)j * m + i] : Pb[(size_t)i * K + j]; };
-
-  float amax[K];
+  if (threadIdx.x < 2 * K) sc[threadIdx.x] = __uint_as_float(amax[(size_t)b * 2 * K + threadIdx.x]) / 7.0f;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    float* su = reinterpret_cast<float*>(pk + L.sec_off[2]);
+    float* sv = reinterpret_cast<float*>(pk + L.sec_off[3]);
+    if (threadIdx.x < K) su[threadIdx.x] = sc[threadIdx.x];
+    else if (threadIdx.x < 2 * K) sv[threadIdx.x - K] = sc[threadIdx.x];
+    for (int s = 0; s < L.nsec; ++s) {
+      const int64_t start = L.sec_off[s] + L.sec_len[s];
+      const int64_t end = (s + 1 < L.nsec) ? L.sec_off[s + 1] : L.tstride;
+      for (int64_t i = start + threadIdx.x; i < end; i += blockDim.x) pk[i] = 0;
+    }
+  }
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n + m) return;
+  const bool isV = r >= n;
+  const int i = isV ? r - n : r;
+  const float* s = sc + (isV ? K : 0);
+  const float* src = isV ? Qt + (size_t)b * K * m + i : P + ((size_t)b * n + i) * K;
+  const size_t stride = isV ? (size_t)m : 1;
+  uint32_t words[K / 8];
 #pragma unroll
-  for (int j = 0; j < K; ++j) amax[j] = 0.f;
-  for (int i = threadIdx.x; i < rows; i += blockDim.x)
-#pragma unroll
-    for (int j = 0; j < K; ++j) amax[j] = fmaxf(amax[j], fabsf(val(i, j)));
-  const int w = threadIdx.x >> 6;
+  for (int q = 0; q < K / 8; ++q) words[q] = 0;
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    float v = amax[j];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    if ((threadIdx.x & 63) == 0) red[w][j] = v;
+    float qv = 0.f;
+    if (s[j] > 0.f) qv = fminf(fmaxf(rintf(src[j * stride] / s[j]), -7.f), 7.f);
+    words[j / 8] |= ((uint32_t)((int)qv) & 0xFu) << (4 * (j % 8));
   }
-  __syncthreads();
-  if (threadIdx.x < K) {
-    const int j = threadIdx.x;
-    const float am = fmaxf(fmaxf(red[0][j], red[1][j]), fmaxf(red[2][j], red[3][j]));
-    const float s = am / 7.0f;
-    scale[j] = s;
-    sc[j] = s;
-  }
-  // zero the section padding of this half (U: gaps after sections 0 and 2; V: 1 and 3)
-  for (int sidx = isV ? 1 : 0; sidx < 4; sidx += 2) {
-    const int64_t start = L.sec_off[sidx] + L.sec_len[sidx];
-    const int64_t end = (sidx + 1 < L.nsec) ? L.sec_off[sidx + 1] : L.tstride;
-    for (int64_t i = start + threadIdx.x; i < end; i += blockDim.x) pk[i] = 0;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < rows; i += blockDim.x) {
-    uint32_t words[K / 8];
+  uint32_t* dst = reinterpret_cast<uint32_t*>(pk + (isV ? L.sec_off[1] : L.sec_off[0]) + (size_t)i * (K / 2));
 #pragma unroll
-    for (int q = 0; q < K / 8; ++q) words[q] = 0;
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const float s = scale[j];
-      float qv = 0.f;
-      if (s > 0.f) qv = fminf(fmaxf(rintf(val(i, j) / s), -7.f), 7.f);
-      const uint32_t code = (uint32_t)((int)qv) & 0xFu;
-      words[j / 8] |= code << (4 * (j % 8));
-    }
-    uint32_t* dst = reinterpret_cast<uint32_t*>(nib + (size_t)i * (K / 2));
-#pragma unroll
-    for (int q = 0; q < K / 8; ++q) dst[q] = words[q];
-  }
+  for (int q = 0; q < K / 8; ++q) dst[q] = words[q];
 }
 
 // ---------------------------------------------------------------- reconstruct
-// c = Uq Vq^T on a 32 x 128 tile: the INT4 factors of the tile are decoded into
-// LDS (Us[32][K], Vt[K][128]), each lane accumulates 2 rows x 8 columns as an
-// fp32 FMA chain over k ascending. SENDER: r = a - ahat, e = r - c, ahat += c.
-// Receiver: ahat += c. Both run this same code, so both get the same c.
-constexpr int kRcRows = 32, kRcCols = 128;
+// c = Uq Vq^T on a 64 x 64 tile with fp32 MFMA. The INT4 factors of the tile
+// are decoded into LDS (Us[64][K], Vs[64][K]); wave w computes rows 16w..16w+15
+// as c^T = Vq Uq^T, so each lane ends with 8 consecutive columns of one row in
+// each half of the tile (the MFMA M index is mapped to columns so that the two
+// 16-column MFMA tiles of a half interleave in groups of 4).
+// SENDER: r = a - ahat, e = r - c, ahat += c. Receiver: ahat += c. Both run
+// this same code, so both get the same c bit for bit.
+constexpr int kRc = 64;
 
 __device__ __forceinline__ float int4_at(const uint8_t* nib, int64_t t) {
   const uint32_t byte = nib[t >> 1];
@@ -423,53 +485,47 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
                                                        float* __restrict__ e,
                                                        const uint8_t* __restrict__ packed,
                                                        Layout L) {
-  __shared__ float Us[kRcRows][K];
-  __shared__ __attribute__((aligned(16))) float Vt[K][kRcCols];
+  constexpr int LD = K + 1;
+  __shared__ float Us[kRc * LD];
+  __shared__ float Vs[kRc * LD];
   const int b = blockIdx.y;
   const int n = (int)L.rows, m = (int)L.cols;
-  const int ncol_tiles = (m + kRcCols - 1) / kRcCols;
-  const int r0 = (blockIdx.x / ncol_tiles) * kRcRows, c0 = (blockIdx.x % ncol_tiles) * kRcCols;
+  const int ncol_tiles = m / kRc;
+  const int r0 = (blockIdx.x / ncol_tiles) * kRc, c0 = (blockIdx.x % ncol_tiles) * kRc;
   const uint8_t* pk = packed + (size_t)b * L.tstride;
   const uint8_t* un = pk + L.sec_off[0];
   const uint8_t* vn = pk + L.sec_off[1];
   const float* su = reinterpret_cast<const float*>(pk + L.sec_off[2]);
   const float* sv = reinterpret_cast<const float*>(pk + L.sec_off[3]);
-  for (int idx = threadIdx.x; idx < kRcRows * K; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < kRc * K; idx += blockDim.x) {
     const int r = idx / K, j = idx % K;
     const int row = r0 + r;
-    Us[r][j] = row < n ? int4_at(un, (int64_t)row * K + j) * su[j] : 0.f;
-  }
-  for (int idx = threadIdx.x; idx < kRcCols * K; idx += blockDim.x) {
-    const int j = idx / kRcCols, c = idx % kRcCols;
-    const int col = c0 + c;
-    Vt[j][c] = col < m ? int4_at(vn, (int64_t)col * K + j) * sv[j] : 0.f;
+    Us[r * LD + j] = row < n ? int4_at(un, (int64_t)row * K + j) * su[j] : 0.f;
+    Vs[r * LD + j] = int4_at(vn, (int64_t)(c0 + r) * K + j) * sv[j];
   }
   __syncthreads();
-  const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
-  float acc[2][8];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
+  f32x4 acc[4];
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int p = 0; p < 4; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // MFMA tile p covers local columns 32 (p/2) + 8 (m/4) + 4 (p%2) + m%4, m = 0..15
+  int vcol[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[s][i] = 0.f;
+  for (int p = 0; p < 4; ++p) vcol[p] = 32 * (p >> 1) + 8 * (lr >> 2) + 4 * (p & 1) + (lr & 3);
 #pragma unroll 4
-  for (int j = 0; j < K; ++j) {
-    const float u0 = Us[ty][j], u1 = Us[ty + 16][j];
-    const f32x4 va = *reinterpret_cast<const f32x4*>(&Vt[j][8 * tx]);
-    const f32x4 vb = *reinterpret_cast<const f32x4*>(&Vt[j][8 * tx + 4]);
-    const float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+  for (int k0 = 0; k0 < K; k0 += 4) {
+    const float bu = Us[(16 * w + lr) * LD + k0 + lk];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      acc[0][i] = fmaf(u0, v[i], acc[0][i]);
-      acc[1][i] = fmaf(u1, v[i], acc[1][i]);
-    }
+    for (int p = 0; p < 4; ++p) acc[p] = mfma_f32(Vs[vcol[p] * LD + k0 + lk], bu, acc[p]);
   }
-  const int col = c0 + 8 * tx;
-  if (col >= m) return;
+  const int row = r0 + 16 * w + lr;
+  if (row >= n) return;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int row = r0 + ty + 16 * s;
-    if (row >= n) continue;
+  for (int half = 0; half < 2; ++half) {
+    const int col = c0 + 32 * half + 8 * lk;
     const size_t off = ((size_t)b * n + row) * m + col;
+    const f32x4 cl = acc[2 * half], ch = acc[2 * half + 1];
+    const float c[8] = {cl.x, cl.y, cl.z, cl.w, ch.x, ch.y, ch.z, ch.w};
     F8 h;
     load8<float>(ahat + off, h);
     if constexpr (SENDER) {
@@ -478,13 +534,13 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float r = x.v[i] - h.v[i];
-        ev.v[i] = r - acc[s][i];
-        h.v[i] = h.v[i] + acc[s][i];
+        ev.v[i] = r - c[i];
+        h.v[i] = h.v[i] + c[i];
       }
       store8_nt(e + off, ev);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) h.v[i] = h.v[i] + acc[s][i];
+      for (int i = 0; i < 8; ++i) h.v[i] = h.v[i] + c[i];
     }
     store8(ahat + off, h);
   }
@@ -492,6 +548,20 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
 
 // ---------------------------------------------------------------- launchers
 namespace {
+
+template <int K>
+void cqr_pass(const LowRankWork& w, int n, int B, bool final_pass, hipStream_t s) {
+  const int nt = (int)w.ntiles, rp = (int)w.rows_pad;
+  hipLaunchKernelGGL((lr_gram_reduce_kernel<K>), dim3((K * K + 255) / 256, B), dim3(256), 0, s,
+                     w.gpart, w.gsum, nt);
+  hipLaunchKernelGGL((lr_chol_kernel<K>), dim3(B), dim3(64), 0, s, w.gsum, w.chol);
+  if (final_pass)
+    hipLaunchKernelGGL((lr_solve_kernel<K, false, true>), dim3(nt, B), dim3(64), 0, s, w.P, w.chol,
+                       w.gpart, w.Pbt, w.amax, n, nt, rp);
+  else
+    hipLaunchKernelGGL((lr_solve_kernel<K, true, false>), dim3(nt, B), dim3(64), 0, s, w.P, w.chol,
+                       w.gpart, w.Pbt, w.amax, n, nt, rp);
+}
 
 template <int K>
 hipError_t lr_compress_k(bool bf16, const void* a, float* ahat, float* e, uint8_t* packed, int B,
@@ -503,26 +573,27 @@ hipError_t lr_compress_k(bool bf16, const void* a, float* ahat, float* e, uint8_
     if (it == 0) {
       if (bf16)
         hipLaunchKernelGGL((lr_rq_kernel<uint16_t, true, K>), tiles, dim3(256), 0, s,
-                           static_cast<const uint16_t*>(a), ahat, w.R, w.Q0t, w.P, w.gpart, n, m, nt);
+                           static_cast<const uint16_t*>(a), ahat, w.R, w.Q0t, w.P, w.gpart, w.amax,
+                           n, m, nt);
       else
         hipLaunchKernelGGL((lr_rq_kernel<float, true, K>), tiles, dim3(256), 0, s,
-                           static_cast<const float*>(a), ahat, w.R, w.Q0t, w.P, w.gpart, n, m, nt);
+                           static_cast<const float*>(a), ahat, w.R, w.Q0t, w.P, w.gpart, w.amax,
+                           n, m, nt);
     } else {
       hipLaunchKernelGGL((lr_rq_kernel<uint16_t, false, K>), tiles, dim3(256), 0, s,
                          (const uint16_t*)nullptr, (const float*)nullptr, w.R, w.Qtb, w.P, w.gpart,
-                         n, m, nt);
+                         w.amax, n, m, nt);
     }
-    hipLaunchKernelGGL((lr_chol_kernel<K>), dim3(B), dim3(256), 0, s, w.gpart, w.chol, nt);
-    hipLaunchKernelGGL((lr_solve_kernel<K, true, false>), tiles, dim3(64), 0, s, w.P, w.chol,
-                       w.gpart, w.Pbt, n, nt, rp);
-    hipLaunchKernelGGL((lr_chol_kernel<K>), dim3(B), dim3(256), 0, s, w.gpart, w.chol, nt);
-    hipLaunchKernelGGL((lr_solve_kernel<K, false, true>), tiles, dim3(64), 0, s, w.P, w.chol,
-                       w.gpart, w.Pbt, n, nt, rp);
-    hipLaunchKernelGGL((lr_rtp_kernel<K>), dim3(m / kRtpCols, B), dim3(256), 0, s, w.R, w.Pbt,
-                       w.Qt, w.Qtb, n, m, rp);
+    cqr_pass<K>(w, n, B, false, s);
+    cqr_pass<K>(w, n, B, true, s);
+    hipLaunchKernelGGL((lr_rtp_kernel<K>), dim3(m / kRtpCols, w.nsplit, B), dim3(256), 0, s, w.R,
+                       w.Pbt, w.qpart, n, m, rp, w.nsplit, w.split_rows);
+    hipLaunchKernelGGL((lr_qfinish_kernel<K>), dim3(K, (m + 1023) / 1024, B), dim3(256), 0, s,
+                       w.qpart, w.Qt, w.Qtb, w.amax, m, w.nsplit);
   }
-  hipLaunchKernelGGL((lr_int4_kernel<K>), dim3(2, B), dim3(256), 0, s, w.P, w.Qt, packed, L);
-  const int ntile_rc = ((n + kRcRows - 1) / kRcRows) * ((m + kRcCols - 1) / kRcCols);
+  hipLaunchKernelGGL((lr_int4_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, w.P, w.Qt,
+                     w.amax, packed, L);
+  const int ntile_rc = ((n + kRc - 1) / kRc) * (m / kRc);
   if (bf16)
     hipLaunchKernelGGL((lr_recon_kernel<uint16_t, true, K>), dim3(ntile_rc, B), dim3(256), 0, s,
                        static_cast<const uint16_t*>(a), ahat, e, (const uint8_t*)packed, L);
@@ -535,7 +606,7 @@ hipError_t lr_compress_k(bool bf16, const void* a, float* ahat, float* e, uint8_
 template <int K>
 hipError_t lr_decompress_k(const uint8_t* packed, float* ahat, int B, const Layout& L, hipStream_t s) {
   const int n = (int)L.rows, m = (int)L.cols;
-  const int ntile_rc = ((n + kRcRows - 1) / kRcRows) * ((m + kRcCols - 1) / kRcCols);
+  const int ntile_rc = ((n + kRc - 1) / kRc) * (m / kRc);
   hipLaunchKernelGGL((lr_recon_kernel<float, false, K>), dim3(ntile_rc, B), dim3(256), 0, s,
                      (const float*)nullptr, ahat, (float*)nullptr, packed, L);
   return hipGetLastError();
@@ -546,7 +617,7 @@ hipError_t lr_decompress_k(const uint8_t* packed, float* ahat, int B, const Layo
 hipError_t launch_lr_compress(bool bf16_input, const void* a, float* ahat, float* e,
                               uint8_t* packed, int batch, const Layout& L, const LowRankWork& w,
                               hipStream_t s) {
-  if (L.cols % kRtpCols) return hipErrorInvalidValue;
+  if (L.cols % 64) return hipErrorInvalidValue;
   switch (w.rank) {
     case 16: return lr_compress_k<16>(bf16_input, a, ahat, e, packed, batch, L, w, s);
     case 32: return lr_compress_k<32>(bf16_input, a, ahat, e, packed, batch, L, w, s);
@@ -558,6 +629,7 @@ hipError_t launch_lr_compress(bool bf16_input, const void* a, float* ahat, float
 
 hipError_t launch_lr_decompress(const uint8_t* packed, float* ahat, int batch, const Layout& L,
                                 int rank, hipStream_t s) {
+  if (L.cols % 64) return hipErrorInvalidValue;
   switch (rank) {
     case 16: return lr_decompress_k<16>(packed, ahat, batch, L, s);
     case 32: return lr_decompress_k<32>(packed, ahat, batch, L, s);

@@ -112,6 +112,12 @@ rc_status_t setup_lowrank(rc_plan* pl, const float* q0) {
   w.iters = pl->params.iters;
   w.ntiles = (n + 63) / 64;
   w.rows_pad = 64 * w.ntiles;
+  // split the rows of the R^T P product so that the launch has >= ~2048 blocks
+  const int64_t col_blocks = (m / 64) * B;
+  int64_t split = (2048 + col_blocks - 1) / col_blocks;
+  split = split < 1 ? 1 : (split > 8 ? 8 : split);
+  w.split_rows = (int)(((w.rows_pad + split - 1) / split + 31) / 32 * 32);
+  w.nsplit = (int)((w.rows_pad + w.split_rows - 1) / w.split_rows);
   Piece pieces[] = {
       {(void**)&w.R, B * n * m * 2},
       {(void**)&w.P, B * n * k * 4},
@@ -120,7 +126,10 @@ rc_status_t setup_lowrank(rc_plan* pl, const float* q0) {
       {(void**)&w.Q0t, B * k * m * 2},
       {(void**)&w.Qtb, B * k * m * 2},
       {(void**)&w.gpart, B * w.ntiles * k * k * 4},
+      {(void**)&w.gsum, B * k * k * 4},
       {(void**)&w.chol, B * k * (k + 1) * 4},
+      {(void**)&w.qpart, B * w.nsplit * k * m * 4},
+      {(void**)&w.amax, B * 2 * k * 4},
   };
   int64_t total = 0;
   for (auto& pc : pieces) total += align_up(pc.bytes);
@@ -242,11 +251,11 @@ size_t rc_tensor_packed_bytes(rc_plan_t pl) { return pl ? (size_t)pl->layout.tst
 size_t rc_workspace_bytes(rc_plan_t pl) { return pl ? pl->ws_bytes : 0; }
 
 // Diagnostics (not part of the public header): device pointers of the
-// low-rank workspace pieces, in the order R, P, Pbt, Qt, Q0t, Qtb, gpart, chol.
+// low-rank workspace pieces, in the order R, P, Pbt, Qt, Q0t, Qtb, gsum, chol.
 int rcx_lowrank_workspace(rc_plan_t pl, void** ptrs, int count) {
   if (!pl || pl->scheme != RC_LOWRANK || !ptrs || count < 8) return -1;
   const rc::LowRankWork& w = pl->lr;
-  void* v[8] = {w.R, w.P, w.Pbt, w.Qt, w.Q0t, w.Qtb, w.gpart, w.chol};
+  void* v[8] = {w.R, w.P, w.Pbt, w.Qt, w.Q0t, w.Qtb, w.gsum, w.chol};
   for (int i = 0; i < 8; ++i) ptrs[i] = v[i];
   return (int)w.rows_pad;
 }

@@ -146,7 +146,7 @@ def cpu_baseline(config, budget_s, log):
     if spec["scheme"] == "lr":
         kw.update(rank=spec["rank"], iters=spec["iters"])
     oracle.build(force=False)
-    tensors = [0, 1, 2, 3]
+    tensors = list(range(12))
     wl = synth.make(config, tensors=tensors)
     _, a0 = wl.next()
     f32 = lambda a: (a.astype(np.uint32) << 16).view(np.float32) if wl.dtype == "bf16" else a
@@ -173,7 +173,7 @@ def cpu_baseline(config, budget_s, log):
     in_bytes = 2 if wl.dtype == "bf16" else 4
     gbps = done * wl.n * wl.m * in_bytes / elapsed / 1e9
     return dict(value=gbps, unit="GB/s", cores=1, kind="oracle",
-                sample="%s: %d tensor-steps of %dx%d (tensors 0-3, steps 1-%d), compress+decompress, "
+                sample="%s: %d tensor-steps of %dx%d (tensors 0-11, steps 1-%d), compress+decompress, "
                        "%.1f s single-threaded" % (config, done, wl.n, wl.m, t, elapsed))
 
 
@@ -189,6 +189,8 @@ def main():
                     help="distinct input frames for the other workloads (cycled)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (reference kernel for HBM counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -202,6 +204,22 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            dst.copy_(src)
+        ev0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / 5
+        log("[bench] copy 1 GiB -> 1 GiB: %.3f ms, %.0f GB/s (read+write)" % (ms, 2 * (1 << 30) / ms / 1e6))
+        del src, dst
+        torch.cuda.empty_cache()
 
     main_res = measure(args.workload, args.steps, args.warmup, 64, log)
     log("[bench] %s: %.3f ms/step, %.1f GB/s input, compress %.3f ms (%.0f GB/s alg)" % (
