@@ -44,15 +44,17 @@ struct LowRankWork {
   uint16_t* Qtb = nullptr;   // bf16 Q^T for the next product [batch][rank][cols]
   float* gpart = nullptr;    // per-64-row-tile Gram partials [batch][ntiles][rank][rank]
   float* gsum = nullptr;     // summed Gram matrices [batch][rank][rank]
-  float* chol = nullptr;     // Cholesky factor + dead flags [batch][rank][rank + 1]
+  float* linv = nullptr;     // inverse Cholesky factor, dead rows zeroed [batch][rank][rank]
   float* qpart = nullptr;    // R^T P partials [batch][nsplit][rank][cols]
   uint32_t* amax = nullptr;  // column absmax bits of U and V [batch][2][rank]
+  float* ud = nullptr;       // dequantised U [batch][rows][rank]
+  float* vd = nullptr;       // dequantised V [batch][cols][rank]
 };
 
 hipError_t launch_lr_compress(bool bf16_input, const void* a, float* ahat, float* e,
                               uint8_t* packed, int batch, const Layout& L, const LowRankWork& w,
                               hipStream_t s);
 hipError_t launch_lr_decompress(const uint8_t* packed, float* ahat, int batch, const Layout& L,
-                                int rank, hipStream_t s);
+                                const LowRankWork& w, hipStream_t s);
 
 }  // namespace rc

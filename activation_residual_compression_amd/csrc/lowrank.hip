@@ -18,7 +18,8 @@
 //   U = P, V = Q; per-column absmax INT4                          [lr_int4_kernel]
 //   c = Uq Vq^T (fp32 MFMA), e = r - c, ahat += c                 [lr_recon_kernel]
 // CQR(P): G = P^T P (fp32 MFMA on 64-row tiles, tile partials summed in tile
-// order), G = L L^T (one wave, left-looking), P <- P L^{-T} (one lane per row).
+// order), G = L L^T (one wave, left-looking, in registers), P <- P L^{-T} as
+// the product P (L^{-1})^T (fp32 MFMA).
 // A pivot <= 2^-23 * max(trace G, k * FLT_MIN) marks a dead column, whose P
 // column is zeroed, so zero or rank-deficient residuals never produce NaN.
 //
@@ -221,116 +222,139 @@ __global__ __launch_bounds__(256) void lr_gram_reduce_kernel(const float* __rest
 }
 
 // ---------------------------------------------------------------- Cholesky
-// One wave per tensor: left-looking Cholesky of G (upper triangle of gsum),
-// lane i owns row i, with the dead-column rule. Output chol[K][K+1]: L (lower
-// triangle; L[j][j] = 1 for dead j) and, in column K, 1.0 for dead columns.
+// One wave per tensor, everything in registers: lane i holds row i of G (from
+// the upper triangle of gsum) and builds row i of L by the left-looking
+// recurrence; row j of L is read from lane j with v_readlane. Dead columns
+// (pivot <= 2^-23 * max(trace G, K * FLT_MIN)) get L[j][j] = 1 and a zero
+// column below the diagonal. Then lane c solves L y = e_c, giving column c of
+// L^{-1}; rows of dead columns are zeroed, so x = L^{-1} p has x_j = 0 there
+// and the other entries are those of the forward substitution.
+__device__ __forceinline__ float lane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
 template <int K>
 __global__ __launch_bounds__(64) void lr_chol_kernel(const float* __restrict__ gsum,
-                                                     float* __restrict__ chol) {
-  constexpr int LD = K + 1;
-  __shared__ float G[K * LD];
-  __shared__ float L[K * LD];
+                                                     float* __restrict__ linv) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const float* gs = gsum + (size_t)b * K * K;
-  for (int idx = lane; idx < K * K; idx += 64) {
-    const int i = idx / K, j = idx % K;
-    G[i * LD + j] = gs[i <= j ? idx : j * K + i];
-  }
-  for (int idx = lane; idx < K * LD; idx += 64) L[idx] = 0.f;
-  __syncthreads();
-  float tr = lane < K ? G[lane * LD + lane] : 0.f;
+  float g[K], L[K];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) tr += __shfl_xor(tr, o);
+  for (int j = 0; j < K; ++j) {
+    g[j] = (lane < K && j <= lane) ? gs[j * K + lane] : 0.f;  // G[lane][j] = G[j][lane]
+    L[j] = 0.f;
+  }
+  float tr = 0.f;
+#pragma unroll
+  for (int j = 0; j < K; ++j) tr += lane_f32(g[j], j);
   const float tol = ldexpf(fmaxf(tr, (float)K * FLT_MIN), -23);
   uint64_t dead = 0;
+#pragma unroll
   for (int j = 0; j < K; ++j) {
-    float s = 0.f;
-    if (lane >= j && lane < K) {
-      s = G[lane * LD + j];
-      for (int p = 0; p < j; ++p) s -= L[lane * LD + p] * L[j * LD + p];
-    }
-    const float piv = __shfl(s, j);
+    float s = g[j];
+#pragma unroll
+    for (int p = 0; p < j; ++p) s -= L[p] * lane_f32(L[p], j);
+    const float piv = lane_f32(s, j);
     const bool dj = !(piv > tol);
     const float ljj = dj ? 1.0f : sqrtf(piv);
-    if (lane == j) L[j * LD + j] = ljj;
-    if (lane > j && lane < K) L[lane * LD + j] = dj ? 0.f : s / ljj;
+    L[j] = lane == j ? ljj : (lane > j && !dj ? s / ljj : 0.f);
     if (dj) dead |= (uint64_t)1 << j;
-    __syncthreads();
   }
-  if (lane < K) L[lane * LD + K] = ((dead >> lane) & 1) ? 1.f : 0.f;
-  __syncthreads();
-  float* out = chol + (size_t)b * K * LD;
-  for (int idx = lane; idx < K * LD; idx += 64) out[idx] = L[idx];
+  // column `lane` of L^{-1}
+  float y[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    float s = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+    for (int q = 0; q < i; ++q) s -= lane_f32(L[q], i) * y[q];
+    y[i] = ((dead >> i) & 1) ? 0.f : s / lane_f32(L[i], i);
+  }
+  if (lane < K) {
+    float* out = linv + (size_t)b * K * K + lane;
+#pragma unroll
+    for (int i = 0; i < K; ++i) out[(size_t)i * K] = y[i];
+  }
 }
 
 // ---------------------------------------------------------------- P <- P L^-T
-// One wave per 64-row tile, one lane per row: forward substitution x L^T = p.
+// One wave per 64-row tile: X = T L^{-T} with fp32 MFMA (T = the tile of P).
 // GRAM: also write the Gram partial of the solved tile (next CQR pass).
 // FINAL: also write the bf16 transposed panel used by the R^T P product
 // (rows n .. rows_pad-1 written as 0) and fold the column absmax of the tile
 // into amax[b][0][*] (the INT4 scales of U).
 template <int K, bool GRAM, bool FINAL>
 __global__ __launch_bounds__(64) void lr_solve_kernel(float* __restrict__ P,
-                                                      const float* __restrict__ chol,
+                                                      const float* __restrict__ linv,
                                                       float* __restrict__ gpart,
                                                       uint16_t* __restrict__ Pbt,
                                                       uint32_t* __restrict__ amax, int n,
                                                       int ntiles, int rows_pad) {
+  constexpr int NT = K / 16;
   constexpr int LD = K + 1;
-  __shared__ float Ls[K * LD];
+  __shared__ float Li[K * LD];
   __shared__ float T[kTile * LD];
-  const int b = blockIdx.y, tile = blockIdx.x;
-  const int lane = threadIdx.x;
-  const float* src = chol + (size_t)b * K * LD;
-  for (int idx = lane; idx < K * LD; idx += 64) Ls[idx] = src[idx];
+  __shared__ float X[kTile * LD];
+  const int b = blockIdx.y, tile = blockIdx.x, row0 = tile * kTile;
+  const int lane = threadIdx.x, lr = lane & 15, lk = lane >> 4;
+  const float* li = linv + (size_t)b * K * K;
+  for (int idx = lane; idx < K * K; idx += 64) Li[(idx / K) * LD + idx % K] = li[idx];
+  float* Pb = P + (size_t)b * n * K;
+  for (int idx = lane; idx < kTile * K / 4; idx += 64) {
+    const int r = (4 * idx) / K, j = (4 * idx) % K;
+    const f32x4 v = (row0 + r < n) ? *reinterpret_cast<const f32x4*>(Pb + (size_t)(row0 + r) * K + j)
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+    T[r * LD + j] = v.x; T[r * LD + j + 1] = v.y; T[r * LD + j + 2] = v.z; T[r * LD + j + 3] = v.w;
+  }
   __syncthreads();
-  const int row = tile * kTile + lane;
-  const bool valid = row < n;
-  float x[K];
-  float* prow = P + ((size_t)b * n + (valid ? row : 0)) * K;
+  // X[r][i] = sum_c T[r][c] Linv[i][c]: A = T (rows r), B[c][i] = Linv[i][c]
 #pragma unroll
-  for (int j = 0; j < K; j += 4) {
-    const f32x4 v = valid ? *reinterpret_cast<const f32x4*>(prow + j) : f32x4{0.f, 0.f, 0.f, 0.f};
-    x[j] = v.x; x[j + 1] = v.y; x[j + 2] = v.z; x[j + 3] = v.w;
-  }
+  for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    float s = x[j];
+    for (int it = 0; it < NT; ++it) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < j; ++q) s -= Ls[j * LD + q] * x[q];
-    x[j] = (Ls[j * LD + K] != 0.f) ? 0.f : s / Ls[j * LD + j];
-  }
-  if (valid) {
+      for (int k0 = 0; k0 < K; k0 += 4)
+        acc = mfma_f32(T[(16 * rt + lr) * LD + k0 + lk], Li[(16 * it + lr) * LD + k0 + lk], acc);
 #pragma unroll
-    for (int j = 0; j < K; j += 4) *reinterpret_cast<f32x4*>(prow + j) = f32x4{x[j], x[j + 1], x[j + 2], x[j + 3]};
-  }
-#pragma unroll
-  for (int j = 0; j < K; ++j) T[lane * LD + j] = x[j];  // x = 0 for rows past n
+      for (int t = 0; t < 4; ++t) X[(16 * rt + 4 * lk + t) * LD + 16 * it + lr] = acc[t];
+    }
   __syncthreads();
+  for (int idx = lane; idx < kTile * K / 4; idx += 64) {
+    const int r = (4 * idx) / K, j = (4 * idx) % K;
+    if (row0 + r < n)
+      *reinterpret_cast<f32x4*>(Pb + (size_t)(row0 + r) * K + j) =
+          f32x4{X[r * LD + j], X[r * LD + j + 1], X[r * LD + j + 2], X[r * LD + j + 3]};
+  }
   if constexpr (FINAL) {
+    // lane = row of the tile; rows past n are zero in X
+    const int row = row0 + lane;
     if (row < rows_pad) {
       uint16_t* dst = Pbt + (size_t)b * K * rows_pad + row;
 #pragma unroll
-      for (int j = 0; j < K; ++j) dst[(size_t)j * rows_pad] = valid ? (uint16_t)bf16_rne(x[j]) : (uint16_t)0;
+      for (int j = 0; j < K; ++j) dst[(size_t)j * rows_pad] = (uint16_t)bf16_rne(X[lane * LD + j]);
     }
     if (lane < K) {
       float mx = 0.f;
-      for (int r = 0; r < kTile; ++r) mx = fmaxf(mx, fabsf(T[r * LD + lane]));
+      for (int r = 0; r < kTile; ++r) mx = fmaxf(mx, fabsf(X[r * LD + lane]));
       atomicMax(amax + (size_t)b * 2 * K + lane, __float_as_uint(mx));
     }
   }
-  if constexpr (GRAM) tile_gram<K, LD>(T, gpart + ((size_t)b * ntiles + tile) * K * K, 1);
+  if constexpr (GRAM) tile_gram<K, LD>(X, gpart + ((size_t)b * ntiles + tile) * K * K, 1);
 }
 
 // ---------------------------------------------------------------- Q = R^T P
-// Block: 64 columns x one row split of one tensor; each wave owns 16 columns.
-// Per step of 32 rows the R tile [32 x 64] is staged through LDS (double
-// buffered, one barrier per step) and read back transposed with
-// ds_read_b64_tr_b16 to form the MFMA A operand A[c][i] = R[i][c]. The split's
-// partial Q^T goes to qpart; lr_qfinish_kernel sums the splits.
-constexpr int kRtpCols = 64;
-constexpr int kRtpLd = kRtpCols + 8;  // bf16 elements per LDS row (144 B)
+// Block: 128 columns x one row split of one tensor; wave w owns columns
+// 32w .. 32w+31 (two 16-column MFMA tiles). Per step of 32 rows the R tile
+// [32 x 128] and the matching P^T chunk [K x 32] are staged through LDS
+// (double buffered, one barrier per step). R is read back transposed with
+// ds_read_b64_tr_b16 (A[c][i] = R[i][c]); each P^T fragment read from LDS
+// feeds both column tiles of the wave. The split's partial Q^T goes to qpart;
+// lr_qfinish_kernel sums the splits. A last block of 64 columns (cols % 128 ==
+// 64) zero-fills the missing half and stores only valid columns.
+constexpr int kRtpCols = 128;
+constexpr int kRtpLd = kRtpCols + 8;  // bf16 per staged R row (272 B)
+constexpr int kRtpPld = 32 + 8;       // bf16 per staged P^T row (80 B)
 
 template <int K>
 __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict__ R,
@@ -338,51 +362,78 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
                                                      float* __restrict__ qpart, int n, int m,
                                                      int rows_pad, int nsplit, int split_rows) {
   constexpr int NT = K / 16;
+  constexpr int PCH = K * 4;  // 16-byte chunks of a [K x 32] bf16 P^T block
   __shared__ __attribute__((aligned(16))) uint16_t sR[2][32 * kRtpLd];
+  __shared__ __attribute__((aligned(16))) uint16_t sP[2][K * kRtpPld];
   const int b = blockIdx.z, split = blockIdx.y, c0 = blockIdx.x * kRtpCols;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
-  const int ld_row = threadIdx.x >> 3, ld_col = (threadIdx.x & 7) * 8;
+  const int ld_row = threadIdx.x >> 3, ld_col = (threadIdx.x & 7) * 16;
+  const bool col_ok = c0 + ld_col < m;
   const int i_begin = split * split_rows;
   const int i_end = min(rows_pad, i_begin + split_rows);
   const uint16_t* Rb = R + (size_t)b * n * m;
   const uint16_t* Pb = Pbt + (size_t)b * K * rows_pad;
-  // transposed-read address of this lane inside a staged tile: group lk,
-  // row 8 lk + (lr / 4) (+4 for the second read), columns 16 w + 4 (lr % 4)
-  const int tr_off = (8 * lk + (lr >> 2)) * kRtpLd + 16 * w + 4 * (lr & 3);
+  const int tr_off = (8 * lk + (lr >> 2)) * kRtpLd + 32 * w + 4 * (lr & 3);
 
+  struct Stage { u32x4 r0, r1, p; };
   auto gload = [&](int i0) {
+    Stage st;
     int row = i0 + ld_row;
     row = row < n ? row : n - 1;
-    return *reinterpret_cast<const u32x4*>(Rb + (size_t)row * m + c0 + ld_col);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4* src = reinterpret_cast<const u32x4*>(Rb + (size_t)row * m + c0 + ld_col);
+    st.r0 = col_ok ? src[0] : z;
+    st.r1 = col_ok ? src[1] : z;
+    st.p = z;
+    if (threadIdx.x < PCH) {
+      const int j = threadIdx.x >> 2, q = threadIdx.x & 3;
+      st.p = *reinterpret_cast<const u32x4*>(Pb + (size_t)j * rows_pad + i0 + 8 * q);
+    }
+    return st;
   };
-  f32x4 acc[NT];
+  f32x4 acc[2][NT];
 #pragma unroll
-  for (int g = 0; g < NT; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int g = 0; g < NT; ++g) acc[ct][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 next = gload(i_begin);
+  Stage next = gload(i_begin);
   int buf = 0;
   for (int i0 = i_begin; i0 < i_end; i0 += 32, buf ^= 1) {
-    *reinterpret_cast<u32x4*>(&sR[buf][ld_row * kRtpLd + ld_col]) = next;
+    u32x4* dr = reinterpret_cast<u32x4*>(&sR[buf][ld_row * kRtpLd + ld_col]);
+    dr[0] = next.r0;
+    dr[1] = next.r1;
+    if (threadIdx.x < PCH)
+      *reinterpret_cast<u32x4*>(&sP[buf][(threadIdx.x >> 2) * kRtpPld + 8 * (threadIdx.x & 3)]) = next.p;
     __syncthreads();
     if (i0 + 32 < i_end) next = gload(i0 + 32);
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)&sR[buf][tr_off]);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)&sR[buf][tr_off + 4 * kRtpLd]);
-    u32x4 A;
-    A.x = (uint32_t)(uint16_t)lo.x | ((uint32_t)(uint16_t)lo.y << 16);
-    A.y = (uint32_t)(uint16_t)lo.z | ((uint32_t)(uint16_t)lo.w << 16);
-    A.z = (uint32_t)(uint16_t)hi.x | ((uint32_t)(uint16_t)hi.y << 16);
-    A.w = (uint32_t)(uint16_t)hi.z | ((uint32_t)(uint16_t)hi.w << 16);
+    u32x4 A[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int o = tr_off + 16 * ct;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)&sR[buf][o]);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)&sR[buf][o + 4 * kRtpLd]);
+      A[ct].x = (uint32_t)(uint16_t)lo.x | ((uint32_t)(uint16_t)lo.y << 16);
+      A[ct].y = (uint32_t)(uint16_t)lo.z | ((uint32_t)(uint16_t)lo.w << 16);
+      A[ct].z = (uint32_t)(uint16_t)hi.x | ((uint32_t)(uint16_t)hi.y << 16);
+      A[ct].w = (uint32_t)(uint16_t)hi.z | ((uint32_t)(uint16_t)hi.w << 16);
+    }
 #pragma unroll
     for (int g = 0; g < NT; ++g) {
-      const u32x4 Bv = *reinterpret_cast<const u32x4*>(Pb + (size_t)(16 * g + lr) * rows_pad + i0 + 8 * lk);
-      acc[g] = mfma_bf16(A, Bv, acc[g]);
+      const u32x4 Bv = *reinterpret_cast<const u32x4*>(&sP[buf][(16 * g + lr) * kRtpPld + 8 * lk]);
+      acc[0][g] = mfma_bf16(A[0], Bv, acc[0][g]);
+      acc[1][g] = mfma_bf16(A[1], Bv, acc[1][g]);
     }
   }
-  // D[c][j]: lane holds c = c0 + 16w + 4lk + t, j = 16g + lr
-  const int c = c0 + 16 * w + 4 * lk;
+  // D[c][j]: lane holds c = c0 + 32w + 16ct + 4lk + t, j = 16g + lr
   float* qp = qpart + ((size_t)b * nsplit + split) * K * m;
 #pragma unroll
-  for (int g = 0; g < NT; ++g) *reinterpret_cast<f32x4*>(qp + (size_t)(16 * g + lr) * m + c) = acc[g];
+  for (int ct = 0; ct < 2; ++ct) {
+    const int c = c0 + 32 * w + 16 * ct + 4 * lk;
+    if (c < m)
+#pragma unroll
+      for (int g = 0; g < NT; ++g) *reinterpret_cast<f32x4*>(qp + (size_t)(16 * g + lr) * m + c) = acc[ct][g];
+  }
 }
 
 // Sum the row splits in split order: Qt (fp32, V of the factorisation), Qtb
@@ -418,13 +469,16 @@ __global__ __launch_bounds__(256) void lr_qfinish_kernel(const float* __restrict
 // One lane per factor row: rows 0..n-1 are U (= P, [n][K]), rows n..n+m-1 are V
 // (= Q, stored as Qt [K][m]). Per column j: s_j = absmax_j / 7,
 // q = clamp(rint_even(x / s_j), -7, 7) (0 when s_j = 0), packed row-major,
-// element t in nibble t (even t low), two's complement. Block 0 writes the
-// scale sections and zeroes the section padding.
+// element t in nibble t (even t low), two's complement. The dequantised
+// factors q * s_j go to ud / vd for the sender's reconstruction. Block 0
+// writes the scale sections and zeroes the section padding.
 template <int K>
 __global__ __launch_bounds__(256) void lr_int4_kernel(const float* __restrict__ P,
                                                       const float* __restrict__ Qt,
                                                       const uint32_t* __restrict__ amax,
-                                                      uint8_t* __restrict__ packed, Layout L) {
+                                                      uint8_t* __restrict__ packed,
+                                                      float* __restrict__ ud,
+                                                      float* __restrict__ vd, Layout L) {
   __shared__ float sc[2 * K];
   const int b = blockIdx.y;
   const int n = (int)L.rows, m = (int)L.cols;
@@ -449,100 +503,146 @@ __global__ __launch_bounds__(256) void lr_int4_kernel(const float* __restrict__ 
   const float* s = sc + (isV ? K : 0);
   const float* src = isV ? Qt + (size_t)b * K * m + i : P + ((size_t)b * n + i) * K;
   const size_t stride = isV ? (size_t)m : 1;
+  float* deq = isV ? vd + ((size_t)b * m + i) * K : ud + ((size_t)b * n + i) * K;
   uint32_t words[K / 8];
 #pragma unroll
   for (int q = 0; q < K / 8; ++q) words[q] = 0;
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    float qv = 0.f;
-    if (s[j] > 0.f) qv = fminf(fmaxf(rintf(src[j * stride] / s[j]), -7.f), 7.f);
-    words[j / 8] |= ((uint32_t)((int)qv) & 0xFu) << (4 * (j % 8));
+  for (int j = 0; j < K; j += 4) {
+    float dq[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int qi = 0;
+      if (s[j + u] > 0.f) qi = (int)fminf(fmaxf(rintf(src[(j + u) * stride] / s[j + u]), -7.f), 7.f);
+      words[(j + u) / 8] |= ((uint32_t)qi & 0xFu) << (4 * ((j + u) % 8));
+      dq[u] = (float)qi * s[j + u];  // the receiver's decode: integer code times scale
+    }
+    *reinterpret_cast<f32x4*>(deq + j) = f32x4{dq[0], dq[1], dq[2], dq[3]};
   }
   uint32_t* dst = reinterpret_cast<uint32_t*>(pk + (isV ? L.sec_off[1] : L.sec_off[0]) + (size_t)i * (K / 2));
 #pragma unroll
   for (int q = 0; q < K / 8; ++q) dst[q] = words[q];
 }
 
-// ---------------------------------------------------------------- reconstruct
-// c = Uq Vq^T on a 64 x 64 tile with fp32 MFMA. The INT4 factors of the tile
-// are decoded into LDS (Us[64][K], Vs[64][K]); wave w computes rows 16w..16w+15
-// as c^T = Vq Uq^T, so each lane ends with 8 consecutive columns of one row in
-// each half of the tile (the MFMA M index is mapped to columns so that the two
-// 16-column MFMA tiles of a half interleave in groups of 4).
-// SENDER: r = a - ahat, e = r - c, ahat += c. Receiver: ahat += c. Both run
-// this same code, so both get the same c bit for bit.
-constexpr int kRc = 64;
-
+// Receiver: dequantise the packed factors (same products q * s as the sender).
 __device__ __forceinline__ float int4_at(const uint8_t* nib, int64_t t) {
   const uint32_t byte = nib[t >> 1];
   const int v = (t & 1) ? (int)(byte >> 4) : (int)(byte & 15u);
   return (float)(v >= 8 ? v - 16 : v);
 }
 
+template <int K>
+__global__ __launch_bounds__(256) void lr_dequant_kernel(const uint8_t* __restrict__ packed,
+                                                         float* __restrict__ ud,
+                                                         float* __restrict__ vd, Layout L) {
+  const int b = blockIdx.y;
+  const int n = (int)L.rows, m = (int)L.cols;
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n + m) return;
+  const uint8_t* pk = packed + (size_t)b * L.tstride;
+  const bool isV = r >= n;
+  const int i = isV ? r - n : r;
+  const uint8_t* nib = pk + (isV ? L.sec_off[1] : L.sec_off[0]);
+  const float* s = reinterpret_cast<const float*>(pk + (isV ? L.sec_off[3] : L.sec_off[2]));
+  float* deq = isV ? vd + ((size_t)b * m + i) * K : ud + ((size_t)b * n + i) * K;
+#pragma unroll
+  for (int j = 0; j < K; j += 4) {
+    f32x4 v;
+    v.x = int4_at(nib, (int64_t)i * K + j) * s[j];
+    v.y = int4_at(nib, (int64_t)i * K + j + 1) * s[j + 1];
+    v.z = int4_at(nib, (int64_t)i * K + j + 2) * s[j + 2];
+    v.w = int4_at(nib, (int64_t)i * K + j + 3) * s[j + 3];
+    *reinterpret_cast<f32x4*>(deq + j) = v;
+  }
+}
+
+// ---------------------------------------------------------------- reconstruct
+// c = Uq Vq^T on a 64 x 128 tile with fp32 MFMA from the dequantised factors.
+// The lane's a_t / ahat loads are issued first, then the factor tiles are
+// staged in LDS (Us[64][K], Vs[128][K]); wave w computes rows 16w..16w+15 as
+// c^T = Vq Uq^T, the MFMA M index mapped to columns so that each lane ends with
+// 8 consecutive columns of one row in each 32-column quarter of the tile.
+// SENDER: r = a - ahat, e = r - c, ahat += c. Receiver: ahat += c. Both run
+// this same code on the same dequantised factors, so both get the same c.
+constexpr int kRcRows = 64, kRcCols = 128;
+
 template <typename IN, bool SENDER, int K>
 __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
                                                        float* __restrict__ ahat,
                                                        float* __restrict__ e,
-                                                       const uint8_t* __restrict__ packed,
-                                                       Layout L) {
+                                                       const float* __restrict__ ud,
+                                                       const float* __restrict__ vd, int n, int m) {
   constexpr int LD = K + 1;
-  __shared__ float Us[kRc * LD];
-  __shared__ float Vs[kRc * LD];
+  __shared__ float Us[kRcRows * LD];
+  __shared__ float Vs[kRcCols * LD];
   const int b = blockIdx.y;
-  const int n = (int)L.rows, m = (int)L.cols;
-  const int ncol_tiles = m / kRc;
-  const int r0 = (blockIdx.x / ncol_tiles) * kRc, c0 = (blockIdx.x % ncol_tiles) * kRc;
-  const uint8_t* pk = packed + (size_t)b * L.tstride;
-  const uint8_t* un = pk + L.sec_off[0];
-  const uint8_t* vn = pk + L.sec_off[1];
-  const float* su = reinterpret_cast<const float*>(pk + L.sec_off[2]);
-  const float* sv = reinterpret_cast<const float*>(pk + L.sec_off[3]);
-  for (int idx = threadIdx.x; idx < kRc * K; idx += blockDim.x) {
-    const int r = idx / K, j = idx % K;
-    const int row = r0 + r;
-    Us[r * LD + j] = row < n ? int4_at(un, (int64_t)row * K + j) * su[j] : 0.f;
-    Vs[r * LD + j] = int4_at(vn, (int64_t)(c0 + r) * K + j) * sv[j];
+  const int ncol_tiles = (m + kRcCols - 1) / kRcCols;
+  const int r0 = (blockIdx.x / ncol_tiles) * kRcRows, c0 = (blockIdx.x % ncol_tiles) * kRcCols;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
+  const int row = r0 + 16 * w + lr;
+  const bool row_ok = row < n;
+  // this lane's elements: row, columns c0 + 32 q + 8 lk .. +7 for q = 0..3
+  F8 h[4], x[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int col = c0 + 32 * q + 8 * lk;
+    if (row_ok && col < m) {
+      const size_t off = ((size_t)b * n + row) * m + col;
+      load8<float>(ahat + off, h[q]);
+      if constexpr (SENDER) load8<IN>(a + off, x[q]);
+    }
+  }
+  const float* ub = ud + (size_t)b * n * K;
+  const float* vb = vd + (size_t)b * m * K;
+  for (int idx = threadIdx.x; idx < kRcRows * K / 4; idx += blockDim.x) {
+    const int r = (4 * idx) / K, j = (4 * idx) % K;
+    const f32x4 v = (r0 + r < n) ? *reinterpret_cast<const f32x4*>(ub + (size_t)(r0 + r) * K + j)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    Us[r * LD + j] = v.x; Us[r * LD + j + 1] = v.y; Us[r * LD + j + 2] = v.z; Us[r * LD + j + 3] = v.w;
+  }
+  for (int idx = threadIdx.x; idx < kRcCols * K / 4; idx += blockDim.x) {
+    const int r = (4 * idx) / K, j = (4 * idx) % K;
+    const f32x4 v = (c0 + r < m) ? *reinterpret_cast<const f32x4*>(vb + (size_t)(c0 + r) * K + j)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    Vs[r * LD + j] = v.x; Vs[r * LD + j + 1] = v.y; Vs[r * LD + j + 2] = v.z; Vs[r * LD + j + 3] = v.w;
   }
   __syncthreads();
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
-  f32x4 acc[4];
+  f32x4 acc[8];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // MFMA tile p covers local columns 32 (p/2) + 8 (m/4) + 4 (p%2) + m%4, m = 0..15
-  int vcol[4];
+  for (int p = 0; p < 8; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // MFMA tile p covers local columns 32 (p/2) + 8 (mi/4) + 4 (p%2) + mi%4, mi = 0..15
+  int vrow[8];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) vcol[p] = 32 * (p >> 1) + 8 * (lr >> 2) + 4 * (p & 1) + (lr & 3);
+  for (int p = 0; p < 8; ++p) vrow[p] = (32 * (p >> 1) + 8 * (lr >> 2) + 4 * (p & 1) + (lr & 3)) * LD;
 #pragma unroll 4
   for (int k0 = 0; k0 < K; k0 += 4) {
     const float bu = Us[(16 * w + lr) * LD + k0 + lk];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) acc[p] = mfma_f32(Vs[vcol[p] * LD + k0 + lk], bu, acc[p]);
+    for (int p = 0; p < 8; ++p) acc[p] = mfma_f32(Vs[vrow[p] + k0 + lk], bu, acc[p]);
   }
-  const int row = r0 + 16 * w + lr;
-  if (row >= n) return;
+  if (!row_ok) return;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int col = c0 + 32 * half + 8 * lk;
+  for (int q = 0; q < 4; ++q) {
+    const int col = c0 + 32 * q + 8 * lk;
+    if (col >= m) continue;
     const size_t off = ((size_t)b * n + row) * m + col;
-    const f32x4 cl = acc[2 * half], ch = acc[2 * half + 1];
-    const float c[8] = {cl.x, cl.y, cl.z, cl.w, ch.x, ch.y, ch.z, ch.w};
-    F8 h;
-    load8<float>(ahat + off, h);
+    const f32x4 cl = acc[2 * q], chh = acc[2 * q + 1];
+    const float c[8] = {cl.x, cl.y, cl.z, cl.w, chh.x, chh.y, chh.z, chh.w};
+    F8 hv = h[q];
     if constexpr (SENDER) {
-      F8 x, ev;
-      load8<IN>(a + off, x);
+      F8 ev;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float r = x.v[i] - h.v[i];
+        const float r = x[q].v[i] - hv.v[i];
         ev.v[i] = r - c[i];
-        h.v[i] = h.v[i] + c[i];
+        hv.v[i] = hv.v[i] + c[i];
       }
       store8_nt(e + off, ev);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) h.v[i] = h.v[i] + c[i];
+      for (int i = 0; i < 8; ++i) hv.v[i] = hv.v[i] + c[i];
     }
-    store8(ahat + off, h);
+    store8(ahat + off, hv);
   }
 }
 
@@ -554,12 +654,12 @@ void cqr_pass(const LowRankWork& w, int n, int B, bool final_pass, hipStream_t s
   const int nt = (int)w.ntiles, rp = (int)w.rows_pad;
   hipLaunchKernelGGL((lr_gram_reduce_kernel<K>), dim3((K * K + 255) / 256, B), dim3(256), 0, s,
                      w.gpart, w.gsum, nt);
-  hipLaunchKernelGGL((lr_chol_kernel<K>), dim3(B), dim3(64), 0, s, w.gsum, w.chol);
+  hipLaunchKernelGGL((lr_chol_kernel<K>), dim3(B), dim3(64), 0, s, w.gsum, w.linv);
   if (final_pass)
-    hipLaunchKernelGGL((lr_solve_kernel<K, false, true>), dim3(nt, B), dim3(64), 0, s, w.P, w.chol,
+    hipLaunchKernelGGL((lr_solve_kernel<K, false, true>), dim3(nt, B), dim3(64), 0, s, w.P, w.linv,
                        w.gpart, w.Pbt, w.amax, n, nt, rp);
   else
-    hipLaunchKernelGGL((lr_solve_kernel<K, true, false>), dim3(nt, B), dim3(64), 0, s, w.P, w.chol,
+    hipLaunchKernelGGL((lr_solve_kernel<K, true, false>), dim3(nt, B), dim3(64), 0, s, w.P, w.linv,
                        w.gpart, w.Pbt, w.amax, n, nt, rp);
 }
 
@@ -586,29 +686,35 @@ hipError_t lr_compress_k(bool bf16, const void* a, float* ahat, float* e, uint8_
     }
     cqr_pass<K>(w, n, B, false, s);
     cqr_pass<K>(w, n, B, true, s);
-    hipLaunchKernelGGL((lr_rtp_kernel<K>), dim3(m / kRtpCols, w.nsplit, B), dim3(256), 0, s, w.R,
-                       w.Pbt, w.qpart, n, m, rp, w.nsplit, w.split_rows);
+    hipLaunchKernelGGL((lr_rtp_kernel<K>), dim3((m + kRtpCols - 1) / kRtpCols, w.nsplit, B),
+                       dim3(256), 0, s, w.R, w.Pbt, w.qpart, n, m, rp, w.nsplit, w.split_rows);
     hipLaunchKernelGGL((lr_qfinish_kernel<K>), dim3(K, (m + 1023) / 1024, B), dim3(256), 0, s,
                        w.qpart, w.Qt, w.Qtb, w.amax, m, w.nsplit);
   }
   hipLaunchKernelGGL((lr_int4_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, w.P, w.Qt,
-                     w.amax, packed, L);
-  const int ntile_rc = ((n + kRc - 1) / kRc) * (m / kRc);
+                     w.amax, packed, w.ud, w.vd, L);
+  const int ntile_rc = ((n + kRcRows - 1) / kRcRows) * ((m + kRcCols - 1) / kRcCols);
   if (bf16)
     hipLaunchKernelGGL((lr_recon_kernel<uint16_t, true, K>), dim3(ntile_rc, B), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(a), ahat, e, (const uint8_t*)packed, L);
+                       static_cast<const uint16_t*>(a), ahat, e, (const float*)w.ud,
+                       (const float*)w.vd, n, m);
   else
     hipLaunchKernelGGL((lr_recon_kernel<float, true, K>), dim3(ntile_rc, B), dim3(256), 0, s,
-                       static_cast<const float*>(a), ahat, e, (const uint8_t*)packed, L);
+                       static_cast<const float*>(a), ahat, e, (const float*)w.ud, (const float*)w.vd,
+                       n, m);
   return hipGetLastError();
 }
 
 template <int K>
-hipError_t lr_decompress_k(const uint8_t* packed, float* ahat, int B, const Layout& L, hipStream_t s) {
+hipError_t lr_decompress_k(const uint8_t* packed, float* ahat, int B, const Layout& L,
+                           const LowRankWork& w, hipStream_t s) {
   const int n = (int)L.rows, m = (int)L.cols;
-  const int ntile_rc = ((n + kRc - 1) / kRc) * (m / kRc);
+  hipLaunchKernelGGL((lr_dequant_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, packed,
+                     w.ud, w.vd, L);
+  const int ntile_rc = ((n + kRcRows - 1) / kRcRows) * ((m + kRcCols - 1) / kRcCols);
   hipLaunchKernelGGL((lr_recon_kernel<float, false, K>), dim3(ntile_rc, B), dim3(256), 0, s,
-                     (const float*)nullptr, ahat, (float*)nullptr, packed, L);
+                     (const float*)nullptr, ahat, (float*)nullptr, (const float*)w.ud,
+                     (const float*)w.vd, n, m);
   return hipGetLastError();
 }
 
@@ -628,13 +734,13 @@ hipError_t launch_lr_compress(bool bf16_input, const void* a, float* ahat, float
 }
 
 hipError_t launch_lr_decompress(const uint8_t* packed, float* ahat, int batch, const Layout& L,
-                                int rank, hipStream_t s) {
+                                const LowRankWork& w, hipStream_t s) {
   if (L.cols % 64) return hipErrorInvalidValue;
-  switch (rank) {
-    case 16: return lr_decompress_k<16>(packed, ahat, batch, L, s);
-    case 32: return lr_decompress_k<32>(packed, ahat, batch, L, s);
-    case 48: return lr_decompress_k<48>(packed, ahat, batch, L, s);
-    case 64: return lr_decompress_k<64>(packed, ahat, batch, L, s);
+  switch (w.rank) {
+    case 16: return lr_decompress_k<16>(packed, ahat, batch, L, w, s);
+    case 32: return lr_decompress_k<32>(packed, ahat, batch, L, w, s);
+    case 48: return lr_decompress_k<48>(packed, ahat, batch, L, w, s);
+    case 64: return lr_decompress_k<64>(packed, ahat, batch, L, w, s);
   }
   return hipErrorInvalidValue;
 }

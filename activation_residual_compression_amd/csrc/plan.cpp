@@ -113,7 +113,7 @@ rc_status_t setup_lowrank(rc_plan* pl, const float* q0) {
   w.ntiles = (n + 63) / 64;
   w.rows_pad = 64 * w.ntiles;
   // split the rows of the R^T P product so that the launch has >= ~2048 blocks
-  const int64_t col_blocks = (m / 64) * B;
+  const int64_t col_blocks = ((m + 127) / 128) * B;
   int64_t split = (2048 + col_blocks - 1) / col_blocks;
   split = split < 1 ? 1 : (split > 8 ? 8 : split);
   w.split_rows = (int)(((w.rows_pad + split - 1) / split + 31) / 32 * 32);
@@ -127,9 +127,11 @@ rc_status_t setup_lowrank(rc_plan* pl, const float* q0) {
       {(void**)&w.Qtb, B * k * m * 2},
       {(void**)&w.gpart, B * w.ntiles * k * k * 4},
       {(void**)&w.gsum, B * k * k * 4},
-      {(void**)&w.chol, B * k * (k + 1) * 4},
+      {(void**)&w.linv, B * k * k * 4},
       {(void**)&w.qpart, B * w.nsplit * k * m * 4},
       {(void**)&w.amax, B * 2 * k * 4},
+      {(void**)&w.ud, B * n * k * 4},
+      {(void**)&w.vd, B * m * k * 4},
   };
   int64_t total = 0;
   for (auto& pc : pieces) total += align_up(pc.bytes);
@@ -223,8 +225,8 @@ rc_status_t rc_decompress(rc_plan_t pl, hipStream_t stream, const void* packed_i
       err = rc::launch_nm_decompress(packed, recon_state, pl->shape.batch, pl->layout, stream);
       break;
     case RC_LOWRANK:
-      err = rc::launch_lr_decompress(packed, recon_state, pl->shape.batch, pl->layout,
-                                     pl->params.rank, stream);
+      err = rc::launch_lr_decompress(packed, recon_state, pl->shape.batch, pl->layout, pl->lr,
+                                     stream);
       break;
   }
   return err == hipSuccess ? RC_OK : RC_ERR_HIP;
@@ -251,11 +253,11 @@ size_t rc_tensor_packed_bytes(rc_plan_t pl) { return pl ? (size_t)pl->layout.tst
 size_t rc_workspace_bytes(rc_plan_t pl) { return pl ? pl->ws_bytes : 0; }
 
 // Diagnostics (not part of the public header): device pointers of the
-// low-rank workspace pieces, in the order R, P, Pbt, Qt, Q0t, Qtb, gsum, chol.
+// low-rank workspace pieces, in the order R, P, Pbt, Qt, Q0t, Qtb, gsum, linv.
 int rcx_lowrank_workspace(rc_plan_t pl, void** ptrs, int count) {
   if (!pl || pl->scheme != RC_LOWRANK || !ptrs || count < 8) return -1;
   const rc::LowRankWork& w = pl->lr;
-  void* v[8] = {w.R, w.P, w.Pbt, w.Qt, w.Q0t, w.Qtb, w.gsum, w.chol};
+  void* v[8] = {w.R, w.P, w.Pbt, w.Qt, w.Q0t, w.Qtb, w.gsum, w.linv};
   for (int i = 0; i < 8; ++i) ptrs[i] = v[i];
   return (int)w.rows_pad;
 }
