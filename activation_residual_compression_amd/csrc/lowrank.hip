@@ -557,93 +557,126 @@ __global__ __launch_bounds__(256) void lr_dequant_kernel(const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------- reconstruct
-// c = Uq Vq^T on a 64 x 128 tile with fp32 MFMA from the dequantised factors.
-// The lane's a_t / ahat loads are issued first, then the factor tiles are
-// staged in LDS (Us[64][K], Vs[128][K]); wave w computes rows 16w..16w+15 as
-// c^T = Vq Uq^T, the MFMA M index mapped to columns so that each lane ends with
-// 8 consecutive columns of one row in each 32-column quarter of the tile.
-// SENDER: r = a - ahat, e = r - c, ahat += c. Receiver: ahat += c. Both run
-// this same code on the same dequantised factors, so both get the same c.
-constexpr int kRcRows = 64, kRcCols = 128;
+// c = Uq Vq^T with fp32 MFMA from the dequantised factors, streamed through the
+// state arrays. Each wave owns a 64-column strip and walks 16-row tiles of a
+// row chunk; the 4 waves of a block own 4 neighbouring strips of the same rows
+// (their U loads hit the same cache lines). Per wave:
+//   * once: the V operands of its strip (4 MFMA column tiles x K) in registers;
+//   * per tile: U operands of 16 rows, the lane's a_t / ahat, K MFMAs
+//     computing c^T = Vq Uq^T, then r = a - ahat, e = r - c, ahat += c
+//     (SENDER) or ahat += c (receiver); the next tile's loads are issued
+//     before the current tile's MFMAs.
+// MFMA step (j, i), j < K/16, i < 4, lane group g = l/16 covers contraction
+// index 16 j + 4 g + i, so both operands come from 16-byte loads of 4
+// consecutive factor columns. The MFMA M index is mapped to columns so that each
+// lane ends with 8 consecutive columns of one row in each 32-column half of the
+// strip. Sender and receiver run this same code on the same dequantised
+// factors, so both get the same c bit for bit. No LDS, no barriers.
+constexpr int kRcStrip = 64;     // columns per wave
+constexpr int kRcWaves = 4;      // strips per block
 
 template <typename IN, bool SENDER, int K>
 __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
                                                        float* __restrict__ ahat,
                                                        float* __restrict__ e,
                                                        const float* __restrict__ ud,
-                                                       const float* __restrict__ vd, int n, int m) {
-  constexpr int LD = K + 1;
-  __shared__ float Us[kRcRows * LD];
-  __shared__ float Vs[kRcCols * LD];
-  const int b = blockIdx.y;
-  const int ncol_tiles = (m + kRcCols - 1) / kRcCols;
-  const int r0 = (blockIdx.x / ncol_tiles) * kRcRows, c0 = (blockIdx.x % ncol_tiles) * kRcCols;
+                                                       const float* __restrict__ vd, int n, int m,
+                                                       int chunk_rows) {
+  constexpr int KJ = K / 16;
+  const int b = blockIdx.z;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
-  const int row = r0 + 16 * w + lr;
-  const bool row_ok = row < n;
-  // this lane's elements: row, columns c0 + 32 q + 8 lk .. +7 for q = 0..3
-  F8 h[4], x[4];
+  const int c0 = (blockIdx.x * kRcWaves + w) * kRcStrip;
+  if (c0 >= m) return;
+  const int rbeg = blockIdx.y * chunk_rows;
+  const int rend = min(n, rbeg + chunk_rows);
+  // V operands: tile p covers strip columns 32 (p/2) + 8 (mi/4) + 4 (p%2) + mi%4
+  f32x4 av[4][KJ];
+  const float* vb = vd + (size_t)b * m * K;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int col = c0 + 32 * q + 8 * lk;
-    if (row_ok && col < m) {
-      const size_t off = ((size_t)b * n + row) * m + col;
-      load8<float>(ahat + off, h[q]);
-      if constexpr (SENDER) load8<IN>(a + off, x[q]);
-    }
+  for (int p = 0; p < 4; ++p) {
+    const int col = c0 + 32 * (p >> 1) + 8 * (lr >> 2) + 4 * (p & 1) + (lr & 3);
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) av[p][j] = *reinterpret_cast<const f32x4*>(vb + (size_t)col * K + 16 * j + 4 * lk);
   }
   const float* ub = ud + (size_t)b * n * K;
-  const float* vb = vd + (size_t)b * m * K;
-  for (int idx = threadIdx.x; idx < kRcRows * K / 4; idx += blockDim.x) {
-    const int r = (4 * idx) / K, j = (4 * idx) % K;
-    const f32x4 v = (r0 + r < n) ? *reinterpret_cast<const f32x4*>(ub + (size_t)(r0 + r) * K + j)
-                                 : f32x4{0.f, 0.f, 0.f, 0.f};
-    Us[r * LD + j] = v.x; Us[r * LD + j + 1] = v.y; Us[r * LD + j + 2] = v.z; Us[r * LD + j + 3] = v.w;
-  }
-  for (int idx = threadIdx.x; idx < kRcCols * K / 4; idx += blockDim.x) {
-    const int r = (4 * idx) / K, j = (4 * idx) % K;
-    const f32x4 v = (c0 + r < m) ? *reinterpret_cast<const f32x4*>(vb + (size_t)(c0 + r) * K + j)
-                                 : f32x4{0.f, 0.f, 0.f, 0.f};
-    Vs[r * LD + j] = v.x; Vs[r * LD + j + 1] = v.y; Vs[r * LD + j + 2] = v.z; Vs[r * LD + j + 3] = v.w;
-  }
-  __syncthreads();
-  f32x4 acc[8];
+  struct Tile {
+    f32x4 bu[KJ];
+    F8 h[2], x[2];
+  };
+  auto load_tile = [&](int r0, Tile& T) {
+    const int row = r0 + lr;
+    const bool ok = row < rend;
+    const int rr = ok ? row : rbeg;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // MFMA tile p covers local columns 32 (p/2) + 8 (mi/4) + 4 (p%2) + mi%4, mi = 0..15
-  int vrow[8];
+    for (int j = 0; j < KJ; ++j) T.bu[j] = *reinterpret_cast<const f32x4*>(ub + (size_t)rr * K + 16 * j + 4 * lk);
 #pragma unroll
-  for (int p = 0; p < 8; ++p) vrow[p] = (32 * (p >> 1) + 8 * (lr >> 2) + 4 * (p & 1) + (lr & 3)) * LD;
-#pragma unroll 4
-  for (int k0 = 0; k0 < K; k0 += 4) {
-    const float bu = Us[(16 * w + lr) * LD + k0 + lk];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) acc[p] = mfma_f32(Vs[vrow[p] + k0 + lk], bu, acc[p]);
-  }
-  if (!row_ok) return;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int col = c0 + 32 * q + 8 * lk;
-    if (col >= m) continue;
-    const size_t off = ((size_t)b * n + row) * m + col;
-    const f32x4 cl = acc[2 * q], chh = acc[2 * q + 1];
-    const float c[8] = {cl.x, cl.y, cl.z, cl.w, chh.x, chh.y, chh.z, chh.w};
-    F8 hv = h[q];
-    if constexpr (SENDER) {
-      F8 ev;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float r = x[q].v[i] - hv.v[i];
-        ev.v[i] = r - c[i];
-        hv.v[i] = hv.v[i] + c[i];
-      }
-      store8_nt(e + off, ev);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) hv.v[i] = hv.v[i] + c[i];
+    for (int q = 0; q < 2; ++q) {
+      const size_t off = ((size_t)b * n + rr) * m + c0 + 32 * q + 8 * lk;
+      load8<float>(ahat + off, T.h[q]);
+      if constexpr (SENDER) load8<IN>(a + off, T.x[q]);
     }
-    store8(ahat + off, hv);
+  };
+  // Tiles alternate between two register sets; every load is unconditional (rows
+  // past the chunk read row rbeg and are never stored), so the compiler can keep
+  // the next tile's loads in flight while the current one computes.
+  auto compute_store = [&](int r0, const Tile& T) {
+    f32x4 acc[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KJ; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) acc[p] = mfma_f32(av[p][j][i], T.bu[j][i], acc[p]);
+    const int row = r0 + lr;
+    if (row >= rend) return;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const size_t off = ((size_t)b * n + row) * m + c0 + 32 * q + 8 * lk;
+      const f32x4 cl = acc[2 * q], chh = acc[2 * q + 1];
+      const float c[8] = {cl.x, cl.y, cl.z, cl.w, chh.x, chh.y, chh.z, chh.w};
+      F8 hv = T.h[q];
+      if constexpr (SENDER) {
+        F8 ev;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float r = T.x[q].v[i] - hv.v[i];
+          ev.v[i] = r - c[i];
+          hv.v[i] = hv.v[i] + c[i];
+        }
+        store8_nt(e + off, ev);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv.v[i] = hv.v[i] + c[i];
+      }
+      store8(ahat + off, hv);
+    }
+  };
+  Tile t0, t1;
+  load_tile(rbeg, t0);
+  for (int r0 = rbeg; r0 < rend; r0 += 32) {
+    load_tile(r0 + 16, t1);
+    compute_store(r0, t0);
+    load_tile(r0 + 32, t0);
+    if (r0 + 16 < rend) compute_store(r0 + 16, t1);
   }
+}
+
+// Grid of the reconstruct kernel: strips of 4 waves x row chunks x tensors,
+// with row chunks (multiples of 16 rows) sized for >= ~2048 blocks.
+struct RcGrid {
+  dim3 grid;
+  int chunk_rows;
+};
+inline RcGrid rc_grid(int n, int m, int B) {
+  const int sblocks = (m / kRcStrip + kRcWaves - 1) / kRcWaves;
+  int chunks = (3072 + sblocks * B - 1) / (sblocks * B);
+  const int tiles = (n + 15) / 16;
+  chunks = chunks < 1 ? 1 : (chunks > tiles ? tiles : chunks);
+  const int chunk_rows = ((tiles + chunks - 1) / chunks) * 16;
+  chunks = (n + chunk_rows - 1) / chunk_rows;
+  return RcGrid{dim3(sblocks, chunks, B), chunk_rows};
 }
 
 // ---------------------------------------------------------------- launchers
@@ -693,15 +726,15 @@ hipError_t lr_compress_k(bool bf16, const void* a, float* ahat, float* e, uint8_
   }
   hipLaunchKernelGGL((lr_int4_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, w.P, w.Qt,
                      w.amax, packed, w.ud, w.vd, L);
-  const int ntile_rc = ((n + kRcRows - 1) / kRcRows) * ((m + kRcCols - 1) / kRcCols);
+  const RcGrid g = rc_grid(n, m, B);
   if (bf16)
-    hipLaunchKernelGGL((lr_recon_kernel<uint16_t, true, K>), dim3(ntile_rc, B), dim3(256), 0, s,
+    hipLaunchKernelGGL((lr_recon_kernel<uint16_t, true, K>), g.grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(a), ahat, e, (const float*)w.ud,
-                       (const float*)w.vd, n, m);
+                       (const float*)w.vd, n, m, g.chunk_rows);
   else
-    hipLaunchKernelGGL((lr_recon_kernel<float, true, K>), dim3(ntile_rc, B), dim3(256), 0, s,
+    hipLaunchKernelGGL((lr_recon_kernel<float, true, K>), g.grid, dim3(256), 0, s,
                        static_cast<const float*>(a), ahat, e, (const float*)w.ud, (const float*)w.vd,
-                       n, m);
+                       n, m, g.chunk_rows);
   return hipGetLastError();
 }
 
@@ -711,10 +744,10 @@ hipError_t lr_decompress_k(const uint8_t* packed, float* ahat, int B, const Layo
   const int n = (int)L.rows, m = (int)L.cols;
   hipLaunchKernelGGL((lr_dequant_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, packed,
                      w.ud, w.vd, L);
-  const int ntile_rc = ((n + kRcRows - 1) / kRcRows) * ((m + kRcCols - 1) / kRcCols);
-  hipLaunchKernelGGL((lr_recon_kernel<float, false, K>), dim3(ntile_rc, B), dim3(256), 0, s,
+  const RcGrid g = rc_grid(n, m, B);
+  hipLaunchKernelGGL((lr_recon_kernel<float, false, K>), g.grid, dim3(256), 0, s,
                      (const float*)nullptr, ahat, (float*)nullptr, (const float*)w.ud,
-                     (const float*)w.vd, n, m);
+                     (const float*)w.vd, n, m, g.chunk_rows);
   return hipGetLastError();
 }
 

@@ -47,14 +47,23 @@ __global__ __launch_bounds__(kNmBlock) void nm_compress_kernel(const IN* __restr
   if (blockIdx.x == 0) nm_zero_padding(pk, L);
   const bool hi = threadIdx.x & 1;  // odd lane: elements 8..15 of its block
 
+  // every chunk's loads before the first store (see the quantiser kernel)
+  F8 xs[IT], hs[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int64_t ch = ((int64_t)blockIdx.x * IT + it) * kNmBlock + threadIdx.x;
+    const int64_t off = base + (ch < nch ? ch : (ch & 1)) * 8;
+    load8<IN>(a + off, xs[it]);
+    load8<float>(ahat + off, hs[it]);
+  }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int64_t ch = ((int64_t)blockIdx.x * IT + it) * kNmBlock + threadIdx.x;
     const bool valid = ch < nch;  // lane pairs are valid together (16 | n)
     const int64_t off = base + (valid ? ch : (ch & 1)) * 8;
-    F8 x, h, r;
-    load8<IN>(a + off, x);
-    load8<float>(ahat + off, h);
+    const F8& x = xs[it];
+    F8& h = hs[it];
+    F8 r;
 #pragma unroll
     for (int i = 0; i < 8; ++i) r.v[i] = x.v[i] - h.v[i];
 
@@ -136,13 +145,18 @@ __global__ __launch_bounds__(kNmBlock) void nm_decompress_kernel(const uint8_t* 
   const uint8_t* pk = packed + (int64_t)b * L.tstride;
   const uint32_t* vals = reinterpret_cast<const uint32_t*>(pk);
   const uint8_t* idxs = pk + L.sec_off[1];
+  F8 hs[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int64_t ch = ((int64_t)blockIdx.x * IT + it) * kNmBlock + threadIdx.x;
+    load8<float>(ahat + base + (ch < nch ? ch : 0) * 8, hs[it]);
+  }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int64_t ch = ((int64_t)blockIdx.x * IT + it) * kNmBlock + threadIdx.x;
     if (ch >= nch) continue;
     const int64_t off = base + ch * 8;
-    F8 h;
-    load8<float>(ahat + off, h);
+    F8& h = hs[it];
     const uint32_t v = vals[ch >> 1];
     const uint32_t id = idxs[ch >> 1];
     const uint32_t lo_i = id & 15u, hi_i = id >> 4;

@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "../../include/librescomp.h"
+#include "../../include/librescomp_diag.h"
 #include "launch.hpp"
 
 struct rc_plan {
@@ -252,8 +253,8 @@ size_t rc_tensor_packed_bytes(rc_plan_t pl) { return pl ? (size_t)pl->layout.tst
 
 size_t rc_workspace_bytes(rc_plan_t pl) { return pl ? pl->ws_bytes : 0; }
 
-// Diagnostics (not part of the public header): device pointers of the
-// low-rank workspace pieces, in the order R, P, Pbt, Qt, Q0t, Qtb, gsum, linv.
+// Diagnostics (librescomp_diag.h): device pointers of the low-rank workspace
+// pieces, in the order R, P, Pbt, Qt, Q0t, Qtb, gsum, linv.
 int rcx_lowrank_workspace(rc_plan_t pl, void** ptrs, int count) {
   if (!pl || pl->scheme != RC_LOWRANK || !ptrs || count < 8) return -1;
   const rc::LowRankWork& w = pl->lr;

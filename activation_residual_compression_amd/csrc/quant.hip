@@ -50,16 +50,27 @@ __global__ __launch_bounds__(kBlock) void q_compress_kernel(const IN* __restrict
   uint8_t* meta = pk + L.sec_off[1];
   if (blockIdx.x == 0) zero_padding(pk, L);
 
+  // All chunks' loads are issued before the first store: the stores go to
+  // ahat, so the compiler would otherwise keep each chunk's loads behind the
+  // previous chunk's stores.
+  F8 xs[IT], hs[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int64_t ch = ((int64_t)blockIdx.x * IT + it) * kBlock + threadIdx.x;
+    // Lanes past the end work on chunk 0 and store nothing; groups never mix
+    // valid and invalid lanes because a tensor holds whole groups.
+    const int64_t off = base + (ch < nch ? ch : 0) * 8;
+    load8<IN>(a + off, xs[it]);
+    load8<float>(ahat + off, hs[it]);
+  }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int64_t ch = ((int64_t)blockIdx.x * IT + it) * kBlock + threadIdx.x;
     const bool valid = ch < nch;
-    // Lanes past the end work on chunk 0 and store nothing; groups never mix
-    // valid and invalid lanes because a tensor holds whole groups.
     const int64_t off = base + (valid ? ch : 0) * 8;
-    F8 x, h, c, r;
-    load8<IN>(a + off, x);
-    load8<float>(ahat + off, h);
+    const F8& x = xs[it];
+    F8& h = hs[it];
+    F8 c, r;
 #pragma unroll
     for (int i = 0; i < 8; ++i) r.v[i] = x.v[i] - h.v[i];
 
@@ -129,13 +140,18 @@ __global__ __launch_bounds__(kBlock) void q_decompress_kernel(const uint8_t* __r
   const int64_t base = (int64_t)b * L.n;
   const uint8_t* pk = packed + (int64_t)b * L.tstride;
   const uint8_t* meta = pk + L.sec_off[1];
+  F8 hs[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int64_t ch = ((int64_t)blockIdx.x * IT + it) * kBlock + threadIdx.x;
+    load8<float>(ahat + base + (ch < nch ? ch : 0) * 8, hs[it]);
+  }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int64_t ch = ((int64_t)blockIdx.x * IT + it) * kBlock + threadIdx.x;
     if (ch >= nch) continue;
     const int64_t off = base + ch * 8;
-    F8 h;
-    load8<float>(ahat + off, h);
+    F8& h = hs[it];
     if constexpr (BITS == 1) {
       const uint32_t byte = pk[ch];
       const float scale = reinterpret_cast<const float*>(meta)[ch / LANES];

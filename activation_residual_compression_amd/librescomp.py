@@ -71,6 +71,8 @@ def _load():
     lib.rc_status_string.argtypes = [ctypes.c_int]
     lib.rcx_lowrank_workspace.restype = ctypes.c_int
     lib.rcx_lowrank_workspace.argtypes = [vp, ctypes.POINTER(vp), ctypes.c_int]
+    lib.rcx_hbm_probe.restype = ctypes.c_int
+    lib.rcx_hbm_probe.argtypes = [ctypes.c_int, vp, vp, vp, ctypes.c_int64, vp]
     return lib
 
 
@@ -154,6 +156,16 @@ def make_params(scheme, *, group=0, nm_keep=0, nm_block=0, rank=0, iters=0, q0=N
                     int(flags))
     p._q0_ref = q0
     return p
+
+
+RCX_PROBE_COPY, RCX_PROBE_READ, RCX_PROBE_WRITE, RCX_PROBE_SENDER_MIX, RCX_PROBE_RECEIVER_RMW = range(5)
+
+
+def rcx_hbm_probe(kind, a, b, c, n, stream=None):
+    """Launch one HBM reference kernel (librescomp_diag.h); raises on a HIP error."""
+    err = _lib.rcx_hbm_probe(int(kind), _ptr(a), _ptr(b), _ptr(c), int(n), _stream(stream))
+    if err != 0:
+        raise RuntimeError("rcx_hbm_probe: hipError %d" % err)
 
 
 # ------------------------------------------------------------------ convenience

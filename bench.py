@@ -27,11 +27,68 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+# kernel names (as rocprofv3 reports them) of each workload's sender kernel
+SENDER_KERNEL = {
+    "flux_q2": "q_compress_kernel<unsigned short, 128, 2, 2>",
+    "flux_nm": "nm_compress_kernel<unsigned short, 2>",
+    "video_q1": "q_compress_kernel<unsigned short, 64, 1, 2>",
+    "tiny_q1": "q_compress_kernel<float, 64, 1, 2>",
+}
+LR_CONTRACTIONS = {  # (kernel, launches per step) of the bf16 MFMA products
+    "flux_lr": [("lr_rq_kernel<unsigned short, true, 32>", 1), ("lr_rq_kernel<unsigned short, false, 32>", 1),
+                ("lr_rtp_kernel<32>", 2)],
+    "video_lr": [("lr_rq_kernel<unsigned short, true, 48>", 1), ("lr_rq_kernel<unsigned short, false, 48>", 1),
+                 ("lr_rtp_kernel<48>", 2)],
+}
+
+
+def _fresh_profile(name):
+    """A committed profile JSON, or None when the kernel sources changed since it was taken."""
+    import json as _json
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None
+    data = _json.load(open(path))
+    from activation_residual_compression_amd.profsummary import source_hashes
+    return data if data.get("sources") == source_hashes() else None
+
+
+def hbm_probe(n, log):
+    """Measured HBM ceilings of the path's access patterns (reference kernels) on
+    buffers of the default workload's size: a bf16 [n], b and c fp32 [n]."""
+    import torch
+    from activation_residual_compression_amd import librescomp as rc
+    n = n // 8 * 8
+    a = torch.zeros(n, dtype=torch.bfloat16, device="cuda:0")
+    b = torch.zeros(n, dtype=torch.float32, device="cuda:0")
+    c = torch.zeros(n, dtype=torch.float32, device="cuda:0")
+    out = {}
+    for kind, name, bpe, src in ((rc.RCX_PROBE_COPY, "copy", 8, b), (rc.RCX_PROBE_READ, "read", 4, b),
+                                 (rc.RCX_PROBE_WRITE, "write", 4, b),
+                                 (rc.RCX_PROBE_SENDER_MIX, "sender_mix", 14, a),
+                                 (rc.RCX_PROBE_RECEIVER_RMW, "receiver_rmw", 8, a)):
+        dst, aux = (c, b) if kind in (rc.RCX_PROBE_COPY, rc.RCX_PROBE_READ) else (b, c)
+        for _ in range(2):
+            rc.rcx_hbm_probe(kind, src, dst, aux, n)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            rc.rcx_hbm_probe(kind, src, dst, aux, n)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        out[name] = n * bpe / (ms * 1e6)
+    log("[bench] HBM reference kernels on %d elements (GB/s): " % n
+        + ", ".join("%s %.0f" % kv for kv in out.items()))
+    del a, b, c
+    torch.cuda.empty_cache()
+    return out
 
 
 def algorithmic_bytes(scheme, n_elem, in_bytes, group=None, rank=None, rows=None, cols=None, iters=None,
                       batch=None):
-    """Bytes each kernel family must move at minimum, per call (all tensors)."""
+    """Bytes each call must move at minimum (all tensors): compress and decompress."""
     N = n_elem
     if scheme == "q1":
         meta = N / 8 + 4 * N / group
@@ -56,6 +113,20 @@ def lr_flops(rows, cols, rank, iters, batch):
 
 
 _FRAMES = {}  # host frames per workload sequence, shared by the schemes measured on it
+
+
+def _probe_on(kind, a, b, c, n, reps=5):
+    import torch
+    from activation_residual_compression_amd import librescomp as rc
+    for _ in range(2):
+        rc.rcx_hbm_probe(kind, a, b, c, n)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        rc.rcx_hbm_probe(kind, a, b, c, n)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def measure(config, steps, warmup, max_frames, log):
@@ -128,6 +199,12 @@ def measure(config, steps, warmup, max_frames, log):
         out["tensors_per_ms"] = B / ms_step
         out["mfma_flops"] = fl
         out["mfma_util_whole_compress"] = fl / (c_ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    # reference kernels on these very buffers, after the timed region (the state is
+    # no longer needed): the HBM ceiling of the sender and receiver access patterns
+    if wl.dtype == "bf16" and N % 8 == 0:
+        from activation_residual_compression_amd import librescomp as rc
+        out["ref_sender_mix_GBps"] = 14.0 * N / (_probe_on(rc.RCX_PROBE_SENDER_MIX, seq[0], ahat, e, N) * 1e6)
+        out["ref_receiver_rmw_GBps"] = 8.0 * N / (_probe_on(rc.RCX_PROBE_RECEIVER_RMW, None, recon, None, N) * 1e6)
     plan.close()
     del frames, seq, ahat, recon, e, packed
     torch.cuda.empty_cache()
@@ -189,6 +266,7 @@ def main():
                     help="distinct input frames for the other workloads (cycled)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hbm-probe", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -221,6 +299,9 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
 
+    from activation_residual_compression_amd import synth as _synth
+    _wl = _synth.make(args.workload, tensors=[0])
+    ceiling = None if args.no_hbm_probe else hbm_probe(_wl.batch * _wl.n * _wl.m, log)
     main_res = measure(args.workload, args.steps, args.warmup, 64, log)
     log("[bench] %s: %.3f ms/step, %.1f GB/s input, compress %.3f ms (%.0f GB/s alg)" % (
         args.workload, main_res["ms_per_step"], main_res["input_GBps"], main_res["compress_ms"],
@@ -236,6 +317,26 @@ def main():
         cpu = cpu_baseline(args.workload, args.cpu_budget, log)
 
     ach = main_res["compress_GBps"]
+    traffic = None
+    pmc = _fresh_profile("pmc_traffic.json")
+    kname = SENDER_KERNEL.get(args.workload)
+    if pmc and kname in pmc["kernels"]:
+        traffic = pmc["kernels"][kname]["bytes"]
+    trace = _fresh_profile("kernel_trace.json")
+    for cfg, res in others.items():
+        if cfg in LR_CONTRACTIONS and trace:
+            ks = LR_CONTRACTIONS[cfg]
+            if all(k in trace["kernels"] for k, _ in ks):
+                us = sum(trace["kernels"][k]["avg_us"] * cnt for k, cnt in ks)
+                res["mfma_util_contractions"] = res["mfma_flops"] / (us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+                res["contraction_us_per_step"] = us
+    roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
+            "kernel": kname or "sender kernel (rc_compress)",
+            "alg_bytes_per_launch": main_res["alg_bytes_compress"]}
+    if "ref_sender_mix_GBps" in main_res:
+        roof["measured_ceiling"] = main_res["ref_sender_mix_GBps"]
+        roof["frac_of_measured_ceiling"] = ach / main_res["ref_sender_mix_GBps"]
     line = {
         "metric": "compress+decompress GB/s of activations per GPU (% HBM peak); low-rank MFMA util",
         "value": main_res["input_GBps"],
@@ -252,9 +353,8 @@ def main():
         "config": {"workload": "%s: %d bf16 tensors [%d x %d] per step, scheme %s" % (
             args.workload, *main_res["shape"], main_res["scheme"]),
             "steps_per_sequence": 28, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "sender kernel (rc_compress)"},
+        "roofline": roof,
+        "hbm_reference_kernels_GBps": ceiling,
         "hbm_frac_step": main_res["hbm_frac_step"],
         "cpu_baseline": cpu,
         "workloads": {args.workload: main_res, **others},

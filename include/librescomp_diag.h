@@ -1,0 +1,47 @@
+/*
+ * librescomp diagnostics: measurement helpers that are not part of the
+ * compression path. The tests and the benchmark use them; applications do not
+ * need them.
+ */
+#ifndef LIBRESCOMP_DIAG_H
+#define LIBRESCOMP_DIAG_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "librescomp.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HBM reference kernels (roofline ceilings for the path's access patterns).
+ * n = element count (multiple of 8). Device pointers, caller-owned:
+ *   RCX_PROBE_COPY         b[0..n) = a[0..n)              fp32, 8 B/element
+ *   RCX_PROBE_READ         reads a[0..n) fp32 (c: 1 float, written only in a
+ *                          case that never occurs for finite data), 4 B/element
+ *   RCX_PROBE_WRITE        writes b[0..n) fp32, 4 B/element
+ *   RCX_PROBE_SENDER_MIX   reads bf16 a[0..n) and fp32 b, writes b and c,
+ *                          14 B/element (the sender kernels' stream pattern)
+ *   RCX_PROBE_RECEIVER_RMW reads and rewrites fp32 b in place, 8 B/element
+ * Launches asynchronously on `stream`; returns a hipError_t value (0 = ok). */
+enum {
+  RCX_PROBE_COPY = 0,
+  RCX_PROBE_READ = 1,
+  RCX_PROBE_WRITE = 2,
+  RCX_PROBE_SENDER_MIX = 3,
+  RCX_PROBE_RECEIVER_RMW = 4,
+};
+int rcx_hbm_probe(int kind, const void* a, void* b, void* c, int64_t n, hipStream_t stream);
+
+/* Device pointers of a low-rank plan's workspace pieces, in the order R, P,
+ * Pbt, Qt, Q0t, Qtb, gsum, linv (count >= 8). Returns rows_pad, or -1 for a
+ * NULL plan, another scheme, or count < 8. */
+int rcx_lowrank_workspace(rc_plan_t plan, void** ptrs, int count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBRESCOMP_DIAG_H */

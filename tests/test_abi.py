@@ -11,7 +11,7 @@ import pytest
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "librescomp.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("librescomp.h", "librescomp_diag.h")]
 
 
 @pytest.fixture(scope="module")
@@ -21,9 +21,11 @@ def rc():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rc_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(rcx?_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_function(rc):
