@@ -33,32 +33,47 @@ __device__ __forceinline__ double dpp_f64(double v) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-// All-reduce over aligned groups of L lanes (L = 1, 2, 4, 8, 16). Every lane of
-// a group ends with the same value: each stage combines a lane with one partner
-// and the operations are commutative.
+// All-reduce over aligned groups of L lanes (L = 1, 2, 4, 8, 16, 32). Every lane
+// of a group ends with the same value: each stage combines a lane with one
+// partner and the operations are commutative. Stages inside a row of 16 lanes
+// are DPP moves; the 32-lane stage crosses rows with a lane-xor shuffle.
 template <int L>
 __device__ __forceinline__ double group_sum_f64(double v) {
+  static_assert(L >= 1 && L <= 32 && (L & (L - 1)) == 0, "group of 1..32 lanes");
   if constexpr (L >= 2) v += dpp_f64<kQuadXor1>(v);
   if constexpr (L >= 4) v += dpp_f64<kQuadXor2>(v);
   if constexpr (L >= 8) v += dpp_f64<kHalfMirror>(v);
   if constexpr (L >= 16) v += dpp_f64<kRowMirror>(v);
-  static_assert(L <= 16, "groups wider than a DPP row are not used");
+  if constexpr (L >= 32) v += __shfl_xor(v, 16);
   return v;
 }
 template <int L>
 __device__ __forceinline__ float group_min(float v) {
+  static_assert(L >= 1 && L <= 32 && (L & (L - 1)) == 0, "group of 1..32 lanes");
   if constexpr (L >= 2) v = fminf(v, dpp_f32<kQuadXor1>(v));
   if constexpr (L >= 4) v = fminf(v, dpp_f32<kQuadXor2>(v));
   if constexpr (L >= 8) v = fminf(v, dpp_f32<kHalfMirror>(v));
   if constexpr (L >= 16) v = fminf(v, dpp_f32<kRowMirror>(v));
+  if constexpr (L >= 32) v = fminf(v, __shfl_xor(v, 16));
   return v;
 }
 template <int L>
 __device__ __forceinline__ float group_max(float v) {
+  static_assert(L >= 1 && L <= 32 && (L & (L - 1)) == 0, "group of 1..32 lanes");
   if constexpr (L >= 2) v = fmaxf(v, dpp_f32<kQuadXor1>(v));
   if constexpr (L >= 4) v = fmaxf(v, dpp_f32<kQuadXor2>(v));
   if constexpr (L >= 8) v = fmaxf(v, dpp_f32<kHalfMirror>(v));
   if constexpr (L >= 16) v = fmaxf(v, dpp_f32<kRowMirror>(v));
+  if constexpr (L >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  return v;
+}
+// Bitwise OR over aligned groups of L lanes (L = 1, 2, 4, 8).
+template <int L>
+__device__ __forceinline__ uint32_t group_or(uint32_t v) {
+  static_assert(L >= 1 && L <= 8 && (L & (L - 1)) == 0, "group of 1..8 lanes");
+  if constexpr (L >= 2) v |= dpp_u32<kQuadXor1>(v);
+  if constexpr (L >= 4) v |= dpp_u32<kQuadXor2>(v);
+  if constexpr (L >= 8) v |= dpp_u32<kHalfMirror>(v);
   return v;
 }
 
@@ -71,11 +86,35 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// ---------------------------------------------------------------- 8-element chunks
-// One lane owns 8 consecutive elements: 16 B of bf16 or 32 B of fp32 input,
-// 32 B of each fp32 state array. Native vector types keep every access a
-// single 128-bit load or store.
+// ---------------------------------------------------------------- 4-element chunks
+// The streaming kernels give each lane 4 consecutive elements per chunk, so one
+// wave-wide load or store of a chunk covers a single contiguous run (1 KiB of
+// fp32, 512 B of bf16): every instruction fills whole cache lines by itself.
+// Every array these kernels touch is streamed once per launch and is far larger
+// than the caches, so loads and stores are non-temporal (streaming hint): on
+// this device that measurably raises the read/write mix the kernels sustain.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename IN>
+__device__ __forceinline__ f32x4 load4(const IN* p);
+template <>
+__device__ __forceinline__ f32x4 load4<uint16_t>(const uint16_t* p) {
+  const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+               __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+}
+template <>
+__device__ __forceinline__ f32x4 load4<float>(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ void store4(float* p, f32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+
+// ---------------------------------------------------------------- 8-element chunks
+// The low-rank kernels give a lane 8 consecutive elements: 16 B of bf16 or 32 B
+// of fp32 input, 32 B of each fp32 state array.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct F8 {

@@ -8,13 +8,16 @@
 //
 // Selection: in every block of 16 contiguous elements keep the 2 with the
 // largest |r|, ties to the lower index. No sort and no shared memory: a block is
-// two lanes (8 elements each, one 128-bit bf16 load). Each lane keeps a running
-// top-2 of its 8 elements in registers (strict comparisons in index order keep
-// the lower index on ties), the pair exchanges its lists with one DPP quad move
-// and both lanes merge them the same way. |r| is compared as the integer bit
-// pattern of the magnitude, which orders non-negative floats exactly.
-// Kept values travel as bf16 (round to nearest even); dropped positions decode
-// to 0, so e_t = r there and e_t = r - bf16(r) at kept positions.
+// a quad of lanes, each owning 4 consecutive elements (the lane layout of the
+// quantiser kernels, so every wave-wide access is one contiguous run). Each lane
+// keeps a running top-2 of its 4 elements in registers (strict comparisons in
+// index order keep the lower index on ties); the quad then merges lists twice,
+// first with the neighbouring lane, then with the neighbouring pair, each time
+// through DPP quad moves, so all four lanes end with the block's top-2. |r| is
+// compared as the integer bit pattern of the magnitude, which orders
+// non-negative floats exactly. Kept values travel as bf16 (round to nearest
+// even); dropped positions decode to 0, so e_t = r there and e_t = r - bf16(r)
+// at kept positions.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -32,167 +35,189 @@ __device__ __forceinline__ void nm_zero_padding(uint8_t* tensor_base, const Layo
 
 __device__ __forceinline__ float bf16_round_f32(float x) { return __uint_as_float(bf16_rne(x) << 16); }
 
-template <typename IN, int IT>
+// Running top-2 of a block: keys are |r| bit patterns, indices 0..15 in the block.
+struct Top2 {
+  uint32_t k1, k2, i1, i2;
+  float v1, v2;
+};
+
+__device__ __forceinline__ uint32_t mag_key(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+// Top-2 of A and B where every index in A is below every index in B: B only
+// wins a comparison when strictly larger. Written with selects only.
+__device__ __forceinline__ Top2 merge_top2(const Top2& A, const Top2& B) {
+  const bool bfirst = B.k1 > A.k1;
+  // runner-up: if B leads, the better of B's second and A's first; else the
+  // better of A's second and B's first
+  const bool b2 = B.k2 > A.k1, b1 = B.k1 > A.k2;
+  Top2 o;
+  o.k1 = bfirst ? B.k1 : A.k1;
+  o.i1 = bfirst ? B.i1 : A.i1;
+  o.v1 = bfirst ? B.v1 : A.v1;
+  o.k2 = bfirst ? (b2 ? B.k2 : A.k1) : (b1 ? B.k1 : A.k2);
+  o.i2 = bfirst ? (b2 ? B.i2 : A.i1) : (b1 ? B.i1 : A.i2);
+  o.v2 = bfirst ? (b2 ? B.v2 : A.v1) : (b1 ? B.v1 : A.v2);
+  return o;
+}
+
+// Merge this lane's list with the partner lane's (DPP pattern CTRL); `upper`
+// says that this lane's indices are the higher ones.
+template <int CTRL>
+__device__ __forceinline__ Top2 merge_with(const Top2& t, bool upper) {
+  const float pv1 = dpp_f32<CTRL>(t.v1), pv2 = dpp_f32<CTRL>(t.v2);
+  const uint32_t pidx = dpp_u32<CTRL>(t.i1 | (t.i2 << 8));
+  const uint32_t pi1 = pidx & 0xFFu, pi2 = pidx >> 8;
+  Top2 A, B;
+  A.v1 = upper ? pv1 : t.v1;  B.v1 = upper ? t.v1 : pv1;
+  A.v2 = upper ? pv2 : t.v2;  B.v2 = upper ? t.v2 : pv2;
+  A.i1 = upper ? pi1 : t.i1;  B.i1 = upper ? t.i1 : pi1;
+  A.i2 = upper ? pi2 : t.i2;  B.i2 = upper ? t.i2 : pi2;
+  A.k1 = mag_key(A.v1); A.k2 = mag_key(A.v2);
+  B.k1 = mag_key(B.v1); B.k2 = mag_key(B.v2);
+  return merge_top2(A, B);
+}
+
+template <typename IN, int NC>
 __global__ __launch_bounds__(kNmBlock) void nm_compress_kernel(const IN* __restrict__ a,
                                                                float* __restrict__ ahat,
                                                                float* __restrict__ e,
                                                                uint8_t* __restrict__ packed,
                                                                Layout L) {
   const int b = blockIdx.y;
-  const int64_t nch = L.n / 8;
+  const int64_t n4 = L.n / 4;
   const int64_t base = (int64_t)b * L.n;
   uint8_t* pk = packed + (int64_t)b * L.tstride;
   uint32_t* vals = reinterpret_cast<uint32_t*>(pk);
   uint8_t* idxs = pk + L.sec_off[1];
   if (blockIdx.x == 0) nm_zero_padding(pk, L);
-  const bool hi = threadIdx.x & 1;  // odd lane: elements 8..15 of its block
+  const uint32_t q = threadIdx.x & 3;  // this lane holds elements 4q .. 4q+3 of its block
 
-  // every chunk's loads before the first store (see the quantiser kernel)
-  F8 xs[IT], hs[IT];
+  // Every chunk's loads before the first store. Lanes past the end work on
+  // chunk 0 and store nothing; quads are valid together (16 | n).
+  f32x4 xs[NC], hs[NC];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int64_t ch = ((int64_t)blockIdx.x * IT + it) * kNmBlock + threadIdx.x;
-    const int64_t off = base + (ch < nch ? ch : (ch & 1)) * 8;
-    load8<IN>(a + off, xs[it]);
-    load8<float>(ahat + off, hs[it]);
+  for (int j = 0; j < NC; ++j) {
+    const int64_t c = ((int64_t)blockIdx.x * NC + j) * kNmBlock + threadIdx.x;
+    const int64_t off = base + (c < n4 ? c : (int64_t)q) * 4;
+    xs[j] = load4<IN>(a + off);
+    hs[j] = load4<float>(ahat + off);
   }
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int64_t ch = ((int64_t)blockIdx.x * IT + it) * kNmBlock + threadIdx.x;
-    const bool valid = ch < nch;  // lane pairs are valid together (16 | n)
-    const int64_t off = base + (valid ? ch : (ch & 1)) * 8;
-    const F8& x = xs[it];
-    F8& h = hs[it];
-    F8 r;
+  for (int j = 0; j < NC; ++j) {
+    const int64_t c = ((int64_t)blockIdx.x * NC + j) * kNmBlock + threadIdx.x;
+    const bool valid = c < n4;
+    const int64_t off = base + (valid ? c : (int64_t)q) * 4;
+    f32x4 r;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r.v[i] = x.v[i] - h.v[i];
+    for (int i = 0; i < 4; ++i) r[i] = xs[j][i] - hs[j][i];
 
-    // running top-2 of this lane's 8 elements
-    uint32_t k1 = __float_as_uint(r.v[0]) & 0x7FFFFFFFu, k2 = __float_as_uint(r.v[1]) & 0x7FFFFFFFu;
-    uint32_t i1 = 0, i2 = 1;
-    float v1 = r.v[0], v2 = r.v[1];
-    if (k2 > k1) {
-      const uint32_t tk = k1; k1 = k2; k2 = tk;
-      i1 = 1; i2 = 0;
-      const float tv = v1; v1 = v2; v2 = tv;
+    // running top-2 of this lane's 4 elements
+    Top2 t;
+    t.k1 = mag_key(r[0]); t.k2 = mag_key(r[1]);
+    t.i1 = 0; t.i2 = 1; t.v1 = r[0]; t.v2 = r[1];
+    if (t.k2 > t.k1) {
+      t.k1 = mag_key(r[1]); t.k2 = mag_key(r[0]);
+      t.i1 = 1; t.i2 = 0; t.v1 = r[1]; t.v2 = r[0];
     }
 #pragma unroll
-    for (int i = 2; i < 8; ++i) {
-      const uint32_t k = __float_as_uint(r.v[i]) & 0x7FFFFFFFu;
-      const bool top = k > k1, second = !top && k > k2;
-      k2 = top ? k1 : (second ? k : k2);
-      i2 = top ? i1 : (second ? (uint32_t)i : i2);
-      v2 = top ? v1 : (second ? r.v[i] : v2);
-      k1 = top ? k : k1;
-      i1 = top ? (uint32_t)i : i1;
-      v1 = top ? r.v[i] : v1;
+    for (int i = 2; i < 4; ++i) {
+      const uint32_t k = mag_key(r[i]);
+      const bool top = k > t.k1, second = !top && k > t.k2;
+      t.k2 = top ? t.k1 : (second ? k : t.k2);
+      t.i2 = top ? t.i1 : (second ? (uint32_t)i : t.i2);
+      t.v2 = top ? t.v1 : (second ? r[i] : t.v2);
+      t.k1 = top ? k : t.k1;
+      t.i1 = top ? (uint32_t)i : t.i1;
+      t.v1 = top ? r[i] : t.v1;
     }
-    if (hi) { i1 += 8; i2 += 8; }
-    // exchange with the partner lane of the block
-    const uint32_t pk1 = dpp_u32<kQuadXor1>(k1), pk2 = dpp_u32<kQuadXor1>(k2);
-    const uint32_t pidx = dpp_u32<kQuadXor1>(i1 | (i2 << 8));
-    const float pv1 = dpp_f32<kQuadXor1>(v1), pv2 = dpp_f32<kQuadXor1>(v2);
-    // A = list of the low lane (lower indices), B = list of the high lane
-    const uint32_t Ak1 = hi ? pk1 : k1, Ak2 = hi ? pk2 : k2;
-    const uint32_t Ai1 = hi ? (pidx & 0xFF) : i1, Ai2 = hi ? (pidx >> 8) : i2;
-    const float Av1 = hi ? pv1 : v1, Av2 = hi ? pv2 : v2;
-    const uint32_t Bk1 = hi ? k1 : pk1, Bk2 = hi ? k2 : pk2;
-    const uint32_t Bi1 = hi ? i1 : (pidx & 0xFF), Bi2 = hi ? i2 : (pidx >> 8);
-    const float Bv1 = hi ? v1 : pv1, Bv2 = hi ? v2 : pv2;
-    // merge: B only wins a comparison when strictly larger (A has lower indices)
-    uint32_t fi, si;
-    float fv, sv;
-    if (Bk1 > Ak1) {
-      fi = Bi1; fv = Bv1;
-      const bool b2 = Bk2 > Ak1;
-      si = b2 ? Bi2 : Ai1; sv = b2 ? Bv2 : Av1;
-    } else {
-      fi = Ai1; fv = Av1;
-      const bool b1 = Bk1 > Ak2;
-      si = b1 ? Bi1 : Ai2; sv = b1 ? Bv1 : Av2;
-    }
-    const bool swap = si < fi;
-    const uint32_t lo_i = swap ? si : fi, hi_i = swap ? fi : si;
-    const uint32_t lo_b = bf16_rne(swap ? sv : fv), hi_b = bf16_rne(swap ? fv : sv);
+    t.i1 += 4 * q;
+    t.i2 += 4 * q;
+    t = merge_with<kQuadXor1>(t, q & 1u);
+    t = merge_with<kQuadXor2>(t, q & 2u);
+
+    const bool swap = t.i2 < t.i1;
+    const uint32_t lo_i = swap ? t.i2 : t.i1, hi_i = swap ? t.i1 : t.i2;
+    const uint32_t lo_b = bf16_rne(swap ? t.v2 : t.v1), hi_b = bf16_rne(swap ? t.v1 : t.v2);
     const float lo_c = __uint_as_float(lo_b << 16), hi_c = __uint_as_float(hi_b << 16);
 
-    F8 ev;
-    const uint32_t first = hi ? 8u : 0u;
+    f32x4 ev, hn;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t g = first + i;
-      const float c = (g == lo_i) ? lo_c : ((g == hi_i) ? hi_c : 0.0f);
-      ev.v[i] = r.v[i] - c;
-      h.v[i] = h.v[i] + c;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t g = 4 * q + i;
+      const float cv = (g == lo_i) ? lo_c : ((g == hi_i) ? hi_c : 0.0f);
+      ev[i] = r[i] - cv;
+      hn[i] = hs[j][i] + cv;
     }
     if (valid) {
-      if (!hi) {
-        vals[ch >> 1] = lo_b | (hi_b << 16);
-        idxs[ch >> 1] = (uint8_t)(lo_i | (hi_i << 4));
+      if (q == 0) {
+        vals[c >> 2] = lo_b | (hi_b << 16);
+        idxs[c >> 2] = (uint8_t)(lo_i | (hi_i << 4));
       }
-      store8(ahat + off, h);
-      store8_nt(e + off, ev);
+      store4(ahat + off, hn);
+      store4(e + off, ev);
     }
   }
 }
 
-template <int IT>
+template <int NC>
 __global__ __launch_bounds__(kNmBlock) void nm_decompress_kernel(const uint8_t* __restrict__ packed,
                                                                  float* __restrict__ ahat, Layout L) {
   const int b = blockIdx.y;
-  const int64_t nch = L.n / 8;
+  const int64_t n4 = L.n / 4;
   const int64_t base = (int64_t)b * L.n;
   const uint8_t* pk = packed + (int64_t)b * L.tstride;
   const uint32_t* vals = reinterpret_cast<const uint32_t*>(pk);
   const uint8_t* idxs = pk + L.sec_off[1];
-  F8 hs[IT];
+  const uint32_t q = threadIdx.x & 3;
+  f32x4 hs[NC];
+  uint32_t vs[NC], ids[NC];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int64_t ch = ((int64_t)blockIdx.x * IT + it) * kNmBlock + threadIdx.x;
-    load8<float>(ahat + base + (ch < nch ? ch : 0) * 8, hs[it]);
+  for (int j = 0; j < NC; ++j) {
+    const int64_t c = ((int64_t)blockIdx.x * NC + j) * kNmBlock + threadIdx.x;
+    const int64_t cc = c < n4 ? c : 0;
+    hs[j] = load4<float>(ahat + base + cc * 4);
+    vs[j] = vals[cc >> 2];
+    ids[j] = idxs[cc >> 2];
   }
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int64_t ch = ((int64_t)blockIdx.x * IT + it) * kNmBlock + threadIdx.x;
-    if (ch >= nch) continue;
-    const int64_t off = base + ch * 8;
-    F8& h = hs[it];
-    const uint32_t v = vals[ch >> 1];
-    const uint32_t id = idxs[ch >> 1];
-    const uint32_t lo_i = id & 15u, hi_i = id >> 4;
-    const float lo_c = bf16_lo(v), hi_c = bf16_hi(v);
-    const uint32_t first = (ch & 1) ? 8u : 0u;
+  for (int j = 0; j < NC; ++j) {
+    const int64_t c = ((int64_t)blockIdx.x * NC + j) * kNmBlock + threadIdx.x;
+    if (c >= n4) continue;
+    const uint32_t lo_i = ids[j] & 15u, hi_i = ids[j] >> 4;
+    const float lo_c = bf16_lo(vs[j]), hi_c = bf16_hi(vs[j]);
+    f32x4 h = hs[j];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t g = first + i;
-      h.v[i] = h.v[i] + ((g == lo_i) ? lo_c : ((g == hi_i) ? hi_c : 0.0f));
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t g = 4 * q + i;
+      h[i] = h[i] + ((g == lo_i) ? lo_c : ((g == hi_i) ? hi_c : 0.0f));
     }
-    store8(ahat + off, h);
+    store4(ahat + base + c * 4, h);
   }
 }
 
 namespace {
-constexpr int kNmIt = 2;
+constexpr int kNmChunks = 4;     // chunks per lane, sender
+constexpr int kNmDecChunks = 2;  // chunks per lane, receiver
 }
 
 hipError_t launch_nm_compress(bool bf16_input, const void* a, float* ahat, float* e,
                               uint8_t* packed, int batch, const Layout& L, hipStream_t s) {
-  const int64_t nch = L.n / 8;
-  const dim3 grid((unsigned)((nch + kNmBlock * kNmIt - 1) / (kNmBlock * kNmIt)), (unsigned)batch);
+  const int64_t n4 = L.n / 4;
+  const dim3 grid((unsigned)((n4 + kNmBlock * kNmChunks - 1) / (kNmBlock * kNmChunks)), (unsigned)batch);
   if (bf16_input)
-    hipLaunchKernelGGL((nm_compress_kernel<uint16_t, kNmIt>), grid, dim3(kNmBlock), 0, s,
+    hipLaunchKernelGGL((nm_compress_kernel<uint16_t, kNmChunks>), grid, dim3(kNmBlock), 0, s,
                        static_cast<const uint16_t*>(a), ahat, e, packed, L);
   else
-    hipLaunchKernelGGL((nm_compress_kernel<float, kNmIt>), grid, dim3(kNmBlock), 0, s,
+    hipLaunchKernelGGL((nm_compress_kernel<float, kNmChunks>), grid, dim3(kNmBlock), 0, s,
                        static_cast<const float*>(a), ahat, e, packed, L);
   return hipGetLastError();
 }
 
 hipError_t launch_nm_decompress(const uint8_t* packed, float* ahat, int batch, const Layout& L,
                                 hipStream_t s) {
-  const int64_t nch = L.n / 8;
-  const dim3 grid((unsigned)((nch + kNmBlock * kNmIt - 1) / (kNmBlock * kNmIt)), (unsigned)batch);
-  hipLaunchKernelGGL((nm_decompress_kernel<kNmIt>), grid, dim3(kNmBlock), 0, s, packed, ahat, L);
+  const int64_t n4 = L.n / 4;
+  const dim3 grid((unsigned)((n4 + kNmBlock * kNmDecChunks - 1) / (kNmBlock * kNmDecChunks)), (unsigned)batch);
+  hipLaunchKernelGGL((nm_decompress_kernel<kNmDecChunks>), grid, dim3(kNmBlock), 0, s, packed, ahat, L);
   return hipGetLastError();
 }
 

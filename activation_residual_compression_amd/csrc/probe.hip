@@ -35,57 +35,56 @@ __global__ __launch_bounds__(kProbeBlock) void probe_write(f32x4* __restrict__ b
   if (i < n4) b[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// sender-like: per 8 elements read 16 B bf16 + 32 B fp32, write 32 B + 32 B (2
-// chunks per lane). As in the sender kernels, both chunks' loads are issued
-// before the first store, unconditionally (lanes past the end reread chunk 0
-// and store nothing).
+// sender-like: per 4 elements read 8 B bf16 + 16 B fp32, write 16 B + 16 B, in
+// the lane layout of the sender kernels (4 consecutive elements per lane and
+// chunk, kMixChunks chunks a block-width apart, all loads before the first
+// store; lanes past the end reread chunk 0 and store nothing).
+constexpr int kMixChunks = 4;
+constexpr int kRmwChunks = 2;
+
 __global__ __launch_bounds__(kProbeBlock) void probe_mix14(const uint16_t* __restrict__ a,
                                                            float* __restrict__ h, float* __restrict__ e,
-                                                           int64_t nch) {
-  F8 xs[2], hs[2];
+                                                           int64_t n4) {
+  f32x4 xs[kMixChunks], hs[kMixChunks];
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int64_t c = ((int64_t)blockIdx.x * 2 + it) * kProbeBlock + threadIdx.x;
-    const int64_t cc = c < nch ? c : 0;
-    load8<uint16_t>(a + cc * 8, xs[it]);
-    load8<float>(h + cc * 8, hs[it]);
+  for (int j = 0; j < kMixChunks; ++j) {
+    const int64_t c = ((int64_t)blockIdx.x * kMixChunks + j) * kProbeBlock + threadIdx.x;
+    const int64_t cc = c < n4 ? c : 0;
+    xs[j] = load4<uint16_t>(a + cc * 4);
+    hs[j] = load4<float>(h + cc * 4);
   }
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int64_t c = ((int64_t)blockIdx.x * 2 + it) * kProbeBlock + threadIdx.x;
-    const bool valid = c < nch;
-    const F8& x = xs[it];
-    F8& hv = hs[it];
-    F8 ev;
+  for (int j = 0; j < kMixChunks; ++j) {
+    const int64_t c = ((int64_t)blockIdx.x * kMixChunks + j) * kProbeBlock + threadIdx.x;
+    f32x4 ev, hn;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float r = x.v[i] - hv.v[i];
-      ev.v[i] = r;
-      hv.v[i] = hv.v[i] + 0.5f * r;
+    for (int i = 0; i < 4; ++i) {
+      const float r = xs[j][i] - hs[j][i];
+      ev[i] = r;
+      hn[i] = hs[j][i] + 0.5f * r;
     }
-    if (valid) {
-      store8(h + c * 8, hv);
-      store8_nt(e + c * 8, ev);
+    if (c < n4) {
+      store4(h + c * 4, hn);
+      store4(e + c * 4, ev);
     }
   }
 }
 
-// receiver-like: read and write back fp32 in place (2 chunks of 8 per lane)
-__global__ __launch_bounds__(kProbeBlock) void probe_rmw8(float* __restrict__ h, int64_t nch) {
-  F8 hs[2];
+// receiver-like: read and write back fp32 in place, same lane layout
+__global__ __launch_bounds__(kProbeBlock) void probe_rmw8(float* __restrict__ h, int64_t n4) {
+  f32x4 hs[kRmwChunks];
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int64_t c = ((int64_t)blockIdx.x * 2 + it) * kProbeBlock + threadIdx.x;
-    load8<float>(h + (c < nch ? c : 0) * 8, hs[it]);
+  for (int j = 0; j < kRmwChunks; ++j) {
+    const int64_t c = ((int64_t)blockIdx.x * kRmwChunks + j) * kProbeBlock + threadIdx.x;
+    hs[j] = load4<float>(h + (c < n4 ? c : 0) * 4);
   }
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int64_t c = ((int64_t)blockIdx.x * 2 + it) * kProbeBlock + threadIdx.x;
-    const bool valid = c < nch;
-    F8& hv = hs[it];
+  for (int j = 0; j < kRmwChunks; ++j) {
+    const int64_t c = ((int64_t)blockIdx.x * kRmwChunks + j) * kProbeBlock + threadIdx.x;
+    f32x4 hn;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) hv.v[i] = hv.v[i] + 1.0f;
-    if (valid) store8(h + c * 8, hv);
+    for (int i = 0; i < 4; ++i) hn[i] = hs[j][i] + 1.0f;
+    if (c < n4) store4(h + c * 4, hn);
   }
 }
 
@@ -95,9 +94,10 @@ __global__ __launch_bounds__(kProbeBlock) void probe_rmw8(float* __restrict__ h,
 extern "C" int rcx_hbm_probe(int kind, const void* a, void* b, void* c, int64_t n, hipStream_t s) {
   using namespace rc;
   if (n <= 0 || n % 8) return (int)hipErrorInvalidValue;
-  const int64_t n4 = n / 4, nch = n / 8;
+  const int64_t n4 = n / 4;
   const unsigned g4 = (unsigned)((n4 + kProbeBlock - 1) / kProbeBlock);
-  const unsigned g8 = (unsigned)((nch + 2 * kProbeBlock - 1) / (2 * kProbeBlock));
+  const unsigned gmix = (unsigned)((n4 + kMixChunks * kProbeBlock - 1) / (kMixChunks * kProbeBlock));
+  const unsigned grmw = (unsigned)((n4 + kRmwChunks * kProbeBlock - 1) / (kRmwChunks * kProbeBlock));
   switch (kind) {
     case RCX_PROBE_COPY:
       hipLaunchKernelGGL(probe_copy, dim3(g4), dim3(kProbeBlock), 0, s, (const f32x4*)a, (f32x4*)b, n4);
@@ -109,11 +109,11 @@ extern "C" int rcx_hbm_probe(int kind, const void* a, void* b, void* c, int64_t 
       hipLaunchKernelGGL(probe_write, dim3(g4), dim3(kProbeBlock), 0, s, (f32x4*)b, n4);
       break;
     case RCX_PROBE_SENDER_MIX:
-      hipLaunchKernelGGL(probe_mix14, dim3(g8), dim3(kProbeBlock), 0, s, (const uint16_t*)a, (float*)b,
-                         (float*)c, nch);
+      hipLaunchKernelGGL(probe_mix14, dim3(gmix), dim3(kProbeBlock), 0, s, (const uint16_t*)a, (float*)b,
+                         (float*)c, n4);
       break;
     case RCX_PROBE_RECEIVER_RMW:
-      hipLaunchKernelGGL(probe_rmw8, dim3(g8), dim3(kProbeBlock), 0, s, (float*)b, nch);
+      hipLaunchKernelGGL(probe_rmw8, dim3(grmw), dim3(kProbeBlock), 0, s, (float*)b, n4);
       break;
     default:
       return (int)hipErrorInvalidValue;

@@ -5,11 +5,14 @@
 // receiver's reconstruction, receiver update), Key designs / Error feedback
 // (e_t = r - C(r) kept locally), Main experiment table (1-bit 16x, 2-bit 8x).
 //
-// One fused pass per step on the sender: each lane loads 8 consecutive
-// elements of a_t (one 128-bit load of bf16) and of ahat (two 128-bit loads),
-// forms r = a_t - ahat, reduces the group statistic across the G/8 lanes of its
-// group with DPP row moves, encodes, and writes codes, group metadata, e_t and
-// the new ahat. The receiver kernel decodes and accumulates in one pass.
+// One fused pass per step on the sender. A lane owns 4 consecutive elements
+// per chunk and NC chunks spaced one block-width apart, so each wave-wide access
+// is one contiguous run; all chunks are loaded before the first store. The lane
+// forms r = a_t - ahat, reduces the group statistic across the G/4 lanes of its
+// group (DPP row moves, one lane-xor shuffle for 32 lanes), encodes, gathers
+// the codes of 4 (2-bit) or 8 (1-bit) lanes into one 32-bit word, and writes
+// codes, group metadata, e_t and the new ahat. The receiver kernel decodes and
+// accumulates in one pass with the same lane layout.
 //
 // Arithmetic (fp32, one rounding per operation, no contraction):
 //   Q1: s = fp32(sum_fp64 |r| / G), bit = (r >= 0), c = bit ? s : -s
@@ -37,67 +40,61 @@ __device__ __forceinline__ void zero_padding(uint8_t* tensor_base, const Layout&
   }
 }
 
-template <typename IN, int G, int BITS, int IT>
+template <typename IN, int G, int BITS, int NC>
 __global__ __launch_bounds__(kBlock) void q_compress_kernel(const IN* __restrict__ a,
                                                             float* __restrict__ ahat,
                                                             float* __restrict__ e,
                                                             uint8_t* __restrict__ packed, Layout L) {
-  constexpr int LANES = G / 8;  // lanes per group
+  constexpr int LANES = G / 4;  // lanes per group
   const int b = blockIdx.y;
-  const int64_t nch = L.n / 8;
+  const int64_t n4 = L.n / 4;
   const int64_t base = (int64_t)b * L.n;
   uint8_t* pk = packed + (int64_t)b * L.tstride;
   uint8_t* meta = pk + L.sec_off[1];
   if (blockIdx.x == 0) zero_padding(pk, L);
 
-  // All chunks' loads are issued before the first store: the stores go to
-  // ahat, so the compiler would otherwise keep each chunk's loads behind the
-  // previous chunk's stores.
-  F8 xs[IT], hs[IT];
+  // Lanes past the end work on chunk 0 and store nothing; a group (and the
+  // 4 or 8 lanes sharing a code word) never mixes valid and invalid lanes
+  // because a tensor holds whole groups.
+  f32x4 xs[NC], hs[NC];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int64_t ch = ((int64_t)blockIdx.x * IT + it) * kBlock + threadIdx.x;
-    // Lanes past the end work on chunk 0 and store nothing; groups never mix
-    // valid and invalid lanes because a tensor holds whole groups.
-    const int64_t off = base + (ch < nch ? ch : 0) * 8;
-    load8<IN>(a + off, xs[it]);
-    load8<float>(ahat + off, hs[it]);
+  for (int j = 0; j < NC; ++j) {
+    const int64_t c = ((int64_t)blockIdx.x * NC + j) * kBlock + threadIdx.x;
+    const int64_t off = base + (c < n4 ? c : 0) * 4;
+    xs[j] = load4<IN>(a + off);
+    hs[j] = load4<float>(ahat + off);
   }
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int64_t ch = ((int64_t)blockIdx.x * IT + it) * kBlock + threadIdx.x;
-    const bool valid = ch < nch;
-    const int64_t off = base + (valid ? ch : 0) * 8;
-    const F8& x = xs[it];
-    F8& h = hs[it];
-    F8 c, r;
+  for (int j = 0; j < NC; ++j) {
+    const int64_t c = ((int64_t)blockIdx.x * NC + j) * kBlock + threadIdx.x;
+    const bool valid = c < n4;
+    const int64_t off = base + (valid ? c : 0) * 4;
+    f32x4 r, cq;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r.v[i] = x.v[i] - h.v[i];
+    for (int i = 0; i < 4; ++i) r[i] = xs[j][i] - hs[j][i];
 
     if constexpr (BITS == 1) {
       double s = 0.0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s += (double)fabsf(r.v[i]);
+      for (int i = 0; i < 4; ++i) s += (double)fabsf(r[i]);
       s = group_sum_f64<LANES>(s);
       const float scale = (float)(s * (1.0 / G));
-      uint32_t byte = 0;
+      uint32_t nib = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bool pos = r.v[i] >= 0.0f;
-        byte |= (pos ? 1u : 0u) << i;
-        c.v[i] = pos ? scale : -scale;
+      for (int i = 0; i < 4; ++i) {
+        const bool pos = r[i] >= 0.0f;
+        nib |= (pos ? 1u : 0u) << i;
+        cq[i] = pos ? scale : -scale;
       }
+      // word w holds the sign bits of elements 32w .. 32w+31 (8 lanes)
+      const uint32_t word = group_or<8>(nib << (4 * (threadIdx.x & 7)));
       if (valid) {
-        pk[ch] = (uint8_t)byte;
-        if ((ch % LANES) == 0) reinterpret_cast<float*>(meta)[ch / LANES] = scale;
+        if ((threadIdx.x & 7) == 0) reinterpret_cast<uint32_t*>(pk)[c >> 3] = word;
+        if ((c % LANES) == 0) reinterpret_cast<float*>(meta)[c / LANES] = scale;
       }
     } else {
-      float mn = r.v[0], mx = r.v[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) {
-        mn = fminf(mn, r.v[i]);
-        mx = fmaxf(mx, r.v[i]);
-      }
+      float mn = fminf(fminf(r[0], r[1]), fminf(r[2], r[3]));
+      float mx = fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3]));
       // zeros of the stored minimum and step are normalised to +0 (x + 0)
       mn = group_min<LANES>(mn) + 0.0f;
       mx = group_max<LANES>(mx);
@@ -106,76 +103,80 @@ __global__ __launch_bounds__(kBlock) void q_compress_kernel(const IN* __restrict
       const float inv = 1.0f / d;
       uint32_t code = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float t = (r.v[i] - mn) * inv;
+      for (int i = 0; i < 4; ++i) {
+        const float t = (r[i] - mn) * inv;
         const float q = live ? fminf(rintf(t), 3.0f) : 0.0f;
         code |= ((uint32_t)q) << (2 * i);
-        c.v[i] = fmaf(q, d, mn);
+        cq[i] = fmaf(q, d, mn);
       }
+      // word w holds the codes of elements 16w .. 16w+15 (4 lanes)
+      const uint32_t word = group_or<4>(code << (8 * (threadIdx.x & 3)));
       if (valid) {
-        reinterpret_cast<uint16_t*>(pk)[ch] = (uint16_t)code;
-        if ((ch % LANES) == 0) reinterpret_cast<float2*>(meta)[ch / LANES] = make_float2(mn, d);
+        if ((threadIdx.x & 3) == 0) reinterpret_cast<uint32_t*>(pk)[c >> 2] = word;
+        if ((c % LANES) == 0) reinterpret_cast<float2*>(meta)[c / LANES] = make_float2(mn, d);
       }
     }
 
-    F8 ev;
+    f32x4 ev, hn;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ev.v[i] = r.v[i] - c.v[i];
-      h.v[i] = h.v[i] + c.v[i];
+    for (int i = 0; i < 4; ++i) {
+      ev[i] = r[i] - cq[i];
+      hn[i] = hs[j][i] + cq[i];
     }
     if (valid) {
-      store8(ahat + off, h);
-      store8_nt(e + off, ev);
+      store4(ahat + off, hn);
+      store4(e + off, ev);
     }
   }
 }
 
-template <int G, int BITS, int IT>
+template <int G, int BITS, int NC>
 __global__ __launch_bounds__(kBlock) void q_decompress_kernel(const uint8_t* __restrict__ packed,
                                                               float* __restrict__ ahat, Layout L) {
-  constexpr int LANES = G / 8;
+  constexpr int LANES = G / 4;
   const int b = blockIdx.y;
-  const int64_t nch = L.n / 8;
+  const int64_t n4 = L.n / 4;
   const int64_t base = (int64_t)b * L.n;
   const uint8_t* pk = packed + (int64_t)b * L.tstride;
   const uint8_t* meta = pk + L.sec_off[1];
-  F8 hs[IT];
+  f32x4 hs[NC];
+  uint32_t codes[NC];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int64_t ch = ((int64_t)blockIdx.x * IT + it) * kBlock + threadIdx.x;
-    load8<float>(ahat + base + (ch < nch ? ch : 0) * 8, hs[it]);
+  for (int j = 0; j < NC; ++j) {
+    const int64_t c = ((int64_t)blockIdx.x * NC + j) * kBlock + threadIdx.x;
+    const int64_t cc = c < n4 ? c : 0;
+    hs[j] = load4<float>(ahat + base + cc * 4);
+    codes[j] = BITS == 1 ? pk[cc >> 1] : pk[cc];
   }
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int64_t ch = ((int64_t)blockIdx.x * IT + it) * kBlock + threadIdx.x;
-    if (ch >= nch) continue;
-    const int64_t off = base + ch * 8;
-    F8& h = hs[it];
+  for (int j = 0; j < NC; ++j) {
+    const int64_t c = ((int64_t)blockIdx.x * NC + j) * kBlock + threadIdx.x;
+    if (c >= n4) continue;
+    f32x4 h = hs[j];
     if constexpr (BITS == 1) {
-      const uint32_t byte = pk[ch];
-      const float scale = reinterpret_cast<const float*>(meta)[ch / LANES];
+      const uint32_t nib = codes[j] >> (4 * (c & 1));
+      const float scale = reinterpret_cast<const float*>(meta)[c / LANES];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) h.v[i] = h.v[i] + (((byte >> i) & 1u) ? scale : -scale);
+      for (int i = 0; i < 4; ++i) h[i] = h[i] + (((nib >> i) & 1u) ? scale : -scale);
     } else {
-      const uint32_t code = reinterpret_cast<const uint16_t*>(pk)[ch];
-      const float2 md = reinterpret_cast<const float2*>(meta)[ch / LANES];
+      const float2 md = reinterpret_cast<const float2*>(meta)[c / LANES];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) h.v[i] = h.v[i] + fmaf((float)((code >> (2 * i)) & 3u), md.y, md.x);
+      for (int i = 0; i < 4; ++i) h[i] = h[i] + fmaf((float)((codes[j] >> (2 * i)) & 3u), md.y, md.x);
     }
-    store8(ahat + off, h);
+    store4(ahat + base + c * 4, h);
   }
 }
 
 namespace {
-constexpr int kIt = 2;  // chunks per lane
+constexpr int kChunks = 4;     // chunks per lane, sender
+constexpr int kDecChunks = 2;  // chunks per lane, receiver
 
 template <typename IN, int G, int BITS>
 hipError_t q_compress_t(const void* a, float* ahat, float* e, uint8_t* packed, int batch,
                         const Layout& L, hipStream_t s) {
-  const int64_t nch = L.n / 8;
-  const dim3 grid((unsigned)((nch + kBlock * kIt - 1) / (kBlock * kIt)), (unsigned)batch);
-  hipLaunchKernelGGL((q_compress_kernel<IN, G, BITS, kIt>), grid, dim3(kBlock), 0, s,
+  const int64_t n4 = L.n / 4;
+  const dim3 grid((unsigned)((n4 + kBlock * kChunks - 1) / (kBlock * kChunks)), (unsigned)batch);
+  hipLaunchKernelGGL((q_compress_kernel<IN, G, BITS, kChunks>), grid, dim3(kBlock), 0, s,
                      static_cast<const IN*>(a), ahat, e, packed, L);
   return hipGetLastError();
 }
@@ -183,9 +184,9 @@ hipError_t q_compress_t(const void* a, float* ahat, float* e, uint8_t* packed, i
 template <int G, int BITS>
 hipError_t q_decompress_t(const uint8_t* packed, float* ahat, int batch, const Layout& L,
                           hipStream_t s) {
-  const int64_t nch = L.n / 8;
-  const dim3 grid((unsigned)((nch + kBlock * kIt - 1) / (kBlock * kIt)), (unsigned)batch);
-  hipLaunchKernelGGL((q_decompress_kernel<G, BITS, kIt>), grid, dim3(kBlock), 0, s, packed, ahat, L);
+  const int64_t n4 = L.n / 4;
+  const dim3 grid((unsigned)((n4 + kBlock * kDecChunks - 1) / (kBlock * kDecChunks)), (unsigned)batch);
+  hipLaunchKernelGGL((q_decompress_kernel<G, BITS, kDecChunks>), grid, dim3(kBlock), 0, s, packed, ahat, L);
   return hipGetLastError();
 }
 

@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 output (rocpd SQLite databases) for the profiles/ folder.
 
-  python -m activation_residual_compression_amd.profsummary trace <trace_results.db> [--md OUT]
+  python -m activation_residual_compression_amd.profsummary trace <trace_results.db> [--md OUT] [--json OUT]
       per-kernel dispatch count and duration (avg/min/max, microseconds)
 
   python -m activation_residual_compression_amd.profsummary pmc <fetch.db> <write.db> [--md OUT] [--json OUT]
@@ -9,6 +9,9 @@
       plain 1 GiB -> 1 GiB device copy (__amd_rocclr_copyBuffer) captured in the run.
       The JSON records the sha256 of the kernel sources, so a later reader can tell
       whether the kernels changed since the counters were taken.
+
+--title and --command (repeatable) put a heading and the commands that made the
+databases at the top of the Markdown summary.
 """
 from __future__ import annotations
 
@@ -77,7 +80,15 @@ def main(argv=None):
     p.add_argument("write_db")
     p.add_argument("--md")
     p.add_argument("--json")
+    for q in (t, p):
+        q.add_argument("--title")
+        q.add_argument("--command", action="append", default=[])
     args = ap.parse_args(argv)
+    head = []
+    if args.title:
+        head += ["# " + args.title, ""]
+    if args.command:
+        head += ["Made by:", "", "```"] + args.command + ["```", ""]
 
     if args.mode == "trace":
         rows = trace_table(args.db)
@@ -110,6 +121,7 @@ def main(argv=None):
             lines.append("| `%s` | %d | %.0f | %.0f | %.1f |" % (k, v["dispatches"], v["fetch_kb"],
                                                               v["write_kb"], v["bytes"] / 2 ** 20))
         text = "\n".join(lines)
+    text = "\n".join(head) + text
     if args.md:
         open(args.md, "w").write(text + "\n")
     print(text)

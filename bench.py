@@ -318,7 +318,7 @@ def main():
 
     ach = main_res["compress_GBps"]
     traffic = None
-    pmc = _fresh_profile("pmc_traffic.json")
+    pmc = _fresh_profile("bench_workloads_hbm_traffic.json")
     kname = SENDER_KERNEL.get(args.workload)
     if pmc and kname in pmc["kernels"]:
         traffic = pmc["kernels"][kname]["bytes"]
