@@ -60,11 +60,13 @@ def pmc_values(db: str, counter: str):
 
 
 def calibration(vals) -> float:
-    """Factor = true KB / counter KB for the 1 GiB copies in the run."""
-    cands = [v for v in vals.get("__amd_rocclr_copyBuffer", []) if v > 0.25 * COPY_BYTES_KB]
-    if not cands:
-        raise SystemExit("no 1 GiB __amd_rocclr_copyBuffer dispatch in the run (bench.py --copy-calibration)")
-    cands.sort()
+    """Factor = true KB / counter KB for the 1 GiB copies in the run: the largest
+    __amd_rocclr_copyBuffer dispatches (other copies in the run are smaller)."""
+    copies = vals.get("__amd_rocclr_copyBuffer", [])
+    if not copies:
+        raise SystemExit("no __amd_rocclr_copyBuffer dispatch in the run (bench.py --copy-calibration)")
+    top = max(copies)
+    cands = sorted(v for v in copies if v > 0.9 * top)
     return COPY_BYTES_KB / cands[len(cands) // 2]
 
 
@@ -121,7 +123,7 @@ def main(argv=None):
             lines.append("| `%s` | %d | %.0f | %.0f | %.1f |" % (k, v["dispatches"], v["fetch_kb"],
                                                               v["write_kb"], v["bytes"] / 2 ** 20))
         text = "\n".join(lines)
-    text = "\n".join(head) + text
+    text = "\n".join(head) + ("\n" if head else "") + text
     if args.md:
         open(args.md, "w").write(text + "\n")
     print(text)

@@ -322,7 +322,7 @@ def main():
     kname = SENDER_KERNEL.get(args.workload)
     if pmc and kname in pmc["kernels"]:
         traffic = pmc["kernels"][kname]["bytes"]
-    trace = _fresh_profile("kernel_trace.json")
+    trace = _fresh_profile("bench_workloads_kernel_trace.json")
     for cfg, res in others.items():
         if cfg in LR_CONTRACTIONS and trace:
             ks = LR_CONTRACTIONS[cfg]
