@@ -137,7 +137,7 @@ def accumulate(c, ahat) -> np.ndarray:
 # ------------------------------------------------------------ schemes
 def q1_encode(r, group=64):
     r = _f32(r)
-    assert r.size % group == 0 and group % 8 == 0
+    assert r.size % group == 0 and group in (8, 16, 32, 64, 128, 256)
     bits = np.zeros(r.size // 8, np.uint8)
     scale = np.empty(r.size // group, np.float32)
     _load().orc_q1_encode(r.size, group, _p(r), _p(bits), _p(scale))

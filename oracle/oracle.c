@@ -107,14 +107,28 @@ void orc_accumulate_f64(int64_t count, const double* c, float* ahat) {
  * minimises the squared error for fixed signs), computed as an fp64 sum
  * rounded once to fp32 after dividing by the group size; the bit is 1 when
  * r >= 0 (so -0 and +0 both give 1). Bits are LSB-first: element k of the
- * array is bit k%8 of byte k/8. */
+ * array is bit k%8 of byte k/8.
+ * The pages fix no summation order, and an fp64 sum of fp32 magnitudes is
+ * exact only while they span less than about 2^23, so the order is part of the
+ * reading: each run of 4 contiguous elements is summed left to right, then the
+ * run sums are added pairwise, neighbours first (a balanced binary tree). */
+static double q1_abs_sum(const float* r, int group) {
+  double part[64]; /* group <= 256: at most 64 runs of 4 */
+  const int runs = group / 4;
+  for (int j = 0; j < runs; ++j) {
+    double s = fabs((double)r[4 * j]);
+    for (int i = 1; i < 4; ++i) s += fabs((double)r[4 * j + i]);
+    part[j] = s;
+  }
+  for (int len = runs; len > 1; len /= 2)
+    for (int j = 0; j < len / 2; ++j) part[j] = part[2 * j] + part[2 * j + 1];
+  return part[0];
+}
+
 void orc_q1_encode(int64_t count, int group, const float* r, uint8_t* bits, float* scale) {
   memset(bits, 0, (size_t)(count / 8));
-  for (int64_t g = 0; g < count / group; ++g) {
-    double sum = 0.0;
-    for (int i = 0; i < group; ++i) sum += fabs((double)r[g * group + i]);
-    scale[g] = (float)(sum / (double)group);
-  }
+  for (int64_t g = 0; g < count / group; ++g)
+    scale[g] = (float)(q1_abs_sum(r + g * group, group) / (double)group);
   for (int64_t k = 0; k < count; ++k)
     if (r[k] >= 0.0f) bits[k / 8] |= (uint8_t)(1u << (k % 8));
 }

@@ -105,6 +105,51 @@ def test_crafted_edge_cases(scheme, group):
         run.close()
 
 
+def _q1_order_sensitive_groups(n, m, group, seed):
+    """Groups whose exact |r| sum puts the mean just above an fp32 rounding
+    midpoint, by terms that vanish when added one at a time to a large running
+    sum: the first half of each group sums to group * (1 + 2^-24) (the midpoint
+    between 1 and 1 + 2^-23, times group), the second half holds group/2 terms of
+    2^-51 that together make one fp64 ulp of that sum. Added left to right the
+    small terms are lost and the mean rounds to even (1.0); summed among
+    themselves first they survive and it rounds up. Each group is scaled by a
+    power of two and given random signs (both exact)."""
+    rng = np.random.default_rng(seed)
+    half = group // 2
+    g = np.empty(group, np.float64)
+    g[:half] = 2.0
+    g[half - 1] = 2.0 + group * 2.0 ** -24
+    g[half:] = 2.0 ** -51
+    rows = np.tile(g, (n * m // group, 1))
+    rows *= 2.0 ** rng.integers(-20, 20, (rows.shape[0], 1)).astype(np.float64)
+    rows *= rng.choice([-1.0, 1.0], rows.shape)
+    return rows.reshape(n, m).astype(np.float32)
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_q1_summation_order_sensitive_groups(group):
+    """The 1-bit scale is an fp64 sum in a fixed order (runs of 4, then a
+    pairwise tree); on groups where that order decides the fp32 scale the GPU
+    must still match the oracle bit for bit."""
+    n, m = 48, 512
+    a = _q1_order_sensitive_groups(n, m, group, seed=11)
+    ahat = np.zeros((n, m), np.float32)
+    # precondition: a left-to-right fp64 sum would give other scales
+    seq = np.array([np.float32(sum(abs(float(v)) for v in row) / group)
+                    for row in a.reshape(-1, group)], np.float32)
+    _, want = oracle.q1_encode(a.reshape(-1), group)
+    assert np.all(seq.view(np.uint32) != want.view(np.uint32))
+    run = GpuRun((1, n, m), "f32", "q1", group=group)
+    try:
+        run.set_state(ahat[None])
+        say("[gpu] q1 order-sensitive groups, group %d" % group)
+        run.step(a[None])
+        packed, e, ahat_g, recon = run.fetch()
+        check_exact_step(run, 0, a, ahat, packed, e, ahat_g, recon, dict(group=group))
+    finally:
+        run.close()
+
+
 @pytest.mark.parametrize("scheme,group", [("q1", 64), ("q2", 128), ("nm", None)])
 def test_zero_residual_everywhere(scheme, group):
     wl = synth.FluxWorkload(batch=2, n=33, m=256, steps=1)

@@ -54,6 +54,45 @@ def test_q1_scale_is_exactly_rounded_mean_abs():
         assert f32_bits(scale[g]) == f32_bits(round_fraction_to_f32(exact)), g
 
 
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_q1_scale_exactly_rounded_when_small_terms_decide(group):
+    # The first half of the group sums to group * (1 + 2^-24), so the mean is
+    # the midpoint between 1 and 1 + 2^-23; the second half adds group/2 terms
+    # of 2^-51, pushing the exact mean just above it. The correctly rounded
+    # scale is 1 + 2^-23. (Added one at a time to the large running sum, the
+    # small terms would vanish and the tie would round down to 1.0.)
+    half = group // 2
+    g = np.full(group, 2.0)
+    g[half - 1] = 2.0 + group * 2.0 ** -24
+    g[half:] = 2.0 ** -51
+    for k, sign_seed in ((0, 1), (7, 2), (-9, 3)):
+        r = (g * 2.0 ** k * np.random.default_rng(sign_seed).choice([-1.0, 1.0], group)).astype(np.float32)
+        _, scale = oracle.q1_encode(r, group)
+        exact = sum(Fraction(float(abs(v))) for v in r) / group
+        assert f32_bits(scale[0]) == f32_bits(round_fraction_to_f32(exact))
+        assert scale[0] == np.float32((1 + 2.0 ** -23) * 2.0 ** k)
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_q1_scale_wide_magnitude_span_within_summation_bound(group):
+    # Magnitudes spread over 2^-45 .. 2 make the fp64 partial sums round, so
+    # the summation order matters in the last bits. Whatever the order, an fp64
+    # sum of `group` terms with at most log2(group) + 1 roundings on any path
+    # lies within (log2(group) + 1) * 2^-53 * sum|r| of the exact sum; the
+    # scale is then one fp32 rounding of sum/group.
+    depth = int(np.log2(group)) + 1
+    for trial in range(200):
+        mag = RNG.uniform(1.0, 2.0, group) * 2.0 ** -RNG.integers(0, 46, group).astype(np.float64)
+        r = (mag * RNG.choice([-1.0, 1.0], group)).astype(np.float32)
+        _, scale = oracle.q1_encode(r, group)
+        total = sum(Fraction(float(abs(v))) for v in r)
+        exact = total / group
+        slack = Fraction(depth) * Fraction(2) ** -53 * total / group
+        lo = round_fraction_to_f32(exact - slack)
+        hi = round_fraction_to_f32(exact + slack)
+        assert lo <= scale[0] <= hi, trial
+
+
 def test_q1_scale_minimises_squared_error_for_fixed_signs():
     r = RNG.standard_normal(64 * 50).astype(np.float32)
     bits, scale = oracle.q1_encode(r, 64)
