@@ -348,10 +348,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "%s: %d bf16 tensors [%d x %d] per step, scheme %s" % (
             args.workload, *main_res["shape"], main_res["scheme"]),
+            "input_dtype": main_res["dtype"], "state_dtype": "f32",
             "steps_per_sequence": 28, "parallelism": "single GPU"},
         "roofline": roof,
         "hbm_reference_kernels_GBps": ceiling,
