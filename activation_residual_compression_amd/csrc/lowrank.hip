@@ -557,23 +557,26 @@ __global__ __launch_bounds__(256) void lr_dequant_kernel(const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------- reconstruct
-// c = Uq Vq^T with fp32 MFMA from the dequantised factors, streamed through the
-// state arrays. Each wave owns a 64-column strip and walks 16-row tiles of a
-// row chunk; the 4 waves of a block own 4 neighbouring strips of the same rows
-// (their U loads hit the same cache lines). Per wave:
-//   * once: the V operands of its strip (4 MFMA column tiles x K) in registers;
-//   * per tile: U operands of 16 rows, the lane's a_t / ahat, K MFMAs
-//     computing c^T = Vq Uq^T, then r = a - ahat, e = r - c, ahat += c
-//     (SENDER) or ahat += c (receiver); the next tile's loads are issued
-//     before the current tile's MFMAs.
-// MFMA step (j, i), j < K/16, i < 4, lane group g = l/16 covers contraction
+// c = Uq Vq^T with fp32 MFMA from the dequantised factors, applied to the state
+// arrays. A block owns 256 columns (four 64-column strips, one per wave) of a
+// chunk of rows and walks it in 16-row tiles:
+//   * once: each wave's V operands (4 MFMA column tiles x K) in registers;
+//   * per tile: each wave computes its 16 x 64 piece of c^T = Vq Uq^T with K
+//     MFMAs and writes it to an LDS tile (two buffers, one barrier per tile);
+//     then wave w applies rows 4w .. 4w+3 of the tile, each lane owning 4
+//     consecutive columns, so every global access of a wave is one contiguous
+//     1 KiB run: r = a - ahat, e = r - c, ahat += c (SENDER) or ahat += c.
+//     The next tile's U operands and state rows are loaded before the current
+//     tile's MFMAs.
+// MFMA step (j, i), j < K/16, i < 4: lane group g = l/16 covers contraction
 // index 16 j + 4 g + i, so both operands come from 16-byte loads of 4
-// consecutive factor columns. The MFMA M index is mapped to columns so that each
-// lane ends with 8 consecutive columns of one row in each 32-column half of the
-// strip. Sender and receiver run this same code on the same dequantised
-// factors, so both get the same c bit for bit. No LDS, no barriers.
-constexpr int kRcStrip = 64;     // columns per wave
-constexpr int kRcWaves = 4;      // strips per block
+// consecutive factor columns. The M index mi of column tile p is strip column
+// 32 (p/2) + 8 (mi/4) + 4 (p%2) + mi%4, so each lane's results are two runs of
+// 8 columns of one row. Sender and receiver run the same MFMA sequence on the
+// same dequantised factors, so both get the same c bit for bit. Strips and
+// lanes past m (m a multiple of 64 but not of 256) compute and store nothing.
+constexpr int kRcCols = 256;         // columns per block (4 waves x 64)
+constexpr int kRcLds = kRcCols + 4;  // LDS row stride, floats
 
 template <typename IN, bool SENDER, int K>
 __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
@@ -583,100 +586,106 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
                                                        const float* __restrict__ vd, int n, int m,
                                                        int chunk_rows) {
   constexpr int KJ = K / 16;
+  __shared__ float tile[2][16 * kRcLds];
   const int b = blockIdx.z;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
-  const int c0 = (blockIdx.x * kRcWaves + w) * kRcStrip;
-  if (c0 >= m) return;
+  const int cb = blockIdx.x * kRcCols;
+  const int c0 = cb + 64 * w;
+  const bool strip_ok = c0 < m;
+  const bool col_ok = cb + 4 * lane < m;
   const int rbeg = blockIdx.y * chunk_rows;
   const int rend = min(n, rbeg + chunk_rows);
-  // V operands: tile p covers strip columns 32 (p/2) + 8 (mi/4) + 4 (p%2) + mi%4
+
   f32x4 av[4][KJ];
   const float* vb = vd + (size_t)b * m * K;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const int col = c0 + 32 * (p >> 1) + 8 * (lr >> 2) + 4 * (p & 1) + (lr & 3);
+    const int col = (strip_ok ? c0 : 0) + 32 * (p >> 1) + 8 * (lr >> 2) + 4 * (p & 1) + (lr & 3);
 #pragma unroll
     for (int j = 0; j < KJ; ++j) av[p][j] = *reinterpret_cast<const f32x4*>(vb + (size_t)col * K + 16 * j + 4 * lk);
   }
   const float* ub = ud + (size_t)b * n * K;
-  struct Tile {
-    f32x4 bu[KJ];
-    F8 h[2], x[2];
+  const size_t tb = (size_t)b * n * m + (size_t)(col_ok ? cb + 4 * lane : 0);
+
+  struct Rows {
+    f32x4 u[KJ];  // U operands of the tile's 16 rows
+    f32x4 h[4];   // ahat of this wave's 4 rows, this lane's 4 columns
+    f32x4 x[4];   // a_t of the same (SENDER)
   };
-  auto load_tile = [&](int r0, Tile& T) {
-    const int row = r0 + lr;
-    const bool ok = row < rend;
-    const int rr = ok ? row : rbeg;
+  // Rows past the chunk reread its last row and are never stored.
+  auto load = [&](int r0, Rows& R) {
+    const int ru = min(r0 + lr, rend - 1);
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) T.bu[j] = *reinterpret_cast<const f32x4*>(ub + (size_t)rr * K + 16 * j + 4 * lk);
+    for (int j = 0; j < KJ; ++j) R.u[j] = *reinterpret_cast<const f32x4*>(ub + (size_t)ru * K + 16 * j + 4 * lk);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const size_t off = ((size_t)b * n + rr) * m + c0 + 32 * q + 8 * lk;
-      load8<float>(ahat + off, T.h[q]);
-      if constexpr (SENDER) load8<IN>(a + off, T.x[q]);
+    for (int i = 0; i < 4; ++i) {
+      const size_t off = tb + (size_t)min(r0 + 4 * w + i, rend - 1) * m;
+      R.h[i] = load4<float>(ahat + off);
+      if constexpr (SENDER) R.x[i] = load4<IN>(a + off);
     }
   };
-  // Tiles alternate between two register sets; every load is unconditional (rows
-  // past the chunk read row rbeg and are never stored), so the compiler can keep
-  // the next tile's loads in flight while the current one computes.
-  auto compute_store = [&](int r0, const Tile& T) {
+
+  Rows cur, nxt;
+  load(rbeg, cur);
+  int it = 0;
+  for (int r0 = rbeg; r0 < rend; r0 += 16, ++it) {
+    load(r0 + 16 < rend ? r0 + 16 : r0, nxt);
     f32x4 acc[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (strip_ok) {
 #pragma unroll
-    for (int j = 0; j < KJ; ++j)
+      for (int j = 0; j < KJ; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) acc[p] = mfma_f32(av[p][j][i], T.bu[j][i], acc[p]);
-    const int row = r0 + lr;
-    if (row >= rend) return;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const size_t off = ((size_t)b * n + row) * m + c0 + 32 * q + 8 * lk;
-      const f32x4 cl = acc[2 * q], chh = acc[2 * q + 1];
-      const float c[8] = {cl.x, cl.y, cl.z, cl.w, chh.x, chh.y, chh.z, chh.w};
-      F8 hv = T.h[q];
-      if constexpr (SENDER) {
-        F8 ev;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float r = T.x[q].v[i] - hv.v[i];
-          ev.v[i] = r - c[i];
-          hv.v[i] = hv.v[i] + c[i];
-        }
-        store8_nt(e + off, ev);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) hv.v[i] = hv.v[i] + c[i];
-      }
-      store8(ahat + off, hv);
+          for (int p = 0; p < 4; ++p) acc[p] = mfma_f32(av[p][j][i], cur.u[j][i], acc[p]);
     }
-  };
-  Tile t0, t1;
-  load_tile(rbeg, t0);
-  for (int r0 = rbeg; r0 < rend; r0 += 32) {
-    load_tile(r0 + 16, t1);
-    compute_store(r0, t0);
-    load_tile(r0 + 32, t0);
-    if (r0 + 16 < rend) compute_store(r0 + 16, t1);
+    float* T = tile[it & 1];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      *reinterpret_cast<f32x4*>(&T[lr * kRcLds + 64 * w + 32 * (p >> 1) + 8 * lk + 4 * (p & 1)]) = acc[p];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = r0 + 4 * w + i;
+      const f32x4 c = *reinterpret_cast<const f32x4*>(&T[(4 * w + i) * kRcLds + 4 * lane]);
+      if (row < rend && col_ok) {
+        const size_t off = tb + (size_t)row * m;
+        f32x4 hn;
+        if constexpr (SENDER) {
+          f32x4 ev;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float r = cur.x[i][t] - cur.h[i][t];
+            ev[t] = r - c[t];
+            hn[t] = cur.h[i][t] + c[t];
+          }
+          store4(e + off, ev);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) hn[t] = cur.h[i][t] + c[t];
+        }
+        store4(ahat + off, hn);
+      }
+    }
+    cur = nxt;
   }
 }
 
-// Grid of the reconstruct kernel: strips of 4 waves x row chunks x tensors,
-// with row chunks (multiples of 16 rows) sized for >= ~2048 blocks.
+// Grid of the reconstruct kernel: 256-column blocks x row chunks x tensors.
+// Short chunks keep the blocks that run together on neighbouring rows; the V
+// operands are loaded once per block, so chunks stay long enough (64 or 128
+// rows) to amortise them.
 struct RcGrid {
   dim3 grid;
   int chunk_rows;
 };
-inline RcGrid rc_grid(int n, int m, int B) {
-  const int sblocks = (m / kRcStrip + kRcWaves - 1) / kRcWaves;
-  int chunks = (3072 + sblocks * B - 1) / (sblocks * B);
-  const int tiles = (n + 15) / 16;
-  chunks = chunks < 1 ? 1 : (chunks > tiles ? tiles : chunks);
-  const int chunk_rows = ((tiles + chunks - 1) / chunks) * 16;
-  chunks = (n + chunk_rows - 1) / chunk_rows;
-  return RcGrid{dim3(sblocks, chunks, B), chunk_rows};
+inline RcGrid rc_grid(int n, int m, int B, int k) {
+  const int chunk_rows = k <= 32 ? 64 : 128;
+  return RcGrid{dim3((unsigned)((m + kRcCols - 1) / kRcCols), (unsigned)((n + chunk_rows - 1) / chunk_rows),
+                     (unsigned)B),
+                chunk_rows};
 }
 
 // ---------------------------------------------------------------- launchers
@@ -726,7 +735,7 @@ hipError_t lr_compress_k(bool bf16, const void* a, float* ahat, float* e, uint8_
   }
   hipLaunchKernelGGL((lr_int4_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, w.P, w.Qt,
                      w.amax, packed, w.ud, w.vd, L);
-  const RcGrid g = rc_grid(n, m, B);
+  const RcGrid g = rc_grid(n, m, B, K);
   if (bf16)
     hipLaunchKernelGGL((lr_recon_kernel<uint16_t, true, K>), g.grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(a), ahat, e, (const float*)w.ud,
@@ -744,7 +753,7 @@ hipError_t lr_decompress_k(const uint8_t* packed, float* ahat, int B, const Layo
   const int n = (int)L.rows, m = (int)L.cols;
   hipLaunchKernelGGL((lr_dequant_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, packed,
                      w.ud, w.vd, L);
-  const RcGrid g = rc_grid(n, m, B);
+  const RcGrid g = rc_grid(n, m, B, K);
   hipLaunchKernelGGL((lr_recon_kernel<float, false, K>), g.grid, dim3(256), 0, s,
                      (const float*)nullptr, ahat, (float*)nullptr, (const float*)w.ud,
                      (const float*)w.vd, n, m, g.chunk_rows);
