@@ -35,6 +35,8 @@
 // runs of memory.
 #include <float.h>
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -91,14 +93,22 @@ __device__ __forceinline__ u32x4 pack_r(const F8& x, const F8& h) {
 }
 
 // ---------------------------------------------------------------- P = R * Q
-// Block: 64 rows of one tensor (4 row fragments of 16); the 4 waves split the
-// 64-column K-steps (interleaved) and their products are summed through LDS
-// in a fixed order. In a K-step lane group g = l/16 owns columns
-// [64 ks + 16 g, +16): one 32-byte bf16 run that feeds two MFMAs (its first
-// and second 8 columns), so every row is read as whole 128-byte lines.
-// FROM_A: R is formed here from a_t and ahat and written out for later passes.
-// Block (0, b) clears the tensor's INT4 absmax slots, which the last solve and
-// the last Q sum of the iteration fill.
+// Block: 64 rows of one tensor, walked in steps of 128 columns. Each step's
+// 64 x 128 bf16 tile of R is staged in LDS: wave w loads rows 16w .. 16w+15,
+// 32 lanes per row with 4 consecutive columns each, so every wave-wide load
+// covers two contiguous row runs (256 B of R or a_t, 512 B of ahat). The next
+// step's rows are loaded while the current tile is multiplied. For the MFMAs
+// wave w takes the step's columns [32 w, +32) over all 64 rows: lane group
+// g = l/16 owns columns [8 g, +8) of that quarter, one 16-byte LDS read per
+// 16-row fragment, with the bf16 Q^T operand read the same way from global
+// memory (each B operand serves the 4 row fragments). The four waves' partial
+// tiles are summed through LDS as (w0 + w2) + (w1 + w3).
+// FROM_A: R = bf16(a_t - ahat) is formed while staging and written out for the
+// later passes. Block (0, b) clears the tensor's INT4 absmax slots, which the
+// last solve and the last Q sum of the iteration fill.
+constexpr int kRqStep = 128;        // columns per step
+constexpr int kRqLd = kRqStep + 8;  // bf16 per staged row (272 B)
+
 template <typename IN, bool FROM_A, int K>
 __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
                                                     const float* __restrict__ ahat,
@@ -109,12 +119,62 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
                                                     int ntiles) {
   constexpr int NT = K / 16;
   constexpr int LD = K + 1;
-  __shared__ float red[2][kTile * LD];
+  constexpr int kStageF = kTile * kRqLd / 2;  // floats spanned by the staged tile
+  constexpr int kRedF = 2 * kTile * LD;       // floats of the two reduction tiles
+  __shared__ __attribute__((aligned(16))) float lds[kStageF > kRedF ? kStageF : kRedF];
+  uint16_t* sR = reinterpret_cast<uint16_t*>(lds);
+  float* red0 = lds;
+  float* red1 = lds + kTile * LD;
   const int b = blockIdx.y, tile = blockIdx.x, row0 = tile * kTile;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
-  const int nks = m / 64;
   const uint16_t* Qb = Qtb + (size_t)b * K * m;
   if (tile == 0 && threadIdx.x < 2 * K) amax[(size_t)b * 2 * K + threadIdx.x] = 0u;
+
+  // staging: lane covers row 16w + 2i + (lane >> 5), columns 4 (lane & 31) .. +3
+  using Raw = typename std::conditional<std::is_same<IN, uint16_t>::value, u32x2, f32x4>::type;
+  struct Stage {
+    Raw x[8];
+    f32x4 h[8];  // FROM_A: a_t (as loaded) and ahat
+    u32x2 r[8];  // otherwise: R
+  };
+  const int srow = 16 * w + (lane >> 5), scol = 4 * (lane & 31);
+  // element offset of staged row i within the tensor (rows past n reread row n-1)
+  auto soff = [&](int c0, int i) -> size_t {
+    const int row = min(row0 + srow + 2 * i, n - 1);
+    return ((size_t)b * n + row) * m + (c0 + scol < m ? c0 + scol : 0);
+  };
+  auto gload = [&](int c0, Stage& S) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const size_t off = soff(c0, i);
+      if constexpr (FROM_A) {
+        S.x[i] = __builtin_nontemporal_load(reinterpret_cast<const Raw*>(a + off));
+        S.h[i] = load4<float>(ahat + off);
+      } else {
+        S.r[i] = *reinterpret_cast<const u32x2*>(R + off);
+      }
+    }
+  };
+  auto put = [&](int c0, const Stage& S) {
+    const bool col_ok = c0 + scol < m;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      u32x2 v;
+      if constexpr (FROM_A) {
+        f32x4 x;
+        if constexpr (std::is_same<IN, uint16_t>::value)
+          x = f32x4{bf16_lo(S.x[i].x), bf16_hi(S.x[i].x), bf16_lo(S.x[i].y), bf16_hi(S.x[i].y)};
+        else
+          x = S.x[i];
+        v.x = bf16_rne(x[0] - S.h[i][0]) | (bf16_rne(x[1] - S.h[i][1]) << 16);
+        v.y = bf16_rne(x[2] - S.h[i][2]) | (bf16_rne(x[3] - S.h[i][3]) << 16);
+        if (col_ok && row0 + srow + 2 * i < n) *reinterpret_cast<u32x2*>(R + soff(c0, i)) = v;
+      } else {
+        v = S.r[i];
+      }
+      *reinterpret_cast<u32x2*>(&sR[(srow + 2 * i) * kRqLd + scol]) = v;
+    }
+  };
 
   f32x4 acc[4][NT];
 #pragma unroll
@@ -122,45 +182,30 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
 #pragma unroll
     for (int g = 0; g < NT; ++g) acc[f][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int ks = w; ks < nks; ks += 4) {
-    const int c0 = ks * 64 + lk * 16;
-    u32x4 A0[4], A1[4];
+  Stage S;
+  gload(0, S);
+  for (int c0 = 0; c0 < m; c0 += kRqStep) {
+    __syncthreads();  // the previous tile has been read
+    put(c0, S);
+    __syncthreads();
+    if (c0 + kRqStep < m) gload(c0 + kRqStep, S);
+    const int kc = c0 + 32 * w;
+    if (kc < m) {
+      u32x4 B[NT];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int row = row0 + 16 * f + lr;
-      const int rcl = row < n ? row : n - 1;
-      const size_t off = ((size_t)b * n + rcl) * m + c0;
-      if constexpr (FROM_A) {
-        F8 x0, x1, h0, h1;
-        load8<IN>(a + off, x0);
-        load8<IN>(a + off + 8, x1);
-        load8<float>(ahat + off, h0);
-        load8<float>(ahat + off + 8, h1);
-        A0[f] = pack_r(x0, h0);
-        A1[f] = pack_r(x1, h1);
-        if (row < n) {
-          reinterpret_cast<u32x4*>(R + off)[0] = A0[f];
-          reinterpret_cast<u32x4*>(R + off)[1] = A1[f];
-        }
-      } else {
-        A0[f] = reinterpret_cast<const u32x4*>(R + off)[0];
-        A1[f] = reinterpret_cast<const u32x4*>(R + off)[1];
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < NT; ++g) {
-      const u32x4* q = reinterpret_cast<const u32x4*>(Qb + (size_t)(16 * g + lr) * m + c0);
-      const u32x4 B0 = q[0], B1 = q[1];
+      for (int g = 0; g < NT; ++g)
+        B[g] = *reinterpret_cast<const u32x4*>(Qb + (size_t)(16 * g + lr) * m + kc + 8 * lk);
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        acc[f][g] = mfma_bf16(A0[f], B0, acc[f][g]);
-        acc[f][g] = mfma_bf16(A1[f], B1, acc[f][g]);
+        const u32x4 A = *reinterpret_cast<const u32x4*>(&sR[(16 * f + lr) * kRqLd + 32 * w + 8 * lk]);
+#pragma unroll
+        for (int g = 0; g < NT; ++g) acc[f][g] = mfma_bf16(A, B[g], acc[f][g]);
       }
     }
   }
 
-  // (w0 + w2) + (w1 + w3), rows past n zeroed, tile kept in red[1]
-  auto put = [&](float* dst) {
+  // (w0 + w2) + (w1 + w3), rows past n zeroed, tile kept in red1
+  auto store_acc = [&](float* dst) {
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
@@ -168,7 +213,7 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
 #pragma unroll
         for (int t = 0; t < 4; ++t) dst[(16 * f + 4 * lk + t) * LD + 16 * g + lr] = acc[f][g][t];
   };
-  auto add = [&](const float* src) {
+  auto add_acc = [&](const float* src) {
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
@@ -176,14 +221,15 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[f][g][t] += src[(16 * f + 4 * lk + t) * LD + 16 * g + lr];
   };
-  if (w >= 2) put(red[w - 2]);
+  __syncthreads();  // the staged tile is no longer needed
+  if (w >= 2) store_acc(w == 2 ? red0 : red1);
   __syncthreads();
-  if (w < 2) add(red[w]);
+  if (w < 2) add_acc(w == 0 ? red0 : red1);
   __syncthreads();
-  if (w == 1) put(red[0]);
+  if (w == 1) store_acc(red0);
   __syncthreads();
   if (w == 0) {
-    add(red[0]);
+    add_acc(red0);
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
@@ -191,10 +237,10 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
         if (row0 + 16 * f + 4 * lk + t >= n)
 #pragma unroll
           for (int g = 0; g < NT; ++g) acc[f][g][t] = 0.f;
-    put(red[1]);
+    store_acc(red1);
   }
   __syncthreads();
-  const float* T = red[1];
+  const float* T = red1;
   for (int idx = threadIdx.x; idx < kTile * K; idx += blockDim.x) {
     const int r = idx / K, j = idx % K;
     if (row0 + r < n) P[((size_t)b * n + row0 + r) * K + j] = T[r * LD + j];
