@@ -17,17 +17,25 @@ struct Layout {
   int nsec = 0;
 };
 
+// Receivers decoded by one decompress launch: peer p applies packed[p] to
+// state[p] (both [batch] tensors); the launch grid's z index is the peer.
+constexpr int kMaxPeers = 8;
+struct PeerSet {
+  const uint8_t* packed[kMaxPeers];
+  float* state[kMaxPeers];
+  int count;
+};
+
 // Q1 (bits = 1) and Q2 (bits = 2) group quantisation, group in {32, 64, 128}.
 hipError_t launch_q_compress(int bits, int group, bool bf16_input, const void* a, float* ahat,
                              float* e, uint8_t* packed, int batch, const Layout& L, hipStream_t s);
-hipError_t launch_q_decompress(int bits, int group, const uint8_t* packed, float* ahat, int batch,
+hipError_t launch_q_decompress(int bits, int group, const PeerSet& peers, int batch,
                                const Layout& L, hipStream_t s);
 
 // 2:16 block sparsifier.
 hipError_t launch_nm_compress(bool bf16_input, const void* a, float* ahat, float* e,
                               uint8_t* packed, int batch, const Layout& L, hipStream_t s);
-hipError_t launch_nm_decompress(const uint8_t* packed, float* ahat, int batch, const Layout& L,
-                                hipStream_t s);
+hipError_t launch_nm_decompress(const PeerSet& peers, int batch, const Layout& L, hipStream_t s);
 
 // Low-rank workspace, carved out of one device allocation by the plan.
 // ntiles = ceil(rows / 64); rows_pad = 64 * ntiles; the R^T P product splits

@@ -160,9 +160,10 @@ __global__ __launch_bounds__(kNmBlock) void nm_compress_kernel(const IN* __restr
 }
 
 template <int NC>
-__global__ __launch_bounds__(kNmBlock) void nm_decompress_kernel(const uint8_t* __restrict__ packed,
-                                                                 float* __restrict__ ahat, Layout L) {
+__global__ __launch_bounds__(kNmBlock) void nm_decompress_kernel(PeerSet peers, Layout L) {
   const int b = blockIdx.y;
+  const uint8_t* __restrict__ packed = peers.packed[blockIdx.z];
+  float* __restrict__ ahat = peers.state[blockIdx.z];
   const int64_t n4 = L.n / 4;
   const int64_t base = (int64_t)b * L.n;
   const uint8_t* pk = packed + (int64_t)b * L.tstride;
@@ -213,11 +214,11 @@ hipError_t launch_nm_compress(bool bf16_input, const void* a, float* ahat, float
   return hipGetLastError();
 }
 
-hipError_t launch_nm_decompress(const uint8_t* packed, float* ahat, int batch, const Layout& L,
-                                hipStream_t s) {
+hipError_t launch_nm_decompress(const PeerSet& peers, int batch, const Layout& L, hipStream_t s) {
   const int64_t n4 = L.n / 4;
-  const dim3 grid((unsigned)((n4 + kNmBlock * kNmDecChunks - 1) / (kNmBlock * kNmDecChunks)), (unsigned)batch);
-  hipLaunchKernelGGL((nm_decompress_kernel<kNmDecChunks>), grid, dim3(kNmBlock), 0, s, packed, ahat, L);
+  const dim3 grid((unsigned)((n4 + kNmBlock * kNmDecChunks - 1) / (kNmBlock * kNmDecChunks)), (unsigned)batch,
+                  (unsigned)peers.count);
+  hipLaunchKernelGGL((nm_decompress_kernel<kNmDecChunks>), grid, dim3(kNmBlock), 0, s, peers, L);
   return hipGetLastError();
 }
 

@@ -23,6 +23,9 @@ struct rc_plan {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   rc::LowRankWork lr;
+  // chunk-done events of rc_compress_send, created on first use on ev_device
+  std::vector<hipEvent_t> events;
+  int ev_device = 0;
 };
 
 namespace {
@@ -156,6 +159,77 @@ rc_status_t setup_lowrank(rc_plan* pl, const float* q0) {
   return RC_OK;
 }
 
+// The low-rank workspace seen from tensor b0 on (every piece is per tensor).
+rc::LowRankWork lr_slice(const rc::LowRankWork& w, const rc::Layout& L, int64_t b0) {
+  const int64_t n = L.rows, m = L.cols, k = w.rank;
+  rc::LowRankWork s = w;
+  s.R += b0 * n * m;
+  s.P += b0 * n * k;
+  s.Pbt += b0 * k * w.rows_pad;
+  s.Qt += b0 * k * m;
+  s.Q0t += b0 * k * m;
+  s.Qtb += b0 * k * m;
+  s.gpart += b0 * w.ntiles * k * k;
+  s.gsum += b0 * k * k;
+  s.linv += b0 * k * k;
+  s.qpart += b0 * w.nsplit * k * m;
+  s.amax += b0 * 2 * k;
+  s.ud += b0 * n * k;
+  s.vd += b0 * m * k;
+  return s;
+}
+
+// Sender step on tensors [b0, b0 + nb) of the batch.
+hipError_t compress_range(rc_plan* pl, hipStream_t stream, const void* a_t, const rc_state_t* st,
+                          uint8_t* packed, int b0, int nb) {
+  const int64_t N = pl->layout.n;
+  const bool bf16 = pl->dtype == RC_BF16;
+  const void* a = static_cast<const char*>(a_t) + (size_t)b0 * N * (bf16 ? 2 : 4);
+  float* ahat = st->ahat + (size_t)b0 * N;
+  float* e = st->e + (size_t)b0 * N;
+  uint8_t* pk = packed + (size_t)b0 * pl->layout.tstride;
+  switch (pl->scheme) {
+    case RC_Q1:
+    case RC_Q2:
+      return rc::launch_q_compress(pl->scheme == RC_Q1 ? 1 : 2, pl->params.group, bf16, a, ahat, e,
+                                   pk, nb, pl->layout, stream);
+    case RC_NM:
+      return rc::launch_nm_compress(bf16, a, ahat, e, pk, nb, pl->layout, stream);
+    case RC_LOWRANK:
+      return rc::launch_lr_compress(bf16, a, ahat, e, pk, nb, pl->layout,
+                                    b0 ? lr_slice(pl->lr, pl->layout, b0) : pl->lr, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Receiver step for up to kMaxPeers states.
+hipError_t decompress_peers(rc_plan* pl, hipStream_t stream, const uint8_t* const* packed,
+                            float* const* states, int npeers) {
+  rc::PeerSet ps{};
+  ps.count = npeers;
+  for (int p = 0; p < npeers; ++p) {
+    ps.packed[p] = packed[p];
+    ps.state[p] = states[p];
+  }
+  switch (pl->scheme) {
+    case RC_Q1:
+    case RC_Q2:
+      return rc::launch_q_decompress(pl->scheme == RC_Q1 ? 1 : 2, pl->params.group, ps,
+                                     pl->shape.batch, pl->layout, stream);
+    case RC_NM:
+      return rc::launch_nm_decompress(ps, pl->shape.batch, pl->layout, stream);
+    case RC_LOWRANK:
+      // the dequantised factors live in the plan's workspace: one peer at a time
+      for (int p = 0; p < npeers; ++p) {
+        const hipError_t err = rc::launch_lr_decompress(packed[p], states[p], pl->shape.batch,
+                                                        pl->layout, pl->lr, stream);
+        if (err != hipSuccess) return err;
+      }
+      return hipSuccess;
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 extern "C" {
@@ -189,25 +263,39 @@ rc_status_t rc_compress(rc_plan_t pl, hipStream_t stream, const void* a_t, const
   if (!pl || !a_t || !state || !state->ahat || !state->e || !packed_out) return RC_ERR_INVALID_ARG;
   if (!aligned16(a_t) || !aligned16(state->ahat) || !aligned16(state->e) || !aligned16(packed_out))
     return RC_ERR_ALIGNMENT;
-  const bool bf16 = pl->dtype == RC_BF16;
-  uint8_t* packed = static_cast<uint8_t*>(packed_out);
-  hipError_t err = hipSuccess;
-  switch (pl->scheme) {
-    case RC_Q1:
-    case RC_Q2:
-      err = rc::launch_q_compress(pl->scheme == RC_Q1 ? 1 : 2, pl->params.group, bf16, a_t,
-                                  state->ahat, state->e, packed, pl->shape.batch, pl->layout, stream);
-      break;
-    case RC_NM:
-      err = rc::launch_nm_compress(bf16, a_t, state->ahat, state->e, packed, pl->shape.batch,
-                                   pl->layout, stream);
-      break;
-    case RC_LOWRANK:
-      err = rc::launch_lr_compress(bf16, a_t, state->ahat, state->e, packed, pl->shape.batch,
-                                   pl->layout, pl->lr, stream);
-      break;
-  }
+  const hipError_t err = compress_range(pl, stream, a_t, state, static_cast<uint8_t*>(packed_out), 0,
+                                        pl->shape.batch);
   return err == hipSuccess ? RC_OK : RC_ERR_HIP;
+}
+
+rc_status_t rc_compress_send(rc_plan_t pl, hipStream_t stream, hipStream_t copy_stream,
+                             const void* a_t, const rc_state_t* state, void* packed_out,
+                             void* packed_dst, int chunk) {
+  if (!pl || !a_t || !state || !state->ahat || !state->e || !packed_out || !packed_dst || chunk < 1)
+    return RC_ERR_INVALID_ARG;
+  if (!aligned16(a_t) || !aligned16(state->ahat) || !aligned16(state->e) || !aligned16(packed_out))
+    return RC_ERR_ALIGNMENT;
+  const int B = pl->shape.batch;
+  const int nchunks = (B + chunk - 1) / chunk;
+  if (pl->events.empty() && hipGetDevice(&pl->ev_device) != hipSuccess) return RC_ERR_HIP;
+  while ((int)pl->events.size() < nchunks) {
+    hipEvent_t ev;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return RC_ERR_HIP;
+    pl->events.push_back(ev);
+  }
+  uint8_t* src = static_cast<uint8_t*>(packed_out);
+  uint8_t* dst = static_cast<uint8_t*>(packed_dst);
+  const size_t ts = (size_t)pl->layout.tstride;
+  for (int c = 0; c < nchunks; ++c) {
+    const int b0 = c * chunk, nb = (B - b0 < chunk) ? B - b0 : chunk;
+    if (compress_range(pl, stream, a_t, state, src, b0, nb) != hipSuccess) return RC_ERR_HIP;
+    if (hipEventRecord(pl->events[c], stream) != hipSuccess) return RC_ERR_HIP;
+    if (hipStreamWaitEvent(copy_stream, pl->events[c], 0) != hipSuccess) return RC_ERR_HIP;
+    if (hipMemcpyAsync(dst + b0 * ts, src + b0 * ts, nb * ts, hipMemcpyDefault, copy_stream) !=
+        hipSuccess)
+      return RC_ERR_HIP;
+  }
+  return RC_OK;
 }
 
 rc_status_t rc_decompress(rc_plan_t pl, hipStream_t stream, const void* packed_in,
@@ -215,33 +303,40 @@ rc_status_t rc_decompress(rc_plan_t pl, hipStream_t stream, const void* packed_i
   if (!pl || !packed_in || !recon_state) return RC_ERR_INVALID_ARG;
   if (!aligned16(packed_in) || !aligned16(recon_state)) return RC_ERR_ALIGNMENT;
   const uint8_t* packed = static_cast<const uint8_t*>(packed_in);
-  hipError_t err = hipSuccess;
-  switch (pl->scheme) {
-    case RC_Q1:
-    case RC_Q2:
-      err = rc::launch_q_decompress(pl->scheme == RC_Q1 ? 1 : 2, pl->params.group, packed,
-                                    recon_state, pl->shape.batch, pl->layout, stream);
-      break;
-    case RC_NM:
-      err = rc::launch_nm_decompress(packed, recon_state, pl->shape.batch, pl->layout, stream);
-      break;
-    case RC_LOWRANK:
-      err = rc::launch_lr_decompress(packed, recon_state, pl->shape.batch, pl->layout, pl->lr,
-                                     stream);
-      break;
+  const hipError_t err = decompress_peers(pl, stream, &packed, &recon_state, 1);
+  return err == hipSuccess ? RC_OK : RC_ERR_HIP;
+}
+
+rc_status_t rc_decompress_many(rc_plan_t pl, hipStream_t stream, const void* const* packed_in,
+                               float* const* recon_states, int npeers) {
+  if (!pl || !packed_in || !recon_states || npeers < 1 || npeers > RC_MAX_PEERS)
+    return RC_ERR_INVALID_ARG;
+  const uint8_t* packed[RC_MAX_PEERS];
+  for (int p = 0; p < npeers; ++p) {
+    if (!packed_in[p] || !recon_states[p]) return RC_ERR_INVALID_ARG;
+    if (!aligned16(packed_in[p]) || !aligned16(recon_states[p])) return RC_ERR_ALIGNMENT;
+    packed[p] = static_cast<const uint8_t*>(packed_in[p]);
   }
+  const hipError_t err = decompress_peers(pl, stream, packed, recon_states, npeers);
   return err == hipSuccess ? RC_OK : RC_ERR_HIP;
 }
 
 rc_status_t rc_plan_destroy(rc_plan_t pl) {
   if (!pl) return RC_OK;
   rc_status_t st = RC_OK;
-  if (pl->ws) {
+  if (pl->ws || !pl->events.empty()) {
     int cur = 0;
     if (hipGetDevice(&cur) != hipSuccess) st = RC_ERR_HIP;
-    if (cur != pl->device && hipSetDevice(pl->device) != hipSuccess) st = RC_ERR_HIP;
-    if (hipFree(pl->ws) != hipSuccess) st = RC_ERR_HIP;
-    if (cur != pl->device) (void)hipSetDevice(cur);
+    if (!pl->events.empty()) {
+      if (cur != pl->ev_device && hipSetDevice(pl->ev_device) != hipSuccess) st = RC_ERR_HIP;
+      for (hipEvent_t ev : pl->events)
+        if (hipEventDestroy(ev) != hipSuccess) st = RC_ERR_HIP;
+    }
+    if (pl->ws) {
+      if (hipSetDevice(pl->device) != hipSuccess) st = RC_ERR_HIP;
+      if (hipFree(pl->ws) != hipSuccess) st = RC_ERR_HIP;
+    }
+    (void)hipSetDevice(cur);
   }
   delete pl;
   return st;

@@ -131,10 +131,11 @@ __global__ __launch_bounds__(kBlock) void q_compress_kernel(const IN* __restrict
 }
 
 template <int G, int BITS, int NC>
-__global__ __launch_bounds__(kBlock) void q_decompress_kernel(const uint8_t* __restrict__ packed,
-                                                              float* __restrict__ ahat, Layout L) {
+__global__ __launch_bounds__(kBlock) void q_decompress_kernel(PeerSet peers, Layout L) {
   constexpr int LANES = G / 4;
   const int b = blockIdx.y;
+  const uint8_t* __restrict__ packed = peers.packed[blockIdx.z];
+  float* __restrict__ ahat = peers.state[blockIdx.z];
   const int64_t n4 = L.n / 4;
   const int64_t base = (int64_t)b * L.n;
   const uint8_t* pk = packed + (int64_t)b * L.tstride;
@@ -182,11 +183,11 @@ hipError_t q_compress_t(const void* a, float* ahat, float* e, uint8_t* packed, i
 }
 
 template <int G, int BITS>
-hipError_t q_decompress_t(const uint8_t* packed, float* ahat, int batch, const Layout& L,
-                          hipStream_t s) {
+hipError_t q_decompress_t(const PeerSet& peers, int batch, const Layout& L, hipStream_t s) {
   const int64_t n4 = L.n / 4;
-  const dim3 grid((unsigned)((n4 + kBlock * kDecChunks - 1) / (kBlock * kDecChunks)), (unsigned)batch);
-  hipLaunchKernelGGL((q_decompress_kernel<G, BITS, kDecChunks>), grid, dim3(kBlock), 0, s, packed, ahat, L);
+  const dim3 grid((unsigned)((n4 + kBlock * kDecChunks - 1) / (kBlock * kDecChunks)), (unsigned)batch,
+                  (unsigned)peers.count);
+  hipLaunchKernelGGL((q_decompress_kernel<G, BITS, kDecChunks>), grid, dim3(kBlock), 0, s, peers, L);
   return hipGetLastError();
 }
 
@@ -205,12 +206,12 @@ hipError_t q_compress_g(int group, bool bf16, const void* a, float* ahat, float*
 }
 
 template <int BITS>
-hipError_t q_decompress_g(int group, const uint8_t* p, float* ahat, int batch, const Layout& L,
+hipError_t q_decompress_g(int group, const PeerSet& peers, int batch, const Layout& L,
                           hipStream_t s) {
   switch (group) {
-    case 32: return q_decompress_t<32, BITS>(p, ahat, batch, L, s);
-    case 64: return q_decompress_t<64, BITS>(p, ahat, batch, L, s);
-    case 128: return q_decompress_t<128, BITS>(p, ahat, batch, L, s);
+    case 32: return q_decompress_t<32, BITS>(peers, batch, L, s);
+    case 64: return q_decompress_t<64, BITS>(peers, batch, L, s);
+    case 128: return q_decompress_t<128, BITS>(peers, batch, L, s);
   }
   return hipErrorInvalidValue;
 }
@@ -222,10 +223,10 @@ hipError_t launch_q_compress(int bits, int group, bool bf16_input, const void* a
                    : q_compress_g<2>(group, bf16_input, a, ahat, e, packed, batch, L, s);
 }
 
-hipError_t launch_q_decompress(int bits, int group, const uint8_t* packed, float* ahat, int batch,
+hipError_t launch_q_decompress(int bits, int group, const PeerSet& peers, int batch,
                                const Layout& L, hipStream_t s) {
-  return bits == 1 ? q_decompress_g<1>(group, packed, ahat, batch, L, s)
-                   : q_decompress_g<2>(group, packed, ahat, batch, L, s);
+  return bits == 1 ? q_decompress_g<1>(group, peers, batch, L, s)
+                   : q_decompress_g<2>(group, peers, batch, L, s);
 }
 
 }  // namespace rc

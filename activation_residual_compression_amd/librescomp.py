@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "librescomp.so")
 RC_OK, RC_ERR_INVALID_ARG, RC_ERR_UNSUPPORTED, RC_ERR_ALIGNMENT, RC_ERR_HIP = 0, 1, 2, 3, 4
 RC_BF16, RC_F32 = 0, 1
 RC_Q1, RC_Q2, RC_NM, RC_LOWRANK = 0, 1, 2, 3
+RC_MAX_PEERS = 8
 
 SCHEMES = {"q1": RC_Q1, "q2": RC_Q2, "nm": RC_NM, "lr": RC_LOWRANK}
 DTYPES = {"bf16": RC_BF16, "f32": RC_F32}
@@ -62,6 +63,10 @@ def _load():
     lib.rc_compress.argtypes = [vp, vp, vp, ctypes.POINTER(rc_state_t), vp]
     lib.rc_decompress.restype = st
     lib.rc_decompress.argtypes = [vp, vp, vp, vp]
+    lib.rc_compress_send.restype = st
+    lib.rc_compress_send.argtypes = [vp, vp, vp, vp, ctypes.POINTER(rc_state_t), vp, vp, ctypes.c_int]
+    lib.rc_decompress_many.restype = st
+    lib.rc_decompress_many.argtypes = [vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int]
     lib.rc_plan_destroy.restype = st
     lib.rc_plan_destroy.argtypes = [vp]
     for f in ("rc_packed_bytes", "rc_tensor_packed_bytes", "rc_workspace_bytes"):
@@ -133,6 +138,23 @@ def rc_decompress(plan, stream, packed_in, recon_state):
            "rc_decompress")
 
 
+def rc_compress_send(plan, stream, copy_stream, a_t, state: rc_state_t, packed_out, packed_dst,
+                     chunk):
+    _check(_lib.rc_compress_send(plan, _stream(stream), _stream(copy_stream), _ptr(a_t),
+                                 ctypes.byref(state), _ptr(packed_out), _ptr(packed_dst), int(chunk)),
+           "rc_compress_send")
+
+
+def rc_decompress_many(plan, stream, packed_in, recon_states):
+    """packed_in, recon_states: equal-length sequences (one entry per peer)."""
+    n = len(packed_in)
+    if n != len(recon_states):
+        raise ValueError("one recon state per packed stream")
+    pk = (ctypes.c_void_p * max(n, 1))(*[_ptr(x) for x in packed_in])
+    rs = (ctypes.c_void_p * max(n, 1))(*[_ptr(x) for x in recon_states])
+    _check(_lib.rc_decompress_many(plan, _stream(stream), pk, rs, n), "rc_decompress_many")
+
+
 def rc_plan_destroy(plan):
     _check(_lib.rc_plan_destroy(plan), "rc_plan_destroy")
 
@@ -193,6 +215,13 @@ class Plan:
 
     def decompress(self, packed_in, recon_state, stream=None):
         rc_decompress(self.handle, stream, packed_in, recon_state)
+
+    def compress_send(self, a_t, ahat, e, packed_out, packed_dst, chunk, copy_stream, stream=None):
+        st = rc_state_t(_ptr(ahat), _ptr(e))
+        rc_compress_send(self.handle, stream, copy_stream, a_t, st, packed_out, packed_dst, chunk)
+
+    def decompress_many(self, packed_in, recon_states, stream=None):
+        rc_decompress_many(self.handle, stream, packed_in, recon_states)
 
     def lowrank_workspace(self):
         """Device pointers (R, P, Pbt, Qt, Q0t, Qtb, gpart, chol) and rows_pad (diagnostics)."""

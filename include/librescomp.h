@@ -102,10 +102,40 @@ rc_status_t rc_plan_create(rc_shape_t shape, rc_dtype_t dtype, rc_scheme_t schem
 rc_status_t rc_compress(rc_plan_t plan, hipStream_t stream, const void* a_t, const rc_state_t* state,
                         void* packed_out);
 
+/* Sender step with the packed stream handed off chunk by chunk (Key designs /
+ * System co-design: compression overlapped with communication). The batch is
+ * compressed in chunks of `chunk` tensors on `stream`, with exactly the results
+ * of rc_compress; as soon as a chunk's packed bytes are written, a copy of them
+ * into the same place of `packed_dst` is queued on `copy_stream`
+ * (hipMemcpyAsync, any destination the HIP runtime can copy to: a peer's
+ * receive buffer, another device buffer, pinned host memory), so the copy of
+ * chunk i runs while chunk i+1 is compressed. On return all copies are queued;
+ * nothing waits for them. The caller must let copy_stream pass this call's
+ * copies before packed_out is written again (e.g. alternate two packed_out
+ * buffers, or make the next writer wait on an event recorded on copy_stream),
+ * and before packed_dst is read. chunk >= 1 (chunk >= batch: one chunk).
+ * The plan keeps one event per chunk, created on the first call on the
+ * current device. */
+rc_status_t rc_compress_send(rc_plan_t plan, hipStream_t stream, hipStream_t copy_stream,
+                             const void* a_t, const rc_state_t* state, void* packed_out,
+                             void* packed_dst, int chunk);
+
 /* Receiver step (Overall framework): recon_state += decode(packed_in) for every
  * tensor. recon_state: fp32 [batch][rows][cols], updated in place. */
 rc_status_t rc_decompress(rc_plan_t plan, hipStream_t stream, const void* packed_in,
                           float* recon_state);
+
+/* Receiver step for several senders at once (a sequence-parallel receiver gets
+ * one packed stream from each peer, Overall framework): recon_states[p] +=
+ * decode(packed_in[p]) for p < npeers, 1 <= npeers <= RC_MAX_PEERS, each state
+ * fp32 [batch][rows][cols] and each stream rc_packed_bytes(plan) bytes laid out
+ * by this plan. The results equal npeers calls of rc_decompress. Q1, Q2 and NM
+ * decode all peers in one launch; RC_LOWRANK decodes them one after another
+ * (its dequantised factors live in the plan's workspace). The states must not
+ * overlap. */
+#define RC_MAX_PEERS 8
+rc_status_t rc_decompress_many(rc_plan_t plan, hipStream_t stream, const void* const* packed_in,
+                               float* const* recon_states, int npeers);
 
 /* Free the plan and its workspace. Waits for nothing: the caller must make sure
  * no launched work still uses the plan. NULL is accepted. */

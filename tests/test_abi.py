@@ -116,3 +116,22 @@ def test_compress_rejects_bad_pointers_without_launching(rc):
         assert ei.value.status == rc.RC_ERR_INVALID_ARG
     assert rc.rc_packed_bytes(None) == 0 and rc.rc_workspace_bytes(None) == 0
     rc.rc_plan_destroy(None)
+
+
+def test_send_and_many_reject_bad_arguments_without_launching(rc):
+    with rc.Plan((2, 8, 64), "f32", "q2", group=64) as p:
+        st = rc.rc_state_t(4096, 8192)
+        for chunk, dst, a, status in ((0, 4096, 4096, rc.RC_ERR_INVALID_ARG),
+                                      (1, 0, 4096, rc.RC_ERR_INVALID_ARG),
+                                      (1, 4096, 4100, rc.RC_ERR_ALIGNMENT)):
+            with pytest.raises(rc.RcError) as ei:
+                rc.rc_compress_send(p.handle, 0, 0, a, st, 4096, dst, chunk)
+            assert ei.value.status == status
+        for packed, states, status in (([], [], rc.RC_ERR_INVALID_ARG),
+                                       ([4096] * 9, [4096] * 9, rc.RC_ERR_INVALID_ARG),
+                                       ([4096, 0], [4096, 8192], rc.RC_ERR_INVALID_ARG),
+                                       ([4096, 4104], [4096, 8192], rc.RC_ERR_ALIGNMENT)):
+            with pytest.raises(rc.RcError) as ei:
+                rc.rc_decompress_many(p.handle, 0, packed, states)
+            assert ei.value.status == status
+    assert rc.RC_MAX_PEERS == 8
