@@ -129,7 +129,64 @@ def _probe_on(kind, a, b, c, n, reps=5):
     return e0.elapsed_time(e1) / reps
 
 
-def measure(config, steps, warmup, max_frames, log):
+def exchange_timing(plan, seq, ahat, e, packed, chunks, reps=5):
+    """Sender step plus hand-off of the packed stream (rc_compress_send): compress
+    alone, copy alone, both in sequence, and the chunked pipeline, to a device
+    buffer (stand-in for a peer's receive buffer) and to pinned host memory (a
+    PCIe link). Times are averages over `reps` calls, from an event on the
+    compute stream before the call to an event on the copy stream after it."""
+    import torch
+    stream = torch.cuda.current_stream()
+    cs = torch.cuda.Stream()
+    dsts = {"device": torch.empty_like(packed),
+            "host": torch.empty(packed.numel(), dtype=torch.uint8, pin_memory=True)}
+    out = {}
+
+    def timed(fn):
+        fn(0)
+        torch.cuda.synchronize()
+        t = []
+        for i in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            cs.wait_event(e0)
+            fn(i + 1)
+            e1.record(cs)
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return sum(t) / len(t)
+
+    def compress(i):
+        plan.compress(seq[i % len(seq)], ahat, e, packed, stream)
+        cs.wait_stream(stream)
+
+    t_c = timed(compress)
+    out["compress_ms"] = t_c
+    for name, dst in dsts.items():
+        def copy(i, dst=dst):
+            with torch.cuda.stream(cs):
+                dst.copy_(packed, non_blocking=True)
+
+        def serial(i, dst=dst):
+            plan.compress(seq[i % len(seq)], ahat, e, packed, stream)
+            cs.wait_stream(stream)
+            with torch.cuda.stream(cs):
+                dst.copy_(packed, non_blocking=True)
+
+        t_x, t_s = timed(copy), timed(serial)
+        r = dict(copy_ms=t_x, serial_ms=t_s, copy_GBps=packed.numel() / (t_x * 1e6))
+        for ch in chunks:
+            def pipe(i, dst=dst, ch=ch):
+                plan.compress_send(seq[i % len(seq)], ahat, e, packed, dst, ch, cs, stream)
+            t_p = timed(pipe)
+            r["pipeline_chunk%d_ms" % ch] = t_p
+            # share of the shorter phase hidden by the pipeline (< 0: chunking costs more)
+            r["hidden_frac_chunk%d" % ch] = (t_s - t_p) / min(t_c, t_x)
+        out[name] = r
+    return out
+
+
+def measure(config, steps, warmup, max_frames, log, exchange_chunks=()):
     import numpy as np
     import torch
 
@@ -199,6 +256,9 @@ def measure(config, steps, warmup, max_frames, log):
         out["tensors_per_ms"] = B / ms_step
         out["mfma_flops"] = fl
         out["mfma_util_whole_compress"] = fl / (c_ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if exchange_chunks:
+        out["exchange"] = exchange_timing(plan, seq, ahat, e, packed, exchange_chunks)
+        log("[bench] %s exchange: %s" % (config, json.dumps(out["exchange"])))
     # reference kernels on these very buffers, after the timed region (the state is
     # no longer needed): the HBM ceiling of the sender and receiver access patterns
     if wl.dtype == "bf16" and N % 8 == 0:
@@ -267,6 +327,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-probe", action="store_true")
+    ap.add_argument("--no-exchange", action="store_true",
+                    help="skip the compress + hand-off pipeline timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -302,13 +364,15 @@ def main():
     from activation_residual_compression_amd import synth as _synth
     _wl = _synth.make(args.workload, tensors=[0])
     ceiling = None if args.no_hbm_probe else hbm_probe(_wl.batch * _wl.n * _wl.m, log)
-    main_res = measure(args.workload, args.steps, args.warmup, 64, log)
+    main_res = measure(args.workload, args.steps, args.warmup, 64, log,
+                       exchange_chunks=() if args.no_exchange else (4, 8, 19))
     log("[bench] %s: %.3f ms/step, %.1f GB/s input, compress %.3f ms (%.0f GB/s alg)" % (
         args.workload, main_res["ms_per_step"], main_res["input_GBps"], main_res["compress_ms"],
         main_res["compress_GBps"]))
     others = {}
     for cfg in [c for c in args.also.split(",") if c and c != args.workload]:
-        r = measure(cfg, args.steps, args.warmup, args.also_frames, log)
+        r = measure(cfg, args.steps, args.warmup, args.also_frames, log,
+                    exchange_chunks=(8, 19) if (cfg == "flux_lr" and not args.no_exchange) else ())
         log("[bench] %s: %.3f ms/step, %.1f GB/s input" % (cfg, r["ms_per_step"], r["input_GBps"]))
         others[cfg] = r
 
