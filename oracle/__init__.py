@@ -212,6 +212,23 @@ def lr_decode(qu, qv, su, sv):
     return c
 
 
+def lr_encode_bf16(r, q0, rank, iters):
+    """Low-rank factors sent as bf16 instead of INT4 (the factor-precision
+    alternative of the Low-rank strategy section: fewer, finer factors against
+    more, coarser ones). U, V are the same subspace-iteration factors as in
+    lr_encode; each element is rounded to fp32 and then to bf16 (RNE).
+    Returns (ub, vb, ndead): bf16 bit patterns [n, rank], [m, rank]."""
+    U, V, nd = lr_factors(r, q0, rank, iters)
+    return bf16_bits(U.astype(np.float32)), bf16_bits(V.astype(np.float32)), nd
+
+
+def lr_decode_bf16(ub, vb):
+    """c = Ub Vb^T in fp64 from bf16 factor bit patterns."""
+    U = bf16_value(np.asarray(ub, np.uint16)).astype(np.float64)
+    V = bf16_value(np.asarray(vb, np.uint16)).astype(np.float64)
+    return U @ V.T
+
+
 def lr_factors(r, q0, rank, iters):
     """Unquantised factors (U [n,k], V [m,k]) of the subspace iteration."""
     r = _f32(r)
@@ -231,6 +248,7 @@ def lr_factors(r, q0, rank, iters):
 #   lr: U nibbles [n*k/2] | V nibbles [m*k/2] | s_U f32 [k] | s_V f32 [k]
 #       nibble t of a row-major [rows x k] INT4 matrix = element t; even t in
 #       the low nibble; two's complement.
+#   lr with bf16 factors: U bf16 [n*k] | V bf16 [m*k], row-major.
 ALIGN = 256
 
 
@@ -238,8 +256,10 @@ def _al(x):
     return (x + ALIGN - 1) // ALIGN * ALIGN
 
 
-def section_sizes(scheme, n, m, group=None, rank=None):
+def section_sizes(scheme, n, m, group=None, rank=None, factors="int4"):
     N = n * m
+    if scheme == "lr" and factors == "bf16":
+        return [2 * n * rank, 2 * m * rank]
     if scheme == "q1":
         return [N // 8, 4 * (N // group)]
     if scheme == "q2":
@@ -251,14 +271,14 @@ def section_sizes(scheme, n, m, group=None, rank=None):
     raise ValueError(scheme)
 
 
-def tensor_bytes(scheme, n, m, group=None, rank=None):
-    return sum(_al(s) for s in section_sizes(scheme, n, m, group, rank))
+def tensor_bytes(scheme, n, m, group=None, rank=None, factors="int4"):
+    return sum(_al(s) for s in section_sizes(scheme, n, m, group, rank, factors))
 
 
-def _place(sections, scheme, n, m, group, rank):
-    buf = np.zeros(tensor_bytes(scheme, n, m, group, rank), np.uint8)
+def _place(sections, scheme, n, m, group, rank, factors="int4"):
+    buf = np.zeros(tensor_bytes(scheme, n, m, group, rank, factors), np.uint8)
     off = 0
-    for raw, size in zip(sections, section_sizes(scheme, n, m, group, rank)):
+    for raw, size in zip(sections, section_sizes(scheme, n, m, group, rank, factors)):
         raw = np.ascontiguousarray(raw).view(np.uint8).ravel()
         assert raw.size == size, (raw.size, size)
         buf[off:off + size] = raw
@@ -266,9 +286,9 @@ def _place(sections, scheme, n, m, group, rank):
     return buf
 
 
-def _split(buf, scheme, n, m, group, rank):
+def _split(buf, scheme, n, m, group, rank, factors="int4"):
     out, off = [], 0
-    for size in section_sizes(scheme, n, m, group, rank):
+    for size in section_sizes(scheme, n, m, group, rank, factors):
         out.append(buf[off:off + size])
         off += _al(size)
     return out
@@ -291,7 +311,8 @@ def _unpack_int4(b, count):
 
 
 # ------------------------------------------------------------ one tensor
-def compress_tensor(scheme, a, ahat, *, group=None, rank=None, iters=None, q0=None):
+def compress_tensor(scheme, a, ahat, *, group=None, rank=None, iters=None, q0=None,
+                    factors="int4"):
     """One sender step on one tensor.
 
     a: library-view activations as fp32 values [n, m]; ahat: fp32 [n, m].
@@ -314,6 +335,10 @@ def compress_tensor(scheme, a, ahat, *, group=None, rank=None, iters=None, q0=No
         vals, idx = nm_encode(flat)
         c = nm_decode(vals, idx, flat.size)
         packed = _place([vals, idx], scheme, n, m, group, rank)
+    elif scheme == "lr" and factors == "bf16":
+        ub, vb, _ = lr_encode_bf16(r, q0, rank, iters)
+        c = lr_decode_bf16(ub, vb).ravel()
+        packed = _place([ub, vb], scheme, n, m, group, rank, factors)
     elif scheme == "lr":
         qu, qv, su, sv, _ = lr_encode(r, q0, rank, iters)
         c = lr_decode(qu, qv, su, sv).ravel()
@@ -328,10 +353,13 @@ def compress_tensor(scheme, a, ahat, *, group=None, rank=None, iters=None, q0=No
                 r=r)
 
 
-def decode_tensor(scheme, packed, n, m, *, group=None, rank=None):
+def decode_tensor(scheme, packed, n, m, *, group=None, rank=None, factors="int4"):
     """Decode one tensor's packed bytes to C(r) (fp32, or fp64 for lr)."""
-    secs = _split(np.asarray(packed, np.uint8), scheme, n, m, group, rank)
+    secs = _split(np.asarray(packed, np.uint8), scheme, n, m, group, rank, factors)
     N = n * m
+    if scheme == "lr" and factors == "bf16":
+        return lr_decode_bf16(secs[0].view(np.uint16).reshape(n, rank),
+                              secs[1].view(np.uint16).reshape(m, rank))
     if scheme == "q1":
         return q1_decode(secs[0], secs[1].view(np.float32), N, group).reshape(n, m)
     if scheme == "q2":
@@ -346,15 +374,18 @@ def decode_tensor(scheme, packed, n, m, *, group=None, rank=None):
     raise ValueError(scheme)
 
 
-def decompress_tensor(scheme, packed, ahat_r, *, group=None, rank=None):
+def decompress_tensor(scheme, packed, ahat_r, *, group=None, rank=None, factors="int4"):
     n, m = ahat_r.shape
-    c = decode_tensor(scheme, packed, n, m, group=group, rank=rank)
+    c = decode_tensor(scheme, packed, n, m, group=group, rank=rank, factors=factors)
     return accumulate(c.ravel(), ahat_r.ravel()).reshape(n, m)
 
 
-def unpack_fields(scheme, packed, n, m, *, group=None, rank=None):
+def unpack_fields(scheme, packed, n, m, *, group=None, rank=None, factors="int4"):
     """Named views of one tensor's packed sections (for exact comparisons)."""
-    secs = _split(np.asarray(packed, np.uint8), scheme, n, m, group, rank)
+    secs = _split(np.asarray(packed, np.uint8), scheme, n, m, group, rank, factors)
+    if scheme == "lr" and factors == "bf16":
+        return dict(ub=secs[0].view(np.uint16).reshape(n, rank),
+                    vb=secs[1].view(np.uint16).reshape(m, rank))
     if scheme == "q1":
         return dict(bits=secs[0], scale=secs[1].view(np.float32))
     if scheme == "q2":
@@ -370,7 +401,7 @@ def unpack_fields(scheme, packed, n, m, *, group=None, rank=None):
 
 
 # ------------------------------------------------------------ trajectories
-def compress_values(scheme, x, *, group=None, rank=None, iters=None, q0=None):
+def compress_values(scheme, x, *, group=None, rank=None, iters=None, q0=None, factors="int4"):
     """C(x) for a fp32 matrix x [n, m] (fp32, or fp64 for lr)."""
     x = _f32(x)
     flat = x.ravel()
@@ -380,6 +411,9 @@ def compress_values(scheme, x, *, group=None, rank=None, iters=None, q0=None):
         return q2_decode(*q2_encode(flat, group), flat.size, group).reshape(x.shape)
     if scheme == "nm":
         return nm_decode(*nm_encode(flat), flat.size).reshape(x.shape)
+    if scheme == "lr" and factors == "bf16":
+        ub, vb, _ = lr_encode_bf16(x, q0, rank, iters)
+        return lr_decode_bf16(ub, vb)
     if scheme == "lr":
         qu, qv, su, sv, _ = lr_encode(x, q0, rank, iters)
         return lr_decode(qu, qv, su, sv)

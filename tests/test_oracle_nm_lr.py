@@ -136,3 +136,37 @@ def test_lr_zero_and_rank_deficient_residuals():
     assert nd == 2
     assert np.all(np.isfinite(U)) and np.all(np.isfinite(V))
     assert np.count_nonzero(np.abs(U).max(axis=0)) == 2
+
+
+def test_lr_bf16_factors_rounding_and_bound():
+    # factor-precision alternative: the same factors, each element sent as bf16
+    import torch
+    r = RNG.standard_normal((96, 64)).astype(np.float32)
+    q0 = RNG.standard_normal((64, 16)).astype(np.float32)
+    U, V, _ = oracle.lr_factors(r, q0, 16, 2)
+    ub, vb, _ = oracle.lr_encode_bf16(r, q0, 16, 2)
+    for X, xb in ((U, ub), (V, vb)):
+        want = torch.from_numpy(X.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+        assert np.array_equal(xb.view(np.int16), want)
+    # each factor element within u = 2^-8 (+ the fp32 step) of the fp64 value,
+    # so c = Ub Vb^T is within (2u + u^2) |U| |V|^T of U V^T elementwise
+    u = 2.0 ** -8 + 2.0 ** -24
+    c = oracle.lr_decode_bf16(ub, vb)
+    bound = (2 * u + u * u) * (np.abs(U) @ np.abs(V).T)
+    assert np.all(np.abs(c - U @ V.T) <= bound * (1 + 1e-12))
+
+
+def test_lr_bf16_factor_layout_roundtrip():
+    n, m, k = 40, 64, 16
+    assert oracle.section_sizes("lr", n, m, rank=k, factors="bf16") == [2 * n * k, 2 * m * k]
+    a = RNG.standard_normal((n, m)).astype(np.float32)
+    ahat = RNG.standard_normal((n, m)).astype(np.float32)
+    q0 = RNG.standard_normal((m, k)).astype(np.float32)
+    o = oracle.compress_tensor("lr", a, ahat, rank=k, iters=2, q0=q0, factors="bf16")
+    assert o["packed"].size == oracle.tensor_bytes("lr", n, m, rank=k, factors="bf16")
+    c = oracle.decode_tensor("lr", o["packed"], n, m, rank=k, factors="bf16")
+    assert np.array_equal(c.astype(np.float64), o["c"].astype(np.float64))
+    f = oracle.unpack_fields("lr", o["packed"], n, m, rank=k, factors="bf16")
+    assert f["ub"].shape == (n, k) and f["vb"].shape == (m, k)
+    rec = oracle.decompress_tensor("lr", o["packed"], ahat, rank=k, factors="bf16")
+    assert np.array_equal(rec.view(np.uint32), o["ahat"].view(np.uint32))
