@@ -42,6 +42,7 @@ hipError_t launch_nm_decompress(const PeerSet& peers, int batch, const Layout& L
 // the rows into nsplit chunks of split_rows (a multiple of 32).
 struct LowRankWork {
   int rank = 0, iters = 0;
+  bool bf16_factors = false;  // factors sent as bf16 instead of INT4 + scales
   int64_t ntiles = 0, rows_pad = 0;
   int nsplit = 1, split_rows = 0;
   uint16_t* R = nullptr;     // bf16 residual [batch][rows][cols]

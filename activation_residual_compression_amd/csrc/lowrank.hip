@@ -602,6 +602,68 @@ __global__ __launch_bounds__(256) void lr_dequant_kernel(const uint8_t* __restri
   }
 }
 
+// ---------------------------------------------------------------- bf16 factors
+// The factor-precision alternative: U and V sent as bf16 (round to nearest
+// even), row-major, no scales. One lane per factor row as above; the sender's
+// reconstruction uses the bf16 values, exactly what the receiver decodes.
+template <int K>
+__global__ __launch_bounds__(256) void lr_bf16f_kernel(const float* __restrict__ P,
+                                                       const float* __restrict__ Qt,
+                                                       uint8_t* __restrict__ packed,
+                                                       float* __restrict__ ud,
+                                                       float* __restrict__ vd, Layout L) {
+  const int b = blockIdx.y;
+  const int n = (int)L.rows, m = (int)L.cols;
+  uint8_t* pk = packed + (size_t)b * L.tstride;
+  if (blockIdx.x == 0) {
+    for (int s = 0; s < L.nsec; ++s) {
+      const int64_t start = L.sec_off[s] + L.sec_len[s];
+      const int64_t end = (s + 1 < L.nsec) ? L.sec_off[s + 1] : L.tstride;
+      for (int64_t i = start + threadIdx.x; i < end; i += blockDim.x) pk[i] = 0;
+    }
+  }
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n + m) return;
+  const bool isV = r >= n;
+  const int i = isV ? r - n : r;
+  const float* src = isV ? Qt + (size_t)b * K * m + i : P + ((size_t)b * n + i) * K;
+  const size_t stride = isV ? (size_t)m : 1;
+  float* deq = isV ? vd + ((size_t)b * m + i) * K : ud + ((size_t)b * n + i) * K;
+  uint32_t* dst = reinterpret_cast<uint32_t*>(pk + (isV ? L.sec_off[1] : L.sec_off[0]) + (size_t)i * K * 2);
+#pragma unroll
+  for (int j = 0; j < K; j += 4) {
+    uint32_t h[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) h[u] = bf16_rne(src[(j + u) * stride]);
+    dst[j / 2] = h[0] | (h[1] << 16);
+    dst[j / 2 + 1] = h[2] | (h[3] << 16);
+    *reinterpret_cast<f32x4*>(deq + j) =
+        f32x4{__uint_as_float(h[0] << 16), __uint_as_float(h[1] << 16), __uint_as_float(h[2] << 16),
+              __uint_as_float(h[3] << 16)};
+  }
+}
+
+// Receiver: bf16 factors to fp32.
+template <int K>
+__global__ __launch_bounds__(256) void lr_bf16f_dequant_kernel(const uint8_t* __restrict__ packed,
+                                                               float* __restrict__ ud,
+                                                               float* __restrict__ vd, Layout L) {
+  const int b = blockIdx.y;
+  const int n = (int)L.rows, m = (int)L.cols;
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n + m) return;
+  const bool isV = r >= n;
+  const int i = isV ? r - n : r;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(packed + (size_t)b * L.tstride +
+                                                          (isV ? L.sec_off[1] : L.sec_off[0]) + (size_t)i * K * 2);
+  float* deq = isV ? vd + ((size_t)b * m + i) * K : ud + ((size_t)b * n + i) * K;
+#pragma unroll
+  for (int j = 0; j < K; j += 4) {
+    const uint32_t w0 = src[j / 2], w1 = src[j / 2 + 1];
+    *reinterpret_cast<f32x4*>(deq + j) = f32x4{bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+  }
+}
+
 // ---------------------------------------------------------------- reconstruct
 // c = Uq Vq^T with fp32 MFMA from the dequantised factors, applied to the state
 // arrays. A block owns 256 columns (four 64-column strips, one per wave) of a
@@ -779,8 +841,12 @@ hipError_t lr_compress_k(bool bf16, const void* a, float* ahat, float* e, uint8_
     hipLaunchKernelGGL((lr_qfinish_kernel<K>), dim3(K, (m + 1023) / 1024, B), dim3(256), 0, s,
                        w.qpart, w.Qt, w.Qtb, w.amax, m, w.nsplit);
   }
-  hipLaunchKernelGGL((lr_int4_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, w.P, w.Qt,
-                     w.amax, packed, w.ud, w.vd, L);
+  if (w.bf16_factors)
+    hipLaunchKernelGGL((lr_bf16f_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, w.P,
+                       w.Qt, packed, w.ud, w.vd, L);
+  else
+    hipLaunchKernelGGL((lr_int4_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, w.P,
+                       w.Qt, w.amax, packed, w.ud, w.vd, L);
   const RcGrid g = rc_grid(n, m, B, K);
   if (bf16)
     hipLaunchKernelGGL((lr_recon_kernel<uint16_t, true, K>), g.grid, dim3(256), 0, s,
@@ -797,8 +863,12 @@ template <int K>
 hipError_t lr_decompress_k(const uint8_t* packed, float* ahat, int B, const Layout& L,
                            const LowRankWork& w, hipStream_t s) {
   const int n = (int)L.rows, m = (int)L.cols;
-  hipLaunchKernelGGL((lr_dequant_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, packed,
-                     w.ud, w.vd, L);
+  if (w.bf16_factors)
+    hipLaunchKernelGGL((lr_bf16f_dequant_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s,
+                       packed, w.ud, w.vd, L);
+  else
+    hipLaunchKernelGGL((lr_dequant_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s,
+                       packed, w.ud, w.vd, L);
   const RcGrid g = rc_grid(n, m, B, K);
   hipLaunchKernelGGL((lr_recon_kernel<float, false, K>), g.grid, dim3(256), 0, s,
                      (const float*)nullptr, ahat, (float*)nullptr, (const float*)w.ud,

@@ -50,6 +50,12 @@ rc_status_t make_layout(const rc_shape_t& sh, rc_scheme_t scheme, const rc_param
     case RC_Q2: len[0] = N / 4; len[1] = 8 * (N / p.group); nsec = 2; break;
     case RC_NM: len[0] = 4 * (N / 16); len[1] = N / 16; nsec = 2; break;
     case RC_LOWRANK:
+      if (p.flags & RC_LR_BF16_FACTORS) {
+        len[0] = 2 * (int64_t)sh.rows * p.rank;
+        len[1] = 2 * (int64_t)sh.cols * p.rank;
+        nsec = 2;
+        break;
+      }
       len[0] = (int64_t)sh.rows * p.rank / 2;
       len[1] = (int64_t)sh.cols * p.rank / 2;
       len[2] = 4 * (int64_t)p.rank;
@@ -76,7 +82,8 @@ rc_status_t validate(const rc_shape_t& sh, rc_dtype_t dtype, rc_scheme_t scheme,
   if (sh.batch > 65535) return RC_ERR_UNSUPPORTED;  // one grid row per tensor
   if ((int64_t)sh.batch * sh.rows * sh.cols >= kMaxElems) return RC_ERR_UNSUPPORTED;
   if (dtype != RC_BF16 && dtype != RC_F32) return RC_ERR_INVALID_ARG;
-  if (p->flags != 0) return RC_ERR_INVALID_ARG;
+  const uint32_t allowed = scheme == RC_LOWRANK ? RC_LR_BF16_FACTORS : 0u;
+  if (p->flags & ~allowed) return RC_ERR_INVALID_ARG;
   switch (scheme) {
     case RC_Q1:
     case RC_Q2:
@@ -114,6 +121,7 @@ rc_status_t setup_lowrank(rc_plan* pl, const float* q0) {
   rc::LowRankWork& w = pl->lr;
   w.rank = (int)k;
   w.iters = pl->params.iters;
+  w.bf16_factors = (pl->params.flags & RC_LR_BF16_FACTORS) != 0;
   w.ntiles = (n + 63) / 64;
   w.rows_pad = 64 * w.ntiles;
   // split the rows of the R^T P product so that the launch has >= ~2048 blocks

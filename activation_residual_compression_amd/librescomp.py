@@ -23,6 +23,7 @@ RC_OK, RC_ERR_INVALID_ARG, RC_ERR_UNSUPPORTED, RC_ERR_ALIGNMENT, RC_ERR_HIP = 0,
 RC_BF16, RC_F32 = 0, 1
 RC_Q1, RC_Q2, RC_NM, RC_LOWRANK = 0, 1, 2, 3
 RC_MAX_PEERS = 8
+RC_LR_BF16_FACTORS = 1  # rc_params_t.flags, RC_LOWRANK only
 
 SCHEMES = {"q1": RC_Q1, "q2": RC_Q2, "nm": RC_NM, "lr": RC_LOWRANK}
 DTYPES = {"bf16": RC_BF16, "f32": RC_F32}

@@ -77,8 +77,16 @@ typedef struct {
   int32_t iters;    /* RC_LOWRANK: subspace iterations, 1..16                     */
   const float* q0;  /* RC_LOWRANK: HOST fp32 [batch][cols][rank] start matrices;  */
                     /*   copied at plan creation and reused every step           */
-  uint32_t flags;   /* must be 0                                                  */
+  uint32_t flags;   /* 0, or RC_LOWRANK with RC_LR_BF16_FACTORS                   */
 } rc_params_t;
+
+/* rc_params_t.flags for RC_LOWRANK: send the factors as bf16 (round to nearest
+ * even) instead of INT4 with per-column scales -- the factor-precision side of
+ * the low-rank trade-off (Key designs / Low-rank strategy for extreme
+ * compression: at one payload, bf16 factors of rank k cost as much as INT4
+ * factors of rank 4k). Packed layout per tensor: U bf16 [rows*rank] | V bf16
+ * [cols*rank], row-major, each section 256-byte aligned. */
+#define RC_LR_BF16_FACTORS 1u
 
 typedef struct {
   float* ahat; /* sender's copy of the receiver reconstruction, fp32 [batch][rows][cols] */
@@ -148,7 +156,8 @@ rc_status_t rc_plan_destroy(rc_plan_t plan);
  *   Q2: codes [N/4] (element k = bits 2(k%4)..+1 of byte k/4) | {mn, step} f32 pairs [N/G]
  *   NM: {v_i0, v_i1} bf16 pairs [N/16] | index byte i0 | i1<<4 [N/16], i0 < i1
  *   LR: U nibbles [rows*rank/2] | V nibbles [cols*rank/2] | sU f32 [rank] | sV f32 [rank]
- *       (row-major INT4, element t in nibble t, even t low, two's complement)
+ *       (row-major INT4, element t in nibble t, even t low, two's complement);
+ *       with RC_LR_BF16_FACTORS: U bf16 [rows*rank] | V bf16 [cols*rank]
  * Returns 0 for a NULL plan. */
 size_t rc_packed_bytes(rc_plan_t plan);
 size_t rc_tensor_packed_bytes(rc_plan_t plan);

@@ -17,16 +17,21 @@ import pytest
 import torch
 
 from gpu_harness import GpuRun, lib_view_f32, oracle, relF, say, synth, bits
+from activation_residual_compression_amd import librescomp as rc
 
 pytestmark = pytest.mark.gpu
 
 
-def _decode_bound_check(run, b, packed, a_f, ahat_prev, e, ahat, rank):
+def _decode_bound_check(run, b, packed, a_f, ahat_prev, e, ahat, rank, factors="int4"):
     n, m = a_f.shape
     gp = run.tensor_packed(packed, b)
-    f = oracle.unpack_fields("lr", gp, n, m, rank=rank)
-    U = f["qu"].astype(np.float64) * f["su"].astype(np.float64)
-    V = f["qv"].astype(np.float64) * f["sv"].astype(np.float64)
+    f = oracle.unpack_fields("lr", gp, n, m, rank=rank, factors=factors)
+    if factors == "bf16":
+        U = oracle.bf16_value(f["ub"]).astype(np.float64)
+        V = oracle.bf16_value(f["vb"]).astype(np.float64)
+    else:
+        U = f["qu"].astype(np.float64) * f["su"].astype(np.float64)
+        V = f["qv"].astype(np.float64) * f["sv"].astype(np.float64)
     c = U @ V.T
     mag = np.abs(U) @ np.abs(V).T
     want_ahat = (ahat_prev.astype(np.float64) + c).astype(np.float32)
@@ -40,9 +45,12 @@ def _decode_bound_check(run, b, packed, a_f, ahat_prev, e, ahat, rank):
     return f
 
 
-def _run_lr(wl, rank, iters, check, steps=None, code_agree=0.8):
+def _run_lr(wl, rank, iters, check, steps=None, code_agree=0.8, factors="int4"):
     q0 = wl.q0(rank)
-    run = GpuRun((wl.nb, wl.n, wl.m), wl.dtype, "lr", rank=rank, iters=iters, q0=q0)
+    flags = rc.RC_LR_BF16_FACTORS if factors == "bf16" else 0
+    run = GpuRun((wl.nb, wl.n, wl.m), wl.dtype, "lr", rank=rank, iters=iters, q0=q0, flags=flags)
+    assert run.plan.tensor_packed_bytes == oracle.tensor_bytes("lr", wl.n, wl.m, rank=rank,
+                                                               factors=factors)
     try:
         _, a0 = wl.next()
         run.warmup(a0)
@@ -56,13 +64,16 @@ def _run_lr(wl, rank, iters, check, steps=None, code_agree=0.8):
             assert np.array_equal(bits(recon), bits(ahat)), "receiver differs from sender"
             af = lib_view_f32(a, wl.dtype)
             for b in check:
-                f = _decode_bound_check(run, b, packed, af[b], ahat_prev[b], e, ahat, rank)
-                o = oracle.compress_tensor("lr", af[b], ahat_prev[b], rank=rank, iters=iters, q0=q0[b])
+                f = _decode_bound_check(run, b, packed, af[b], ahat_prev[b], e, ahat, rank, factors)
+                o = oracle.compress_tensor("lr", af[b], ahat_prev[b], rank=rank, iters=iters, q0=q0[b],
+                                           factors=factors)
                 eg, eo = relF(af[b], ahat[b]), relF(af[b], o["ahat"])
                 say("[gpu] lr t=%d b=%d eps gpu %.6f oracle %.6f" % (t, b, eg, eo))
                 assert abs(eg - eo) <= 1e-3
-                of = oracle.unpack_fields("lr", o["packed"], wl.n, wl.m, rank=rank)
-                agree = float(np.mean(f["qu"] == of["qu"]))
+                of = oracle.unpack_fields("lr", o["packed"], wl.n, wl.m, rank=rank, factors=factors)
+                key = "ub" if factors == "bf16" else "qu"
+                agree = float(np.mean(f[key] == of[key]))
+                say("[gpu] lr t=%d b=%d %s factor code agreement %.3f" % (t, b, factors, agree))
                 assert agree >= code_agree, agree
             ahat_prev = ahat
     finally:
@@ -73,6 +84,12 @@ def _run_lr(wl, rank, iters, check, steps=None, code_agree=0.8):
 def test_lr_ragged_small(rank, iters):
     wl = synth.FluxWorkload(batch=2, n=100, m=192, steps=4)
     _run_lr(wl, rank, iters, check=[0, 1])
+
+
+@pytest.mark.parametrize("rank,iters", [(16, 2), (32, 1)])
+def test_lr_bf16_factors_ragged(rank, iters):
+    wl = synth.FluxWorkload(batch=2, n=100, m=192, steps=4)
+    _run_lr(wl, rank, iters, check=[0, 1], factors="bf16", code_agree=0.95)
 
 
 def test_lr_fp32_input_rank48():
