@@ -56,14 +56,13 @@ struct LowRankWork {
   float* linv = nullptr;     // inverse Cholesky factor, dead rows zeroed [batch][rank][rank]
   float* qpart = nullptr;    // R^T P partials [batch][nsplit][rank][cols]
   uint32_t* amax = nullptr;  // column absmax bits of U and V [batch][2][rank]
-  float* ud = nullptr;       // dequantised U [batch][rows][rank]
-  float* vd = nullptr;       // dequantised V [batch][cols][rank]
 };
 
 hipError_t launch_lr_compress(bool bf16_input, const void* a, float* ahat, float* e,
                               uint8_t* packed, int batch, const Layout& L, const LowRankWork& w,
                               hipStream_t s);
-hipError_t launch_lr_decompress(const uint8_t* packed, float* ahat, int batch, const Layout& L,
+// Receiver: every peer in one launch (the decode reads only the packed bytes).
+hipError_t launch_lr_decompress(const PeerSet& peers, int batch, const Layout& L,
                                 const LowRankWork& w, hipStream_t s);
 
 }  // namespace rc

@@ -515,16 +515,14 @@ __global__ __launch_bounds__(256) void lr_qfinish_kernel(const float* __restrict
 // One lane per factor row: rows 0..n-1 are U (= P, [n][K]), rows n..n+m-1 are V
 // (= Q, stored as Qt [K][m]). Per column j: s_j = absmax_j / 7,
 // q = clamp(rint_even(x / s_j), -7, 7) (0 when s_j = 0), packed row-major,
-// element t in nibble t (even t low), two's complement. The dequantised
-// factors q * s_j go to ud / vd for the sender's reconstruction. Block 0
-// writes the scale sections and zeroes the section padding.
+// element t in nibble t (even t low), two's complement. Block 0 writes the
+// scale sections and zeroes the section padding. Sender and receiver both
+// reconstruct from these packed bytes (q * s_j, in the reconstruct kernel).
 template <int K>
 __global__ __launch_bounds__(256) void lr_int4_kernel(const float* __restrict__ P,
                                                       const float* __restrict__ Qt,
                                                       const uint32_t* __restrict__ amax,
-                                                      uint8_t* __restrict__ packed,
-                                                      float* __restrict__ ud,
-                                                      float* __restrict__ vd, Layout L) {
+                                                      uint8_t* __restrict__ packed, Layout L) {
   __shared__ float sc[2 * K];
   const int b = blockIdx.y;
   const int n = (int)L.rows, m = (int)L.cols;
@@ -549,69 +547,28 @@ __global__ __launch_bounds__(256) void lr_int4_kernel(const float* __restrict__ 
   const float* s = sc + (isV ? K : 0);
   const float* src = isV ? Qt + (size_t)b * K * m + i : P + ((size_t)b * n + i) * K;
   const size_t stride = isV ? (size_t)m : 1;
-  float* deq = isV ? vd + ((size_t)b * m + i) * K : ud + ((size_t)b * n + i) * K;
   uint32_t words[K / 8];
 #pragma unroll
   for (int q = 0; q < K / 8; ++q) words[q] = 0;
 #pragma unroll
-  for (int j = 0; j < K; j += 4) {
-    float dq[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      int qi = 0;
-      if (s[j + u] > 0.f) qi = (int)fminf(fmaxf(rintf(src[(j + u) * stride] / s[j + u]), -7.f), 7.f);
-      words[(j + u) / 8] |= ((uint32_t)qi & 0xFu) << (4 * ((j + u) % 8));
-      dq[u] = (float)qi * s[j + u];  // the receiver's decode: integer code times scale
-    }
-    *reinterpret_cast<f32x4*>(deq + j) = f32x4{dq[0], dq[1], dq[2], dq[3]};
+  for (int j = 0; j < K; ++j) {
+    int qi = 0;
+    if (s[j] > 0.f) qi = (int)fminf(fmaxf(rintf(src[j * stride] / s[j]), -7.f), 7.f);
+    words[j / 8] |= ((uint32_t)qi & 0xFu) << (4 * (j % 8));
   }
   uint32_t* dst = reinterpret_cast<uint32_t*>(pk + (isV ? L.sec_off[1] : L.sec_off[0]) + (size_t)i * (K / 2));
 #pragma unroll
   for (int q = 0; q < K / 8; ++q) dst[q] = words[q];
 }
 
-// Receiver: dequantise the packed factors (same products q * s as the sender).
-__device__ __forceinline__ float int4_at(const uint8_t* nib, int64_t t) {
-  const uint32_t byte = nib[t >> 1];
-  const int v = (t & 1) ? (int)(byte >> 4) : (int)(byte & 15u);
-  return (float)(v >= 8 ? v - 16 : v);
-}
-
-template <int K>
-__global__ __launch_bounds__(256) void lr_dequant_kernel(const uint8_t* __restrict__ packed,
-                                                         float* __restrict__ ud,
-                                                         float* __restrict__ vd, Layout L) {
-  const int b = blockIdx.y;
-  const int n = (int)L.rows, m = (int)L.cols;
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= n + m) return;
-  const uint8_t* pk = packed + (size_t)b * L.tstride;
-  const bool isV = r >= n;
-  const int i = isV ? r - n : r;
-  const uint8_t* nib = pk + (isV ? L.sec_off[1] : L.sec_off[0]);
-  const float* s = reinterpret_cast<const float*>(pk + (isV ? L.sec_off[3] : L.sec_off[2]));
-  float* deq = isV ? vd + ((size_t)b * m + i) * K : ud + ((size_t)b * n + i) * K;
-#pragma unroll
-  for (int j = 0; j < K; j += 4) {
-    f32x4 v;
-    v.x = int4_at(nib, (int64_t)i * K + j) * s[j];
-    v.y = int4_at(nib, (int64_t)i * K + j + 1) * s[j + 1];
-    v.z = int4_at(nib, (int64_t)i * K + j + 2) * s[j + 2];
-    v.w = int4_at(nib, (int64_t)i * K + j + 3) * s[j + 3];
-    *reinterpret_cast<f32x4*>(deq + j) = v;
-  }
-}
-
 // ---------------------------------------------------------------- bf16 factors
 // The factor-precision alternative: U and V sent as bf16 (round to nearest
-// even), row-major, no scales. One lane per factor row as above; the sender's
-// reconstruction uses the bf16 values, exactly what the receiver decodes.
+// even), row-major, no scales. One lane per factor row as above; sender and
+// receiver reconstruct from the bf16 values.
 template <int K>
 __global__ __launch_bounds__(256) void lr_bf16f_kernel(const float* __restrict__ P,
                                                        const float* __restrict__ Qt,
-                                                       uint8_t* __restrict__ packed,
-                                                       float* __restrict__ ud,
-                                                       float* __restrict__ vd, Layout L) {
+                                                       uint8_t* __restrict__ packed, Layout L) {
   const int b = blockIdx.y;
   const int n = (int)L.rows, m = (int)L.cols;
   uint8_t* pk = packed + (size_t)b * L.tstride;
@@ -628,46 +585,16 @@ __global__ __launch_bounds__(256) void lr_bf16f_kernel(const float* __restrict__
   const int i = isV ? r - n : r;
   const float* src = isV ? Qt + (size_t)b * K * m + i : P + ((size_t)b * n + i) * K;
   const size_t stride = isV ? (size_t)m : 1;
-  float* deq = isV ? vd + ((size_t)b * m + i) * K : ud + ((size_t)b * n + i) * K;
   uint32_t* dst = reinterpret_cast<uint32_t*>(pk + (isV ? L.sec_off[1] : L.sec_off[0]) + (size_t)i * K * 2);
 #pragma unroll
-  for (int j = 0; j < K; j += 4) {
-    uint32_t h[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) h[u] = bf16_rne(src[(j + u) * stride]);
-    dst[j / 2] = h[0] | (h[1] << 16);
-    dst[j / 2 + 1] = h[2] | (h[3] << 16);
-    *reinterpret_cast<f32x4*>(deq + j) =
-        f32x4{__uint_as_float(h[0] << 16), __uint_as_float(h[1] << 16), __uint_as_float(h[2] << 16),
-              __uint_as_float(h[3] << 16)};
-  }
-}
-
-// Receiver: bf16 factors to fp32.
-template <int K>
-__global__ __launch_bounds__(256) void lr_bf16f_dequant_kernel(const uint8_t* __restrict__ packed,
-                                                               float* __restrict__ ud,
-                                                               float* __restrict__ vd, Layout L) {
-  const int b = blockIdx.y;
-  const int n = (int)L.rows, m = (int)L.cols;
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= n + m) return;
-  const bool isV = r >= n;
-  const int i = isV ? r - n : r;
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(packed + (size_t)b * L.tstride +
-                                                          (isV ? L.sec_off[1] : L.sec_off[0]) + (size_t)i * K * 2);
-  float* deq = isV ? vd + ((size_t)b * m + i) * K : ud + ((size_t)b * n + i) * K;
-#pragma unroll
-  for (int j = 0; j < K; j += 4) {
-    const uint32_t w0 = src[j / 2], w1 = src[j / 2 + 1];
-    *reinterpret_cast<f32x4*>(deq + j) = f32x4{bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
-  }
+  for (int j = 0; j < K; j += 2) dst[j / 2] = bf16_rne(src[j * stride]) | (bf16_rne(src[(j + 1) * stride]) << 16);
 }
 
 // ---------------------------------------------------------------- reconstruct
-// c = Uq Vq^T with fp32 MFMA from the dequantised factors, applied to the state
-// arrays. A block owns 256 columns (four 64-column strips, one per wave) of a
-// chunk of rows and walks it in 16-row tiles:
+// c = Uq Vq^T with fp32 MFMA, read straight from the packed factors (INT4 codes
+// times their column scale, or bf16), applied to the state arrays. A block owns
+// 256 columns (four 64-column strips, one per wave) of a chunk of rows of one
+// tensor of one peer and walks it in 16-row tiles:
 //   * once: each wave's V operands (4 MFMA column tiles x K) in registers;
 //   * per tile: each wave computes its 16 x 64 piece of c^T = Vq Uq^T with K
 //     MFMAs and writes it to an LDS tile (two buffers, one barrier per tile);
@@ -675,27 +602,49 @@ __global__ __launch_bounds__(256) void lr_bf16f_dequant_kernel(const uint8_t* __
 //     consecutive columns, so every global access of a wave is one contiguous
 //     1 KiB run: r = a - ahat, e = r - c, ahat += c (SENDER) or ahat += c.
 //     The next tile's U operands and state rows are loaded before the current
-//     tile's MFMAs.
+//     tile's MFMAs; the last tile has no successor to load.
 // MFMA step (j, i), j < K/16, i < 4: lane group g = l/16 covers contraction
-// index 16 j + 4 g + i, so both operands come from 16-byte loads of 4
-// consecutive factor columns. The M index mi of column tile p is strip column
-// 32 (p/2) + 8 (mi/4) + 4 (p%2) + mi%4, so each lane's results are two runs of
-// 8 columns of one row. Sender and receiver run the same MFMA sequence on the
-// same dequantised factors, so both get the same c bit for bit. Strips and
-// lanes past m (m a multiple of 64 but not of 256) compute and store nothing.
+// index 16 j + 4 g + i, so both operands come from 4 consecutive factor
+// entries of one row (2 bytes of INT4 codes or 8 bytes of bf16). The M index mi
+// of column tile p is strip column 32 (p/2) + 8 (mi/4) + 4 (p%2) + mi%4, so each
+// lane's results are two runs of 8 columns of one row. Sender and receiver run
+// the same MFMA sequence on the same packed bytes, so both get the same c bit
+// for bit. Strips and lanes past m (m a multiple of 64 but not of 256) compute
+// and store nothing. Grid z = peer * batch + tensor.
 constexpr int kRcCols = 256;         // columns per block (4 waves x 64)
 constexpr int kRcLds = kRcCols + 4;  // LDS row stride, floats
 
-template <typename IN, bool SENDER, int K>
+// Factor entries (row, k0 .. k0+3) as the encoder defined them: INT4 code times
+// the column scale (scale4 = the 4 scales of k0 .. k0+3), or the bf16 value.
+template <int K, bool BF16F>
+__device__ __forceinline__ f32x4 factor4(const uint8_t* sec, const f32x4& scale4, int row, int k0) {
+  if constexpr (BF16F) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(sec + ((size_t)row * K + k0) * 2);
+    return f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+  } else {
+    const uint32_t w = *reinterpret_cast<const uint16_t*>(sec + ((size_t)row * K + k0) / 2);
+    f32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = (int)((w >> (4 * i)) & 15u);
+      v[i] = (float)(q >= 8 ? q - 16 : q) * scale4[i];
+    }
+    return v;
+  }
+}
+
+template <typename IN, bool SENDER, int K, bool BF16F>
 __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
-                                                       float* __restrict__ ahat,
-                                                       float* __restrict__ e,
-                                                       const float* __restrict__ ud,
-                                                       const float* __restrict__ vd, int n, int m,
-                                                       int chunk_rows) {
+                                                       float* __restrict__ e, PeerSet peers,
+                                                       int batch, Layout L, int chunk_rows) {
   constexpr int KJ = K / 16;
   __shared__ float tile[2][16 * kRcLds];
-  const int b = blockIdx.z;
+  const int n = (int)L.rows, m = (int)L.cols;
+  const int peer = blockIdx.z / batch, b = blockIdx.z % batch;
+  float* __restrict__ ahat = peers.state[peer];
+  const uint8_t* pk = peers.packed[peer] + (size_t)b * L.tstride;
+  const uint8_t* usec = pk + L.sec_off[0];
+  const uint8_t* vsec = pk + L.sec_off[1];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
   const int cb = blockIdx.x * kRcCols;
   const int c0 = cb + 64 * w;
@@ -704,15 +653,23 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
   const int rbeg = blockIdx.y * chunk_rows;
   const int rend = min(n, rbeg + chunk_rows);
 
+  f32x4 su[KJ], sv[KJ];
+#pragma unroll
+  for (int j = 0; j < KJ; ++j) {
+    if constexpr (BF16F) {
+      su[j] = sv[j] = f32x4{1.f, 1.f, 1.f, 1.f};
+    } else {
+      su[j] = *reinterpret_cast<const f32x4*>(pk + L.sec_off[2] + 4 * (16 * j + 4 * lk));
+      sv[j] = *reinterpret_cast<const f32x4*>(pk + L.sec_off[3] + 4 * (16 * j + 4 * lk));
+    }
+  }
   f32x4 av[4][KJ];
-  const float* vb = vd + (size_t)b * m * K;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int col = (strip_ok ? c0 : 0) + 32 * (p >> 1) + 8 * (lr >> 2) + 4 * (p & 1) + (lr & 3);
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) av[p][j] = *reinterpret_cast<const f32x4*>(vb + (size_t)col * K + 16 * j + 4 * lk);
+    for (int j = 0; j < KJ; ++j) av[p][j] = factor4<K, BF16F>(vsec, sv[j], col, 16 * j + 4 * lk);
   }
-  const float* ub = ud + (size_t)b * n * K;
   const size_t tb = (size_t)b * n * m + (size_t)(col_ok ? cb + 4 * lane : 0);
 
   struct Rows {
@@ -724,7 +681,7 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
   auto load = [&](int r0, Rows& R) {
     const int ru = min(r0 + lr, rend - 1);
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) R.u[j] = *reinterpret_cast<const f32x4*>(ub + (size_t)ru * K + 16 * j + 4 * lk);
+    for (int j = 0; j < KJ; ++j) R.u[j] = factor4<K, BF16F>(usec, su[j], ru, 16 * j + 4 * lk);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const size_t off = tb + (size_t)min(r0 + 4 * w + i, rend - 1) * m;
@@ -732,12 +689,7 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
       if constexpr (SENDER) R.x[i] = load4<IN>(a + off);
     }
   };
-
-  Rows cur, nxt;
-  load(rbeg, cur);
-  int it = 0;
-  for (int r0 = rbeg; r0 < rend; r0 += 16, ++it) {
-    load(r0 + 16 < rend ? r0 + 16 : r0, nxt);
+  auto apply = [&](int r0, int it, const Rows& T) {
     f32x4 acc[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -747,17 +699,17 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int p = 0; p < 4; ++p) acc[p] = mfma_f32(av[p][j][i], cur.u[j][i], acc[p]);
+          for (int p = 0; p < 4; ++p) acc[p] = mfma_f32(av[p][j][i], T.u[j][i], acc[p]);
     }
-    float* T = tile[it & 1];
+    float* S = tile[it & 1];
 #pragma unroll
     for (int p = 0; p < 4; ++p)
-      *reinterpret_cast<f32x4*>(&T[lr * kRcLds + 64 * w + 32 * (p >> 1) + 8 * lk + 4 * (p & 1)]) = acc[p];
+      *reinterpret_cast<f32x4*>(&S[lr * kRcLds + 64 * w + 32 * (p >> 1) + 8 * lk + 4 * (p & 1)]) = acc[p];
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = r0 + 4 * w + i;
-      const f32x4 c = *reinterpret_cast<const f32x4*>(&T[(4 * w + i) * kRcLds + 4 * lane]);
+      const f32x4 c = *reinterpret_cast<const f32x4*>(&S[(4 * w + i) * kRcLds + 4 * lane]);
       if (row < rend && col_ok) {
         const size_t off = tb + (size_t)row * m;
         f32x4 hn;
@@ -765,20 +717,29 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
           f32x4 ev;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const float r = cur.x[i][t] - cur.h[i][t];
+            const float r = T.x[i][t] - T.h[i][t];
             ev[t] = r - c[t];
-            hn[t] = cur.h[i][t] + c[t];
+            hn[t] = T.h[i][t] + c[t];
           }
           store4(e + off, ev);
         } else {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) hn[t] = cur.h[i][t] + c[t];
+          for (int t = 0; t < 4; ++t) hn[t] = T.h[i][t] + c[t];
         }
         store4(ahat + off, hn);
       }
     }
+  };
+
+  Rows cur, nxt;
+  load(rbeg, cur);
+  int it = 0, r0 = rbeg;
+  for (; r0 + 16 < rend; r0 += 16, ++it) {
+    load(r0 + 16, nxt);
+    apply(r0, it, cur);
     cur = nxt;
   }
+  apply(r0, it, cur);
 }
 
 // Grid of the reconstruct kernel: 256-column blocks x row chunks x tensors.
@@ -843,36 +804,53 @@ hipError_t lr_compress_k(bool bf16, const void* a, float* ahat, float* e, uint8_
   }
   if (w.bf16_factors)
     hipLaunchKernelGGL((lr_bf16f_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, w.P,
-                       w.Qt, packed, w.ud, w.vd, L);
+                       w.Qt, packed, L);
   else
     hipLaunchKernelGGL((lr_int4_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, w.P,
-                       w.Qt, w.amax, packed, w.ud, w.vd, L);
+                       w.Qt, w.amax, packed, L);
+  PeerSet self{};
+  self.packed[0] = packed;
+  self.state[0] = ahat;
+  self.count = 1;
   const RcGrid g = rc_grid(n, m, B, K);
-  if (bf16)
-    hipLaunchKernelGGL((lr_recon_kernel<uint16_t, true, K>), g.grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(a), ahat, e, (const float*)w.ud,
-                       (const float*)w.vd, n, m, g.chunk_rows);
+  if (bf16 && w.bf16_factors)
+    hipLaunchKernelGGL((lr_recon_kernel<uint16_t, true, K, true>), g.grid, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(a), e, self, B, L, g.chunk_rows);
+  else if (bf16)
+    hipLaunchKernelGGL((lr_recon_kernel<uint16_t, true, K, false>), g.grid, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(a), e, self, B, L, g.chunk_rows);
+  else if (w.bf16_factors)
+    hipLaunchKernelGGL((lr_recon_kernel<float, true, K, true>), g.grid, dim3(256), 0, s,
+                       static_cast<const float*>(a), e, self, B, L, g.chunk_rows);
   else
-    hipLaunchKernelGGL((lr_recon_kernel<float, true, K>), g.grid, dim3(256), 0, s,
-                       static_cast<const float*>(a), ahat, e, (const float*)w.ud, (const float*)w.vd,
-                       n, m, g.chunk_rows);
+    hipLaunchKernelGGL((lr_recon_kernel<float, true, K, false>), g.grid, dim3(256), 0, s,
+                       static_cast<const float*>(a), e, self, B, L, g.chunk_rows);
   return hipGetLastError();
 }
 
+// Receiver: every peer's tensors in one launch (grid z = peer * batch + tensor),
+// split into several launches only if that exceeds the grid's z limit.
 template <int K>
-hipError_t lr_decompress_k(const uint8_t* packed, float* ahat, int B, const Layout& L,
-                           const LowRankWork& w, hipStream_t s) {
+hipError_t lr_decompress_k(const PeerSet& peers, int B, const Layout& L, const LowRankWork& w,
+                           hipStream_t s) {
   const int n = (int)L.rows, m = (int)L.cols;
-  if (w.bf16_factors)
-    hipLaunchKernelGGL((lr_bf16f_dequant_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s,
-                       packed, w.ud, w.vd, L);
-  else
-    hipLaunchKernelGGL((lr_dequant_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s,
-                       packed, w.ud, w.vd, L);
-  const RcGrid g = rc_grid(n, m, B, K);
-  hipLaunchKernelGGL((lr_recon_kernel<float, false, K>), g.grid, dim3(256), 0, s,
-                     (const float*)nullptr, ahat, (float*)nullptr, (const float*)w.ud,
-                     (const float*)w.vd, n, m, g.chunk_rows);
+  RcGrid g = rc_grid(n, m, B, K);
+  const int per_launch = B * peers.count <= 65535 ? peers.count : 1;
+  for (int p0 = 0; p0 < peers.count; p0 += per_launch) {
+    PeerSet sub{};
+    sub.count = per_launch < peers.count - p0 ? per_launch : peers.count - p0;
+    for (int q = 0; q < sub.count; ++q) {
+      sub.packed[q] = peers.packed[p0 + q];
+      sub.state[q] = peers.state[p0 + q];
+    }
+    g.grid.z = (unsigned)(B * sub.count);
+    if (w.bf16_factors)
+      hipLaunchKernelGGL((lr_recon_kernel<float, false, K, true>), g.grid, dim3(256), 0, s,
+                         (const float*)nullptr, (float*)nullptr, sub, B, L, g.chunk_rows);
+    else
+      hipLaunchKernelGGL((lr_recon_kernel<float, false, K, false>), g.grid, dim3(256), 0, s,
+                         (const float*)nullptr, (float*)nullptr, sub, B, L, g.chunk_rows);
+  }
   return hipGetLastError();
 }
 
@@ -891,14 +869,14 @@ hipError_t launch_lr_compress(bool bf16_input, const void* a, float* ahat, float
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_lr_decompress(const uint8_t* packed, float* ahat, int batch, const Layout& L,
+hipError_t launch_lr_decompress(const PeerSet& peers, int batch, const Layout& L,
                                 const LowRankWork& w, hipStream_t s) {
   if (L.cols % 64) return hipErrorInvalidValue;
   switch (w.rank) {
-    case 16: return lr_decompress_k<16>(packed, ahat, batch, L, w, s);
-    case 32: return lr_decompress_k<32>(packed, ahat, batch, L, w, s);
-    case 48: return lr_decompress_k<48>(packed, ahat, batch, L, w, s);
-    case 64: return lr_decompress_k<64>(packed, ahat, batch, L, w, s);
+    case 16: return lr_decompress_k<16>(peers, batch, L, w, s);
+    case 32: return lr_decompress_k<32>(peers, batch, L, w, s);
+    case 48: return lr_decompress_k<48>(peers, batch, L, w, s);
+    case 64: return lr_decompress_k<64>(peers, batch, L, w, s);
   }
   return hipErrorInvalidValue;
 }

@@ -142,8 +142,6 @@ rc_status_t setup_lowrank(rc_plan* pl, const float* q0) {
       {(void**)&w.linv, B * k * k * 4},
       {(void**)&w.qpart, B * w.nsplit * k * m * 4},
       {(void**)&w.amax, B * 2 * k * 4},
-      {(void**)&w.ud, B * n * k * 4},
-      {(void**)&w.vd, B * m * k * 4},
   };
   int64_t total = 0;
   for (auto& pc : pieces) total += align_up(pc.bytes);
@@ -182,8 +180,6 @@ rc::LowRankWork lr_slice(const rc::LowRankWork& w, const rc::Layout& L, int64_t 
   s.linv += b0 * k * k;
   s.qpart += b0 * w.nsplit * k * m;
   s.amax += b0 * 2 * k;
-  s.ud += b0 * n * k;
-  s.vd += b0 * m * k;
   return s;
 }
 
@@ -227,13 +223,7 @@ hipError_t decompress_peers(rc_plan* pl, hipStream_t stream, const uint8_t* cons
     case RC_NM:
       return rc::launch_nm_decompress(ps, pl->shape.batch, pl->layout, stream);
     case RC_LOWRANK:
-      // the dequantised factors live in the plan's workspace: one peer at a time
-      for (int p = 0; p < npeers; ++p) {
-        const hipError_t err = rc::launch_lr_decompress(packed[p], states[p], pl->shape.batch,
-                                                        pl->layout, pl->lr, stream);
-        if (err != hipSuccess) return err;
-      }
-      return hipSuccess;
+      return rc::launch_lr_decompress(ps, pl->shape.batch, pl->layout, pl->lr, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -137,10 +137,8 @@ rc_status_t rc_decompress(rc_plan_t plan, hipStream_t stream, const void* packed
  * one packed stream from each peer, Overall framework): recon_states[p] +=
  * decode(packed_in[p]) for p < npeers, 1 <= npeers <= RC_MAX_PEERS, each state
  * fp32 [batch][rows][cols] and each stream rc_packed_bytes(plan) bytes laid out
- * by this plan. The results equal npeers calls of rc_decompress. Q1, Q2 and NM
- * decode all peers in one launch; RC_LOWRANK decodes them one after another
- * (its dequantised factors live in the plan's workspace). The states must not
- * overlap. */
+ * by this plan. The results equal npeers calls of rc_decompress; all peers are
+ * decoded in one launch. The states must not overlap. */
 #define RC_MAX_PEERS 8
 rc_status_t rc_decompress_many(rc_plan_t plan, hipStream_t stream, const void* const* packed_in,
                                float* const* recon_states, int npeers);
