@@ -10,6 +10,12 @@
       The JSON records the sha256 of the kernel sources, so a later reader can tell
       whether the kernels changed since the counters were taken.
 
+  python -m activation_residual_compression_amd.profsummary mfma <pmc.db> [--trace trace.json] [--md OUT] [--json OUT]
+      per-kernel MFMA work from one run with SQ_INSTS_VALU_MFMA_MOPS_BF16,
+      SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE: bf16 MFMA flops per dispatch
+      (MOPS x 512), MFMA busy share of the SIMD cycles (busy / (GUI_ACTIVE x SIMDs)),
+      and, with a kernel-trace summary, achieved TFLOP/s against the dense bf16 peak.
+
 --title and --command (repeatable) put a heading and the commands that made the
 databases at the top of the Markdown summary.
 """
@@ -25,6 +31,8 @@ import sqlite3
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 COPY_BYTES_KB = 1 << 20  # 1 GiB copy: 1 GiB read and 1 GiB written
+SIMDS = 256 * 4           # MI355X: 256 CUs x 4 SIMDs
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 
 
 def short_name(name: str) -> str:
@@ -50,12 +58,20 @@ def trace_table(db: str):
     return [(short_name(r[0]), r[1], r[2] / 1e3, r[3] / 1e3, r[4] / 1e3) for r in rows]
 
 
-def pmc_values(db: str, counter: str):
+def pmc_values(db: str, counter: str, reduce=sum):
+    """Per kernel name, one value per dispatch: the counter's instances (per
+    shader engine, per XCD, ...) combined with `reduce` (sum for event counts,
+    max for GRBM_GUI_ACTIVE, as rocprofv3's own derived metrics do)."""
     con = sqlite3.connect(db)
+    per = collections.defaultdict(list)
+    names = {}
+    for did, name, val in con.execute("select dispatch_id, name, counter_value from pmc_events "
+                                      "where counter_name=?", (counter,)):
+        per[did].append(float(val))
+        names[did] = short_name(name)
     d = collections.defaultdict(list)
-    for name, val in con.execute("select name, counter_value from pmc_events where counter_name=?",
-                                 (counter,)):
-        d[short_name(name)].append(float(val))
+    for did in sorted(per):
+        d[names[did]].append(reduce(per[did]))
     return d
 
 
@@ -82,7 +98,12 @@ def main(argv=None):
     p.add_argument("write_db")
     p.add_argument("--md")
     p.add_argument("--json")
-    for q in (t, p):
+    mf = sub.add_parser("mfma")
+    mf.add_argument("db")
+    mf.add_argument("--trace")
+    mf.add_argument("--md")
+    mf.add_argument("--json")
+    for q in (t, p, mf):
         q.add_argument("--title")
         q.add_argument("--command", action="append", default=[])
     args = ap.parse_args(argv)
@@ -100,6 +121,39 @@ def main(argv=None):
                       open(args.json, "w"), indent=1, sort_keys=True)
         lines = ["| kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
         lines += ["| `%s` | %d | %.1f | %.1f | %.1f |" % r for r in rows]
+        text = "\n".join(lines)
+    elif args.mode == "mfma":
+        mops = pmc_values(args.db, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        busy = pmc_values(args.db, "SQ_VALU_MFMA_BUSY_CYCLES")
+        gui = pmc_values(args.db, "GRBM_GUI_ACTIVE", reduce=max)
+        dur = json.load(open(args.trace))["kernels"] if args.trace else {}
+        avg = lambda v: sum(v) / len(v) if v else 0.0
+        kern = {}
+        for k in sorted(mops):
+            if avg(mops[k]) <= 0:
+                continue
+            fl = avg(mops[k]) * 512
+            ent = dict(dispatches=len(mops[k]), bf16_flops=fl,
+                       mfma_busy_frac=avg(busy.get(k, [])) / (avg(gui.get(k, [])) * SIMDS)
+                       if gui.get(k) else None)
+            if k in dur:
+                ent["avg_us"] = dur[k]["avg_us"]
+                ent["tflops"] = fl / (dur[k]["avg_us"] * 1e-6) / 1e12
+                ent["frac_of_bf16_peak"] = ent["tflops"] / BF16_PEAK_TFLOPS
+            kern[k] = ent
+        if args.json:
+            json.dump(dict(kernels=kern, sources=source_hashes(), simds=SIMDS,
+                           bf16_peak_tflops=BF16_PEAK_TFLOPS), open(args.json, "w"), indent=1,
+                      sort_keys=True)
+        lines = ["| kernel | dispatches | bf16 MFMA GFLOP/dispatch | MFMA busy / SIMD cycles | avg us | TFLOP/s | of 2.5 PFLOP/s |",
+                 "|---|---|---|---|---|---|---|"]
+        for k, v in sorted(kern.items(), key=lambda kv: -kv[1]["bf16_flops"]):
+            lines.append("| `%s` | %d | %.2f | %s | %s | %s | %s |" % (
+                k, v["dispatches"], v["bf16_flops"] / 1e9,
+                "%.1f %%" % (100 * v["mfma_busy_frac"]) if v["mfma_busy_frac"] is not None else "-",
+                "%.1f" % v["avg_us"] if "avg_us" in v else "-",
+                "%.1f" % v["tflops"] if "tflops" in v else "-",
+                "%.2f %%" % (100 * v["frac_of_bf16_peak"]) if "tflops" in v else "-"))
         text = "\n".join(lines)
     else:
         F, W = pmc_values(args.fetch_db, "FETCH_SIZE"), pmc_values(args.write_db, "WRITE_SIZE")
