@@ -79,6 +79,8 @@ def _load():
         lib.sg_video_init.argtypes = [u64, i32, ctypes.POINTER(_VideoGeom), i32, vp, vp]
         lib.sg_video_step.argtypes = [u64, i32, i32, ctypes.POINTER(_VideoGeom), i32, dbl, vp, vp, vp]
         lib.sg_q0.argtypes = [u64, i32, i32, i32, vp]
+        lib.sg_latent_init.argtypes = [u64, i32, i32, i32, i32, vp, vp]
+        lib.sg_latent_step.argtypes = [u64, i32, i32, i32, i32, i32, dbl, dbl, dbl, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -259,7 +261,34 @@ class VideoWorkload(Workload):
                               _p(self._sc[i]), _p(self._state[i]), _p(self._scratch))
 
 
-# The five evaluated settings: (workload factory, scheme, scheme parameters).
+class LatentWorkload(Workload):
+    """Spatial token grid H x W (raster order) x C channels, bf16; change per step
+    concentrated in smooth regions (gen.c, sg_latent_*)."""
+
+    def __init__(self, name="latent", batch=16, height=64, width=128, m=320, steps=50,
+                 seed=SEED_BASE + 5, sigma=0.1, gamma=1.0, blur=8.0, tensors=None):
+        self.height, self.width = height, width
+        self.sigma, self.gamma, self.blur = sigma, gamma, blur
+        super().__init__(name, batch, height * width, m, steps, "bf16", seed, tensors)
+
+    def _init(self):
+        lib = _load()
+        self._sc = np.empty((self.nb, self.m), np.float32)
+        self._state = np.empty((self.nb, self.n, self.m), np.float32)
+        self._field = np.empty(2 * self.n, np.float64)
+        for i, b in enumerate(self.tensors):
+            lib.sg_latent_init(self.seed, b, self.height, self.width, self.m, _p(self._sc[i]),
+                               _p(self._state[i]))
+
+    def _step(self, t):
+        lib = _load()
+        for i, b in enumerate(self.tensors):
+            lib.sg_latent_step(self.seed, b, t, self.height, self.width, self.m, self.sigma,
+                               self.gamma, self.blur, _p(self._sc[i]), _p(self._state[i]),
+                               _p(self._field))
+
+
+# The evaluated settings: (workload factory, scheme, scheme parameters).
 CONFIGS = {
     "tiny_q1": dict(workload=lambda **kw: WalkWorkload(**kw), scheme="q1", group=64),
     "flux_q2": dict(workload=lambda **kw: FluxWorkload(**kw), scheme="q2", group=128),
@@ -267,6 +296,9 @@ CONFIGS = {
     "flux_lr": dict(workload=lambda **kw: FluxWorkload(**kw), scheme="lr", rank=32, iters=2),
     "video_q1": dict(workload=lambda **kw: VideoWorkload(**kw), scheme="q1", group=64),
     "video_lr": dict(workload=lambda **kw: VideoWorkload(**kw), scheme="lr", rank=48, iters=2),
+    # Otil-style block selection: 8x8-token blocks, a quarter of them per step
+    "latent_bs": dict(workload=lambda **kw: LatentWorkload(**kw), scheme="bs", grid_w=128,
+                      keep_blocks=32),
 }
 
 
@@ -280,6 +312,6 @@ def sigma_ratio(a_prev: np.ndarray, a_next: np.ndarray) -> float:
     return float(d.std() / a_prev.astype(np.float64).std())
 
 
-__all__ = ["Workload", "WalkWorkload", "FluxWorkload", "VideoWorkload", "CONFIGS", "make", "build",
+__all__ = ["Workload", "WalkWorkload", "FluxWorkload", "VideoWorkload", "LatentWorkload", "CONFIGS", "make", "build",
            "normal", "uniform", "key", "to_bf16_bits", "bf16_bits_to_f32", "SEED_BASE",
            "sigma_ratio"]

@@ -296,3 +296,70 @@ void sg_q0(uint64_t seed, int tensor, int m, int rank, float* q0) {
   const uint64_t k = sg_key(seed, ROLE_Q0, tensor, 0);
   for (int64_t i = 0; i < (int64_t)m * rank; ++i) q0[i] = (float)sm_normal(k, i);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Latent-like share for block selection (the Otil page's setting: diffusion */
+/* activations on a spatial token grid, where adjacent steps change mostly   */
+/* in a few regions). Tokens form an H x W grid in raster order, C channels. */
+/*   a_0 = N(0,1) s_c, s_c ~ LogNormal(0, 0.5) per channel;                  */
+/*   a_t = a_{t-1} + sigma g_t(token) N(0,1) s_c, where the intensity field  */
+/*   g_t = exp(gamma z / std(z)) / rms(...) comes from a per-step N(0,1)     */
+/*   field z on the grid blurred by a 2-D Gaussian (std blur tokens, radius  */
+/*   ceil(3 blur), mirror padding): smooth regions of strong and weak change */
+/*   whose mean square is 1, so E[step^2] = sigma^2 s_c^2.                   */
+/* ------------------------------------------------------------------------ */
+enum { ROLE_FIELD = 9 };
+
+void sg_latent_init(uint64_t seed, int tensor, int H, int W, int C, float* sc, float* a0) {
+  const uint64_t ks = sg_key(seed, ROLE_SCALE, tensor, 0);
+  for (int j = 0; j < C; ++j) sc[j] = (float)exp(0.5 * sm_normal(ks, j));
+  const uint64_t ka = sg_key(seed, ROLE_A0, tensor, 0);
+  const int64_t N = (int64_t)H * W * C;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < N; ++i) a0[i] = (float)(sm_normal(ka, i) * sc[i % C]);
+}
+
+void sg_latent_step(uint64_t seed, int tensor, int t, int H, int W, int C, double sigma,
+                    double gamma, double blur, const float* sc, float* a, double* field /* [2][H*W] */) {
+  const int HW = H * W;
+  const uint64_t kf = sg_key(seed, ROLE_FIELD, tensor, t);
+  double* z = field;
+  double* tmp = field + HW;
+  for (int p = 0; p < HW; ++p) z[p] = sm_normal(kf, p);
+  const int radius = (int)ceil(3.0 * blur);
+  double w[256];
+  double wsum = 0.0;
+  for (int k = -radius; k <= radius; ++k) {
+    w[k + radius] = exp(-(double)k * k / (2.0 * blur * blur));
+    wsum += w[k + radius];
+  }
+  for (int k = 0; k <= 2 * radius; ++k) w[k] /= wsum;
+  for (int h = 0; h < H; ++h)
+    for (int x = 0; x < W; ++x) {
+      double s = 0.0;
+      for (int k = -radius; k <= radius; ++k) s += w[k + radius] * z[h * W + mirror(x + k, W)];
+      tmp[h * W + x] = s;
+    }
+  double m1 = 0.0, m2 = 0.0;
+  for (int h = 0; h < H; ++h)
+    for (int x = 0; x < W; ++x) {
+      double s = 0.0;
+      for (int k = -radius; k <= radius; ++k) s += w[k + radius] * tmp[mirror(h + k, H) * W + x];
+      z[h * W + x] = s;
+      m1 += s;
+      m2 += s * s;
+    }
+  const double mean = m1 / HW, sd = sqrt(m2 / HW - mean * mean);
+  double g2 = 0.0;
+  for (int p = 0; p < HW; ++p) {
+    z[p] = exp(gamma * (z[p] - mean) / sd);
+    g2 += z[p] * z[p];
+  }
+  const double norm = 1.0 / sqrt(g2 / HW);
+  const uint64_t kn = sg_key(seed, ROLE_STEP, tensor, t);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < (int64_t)HW * C; ++i) {
+    const int64_t p = i / C;
+    a[i] = (float)((double)a[i] + sigma * z[p] * norm * sm_normal(kn, i) * (double)sc[i % C]);
+  }
+}

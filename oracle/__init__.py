@@ -68,6 +68,7 @@ def _load():
         lib.orc_lr_encode.restype = i32
         lib.orc_lr_encode.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.orc_lr_decode.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+        lib.orc_bs_scores.argtypes = [i32, i32, i32, vp, vp, vp]
         lib.orc_lr_factors.restype = i32
         lib.orc_lr_factors.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
         _lib = lib
@@ -239,6 +240,41 @@ def lr_factors(r, q0, rank, iters):
     return U, V, nd
 
 
+# ------------------------------------------------------------ block selection
+def bs_scores(a, ahat, grid_w):
+    """Cosine dissimilarity of every 8x8-token block (raster order), fp64."""
+    a, ahat = _f32(a), _f32(ahat)
+    n, m = a.shape
+    K = (n // grid_w // 8) * (grid_w // 8)
+    d = np.empty(K, np.float64)
+    _load().orc_bs_scores(n, m, grid_w, _p(a), _p(ahat), _p(d))
+    return d
+
+
+def bs_select(d, visited, keep):
+    """Top-`keep` blocks by dissimilarity among the blocks not yet visited in
+    this round (ties to the lower index), then mark them visited (Otil page,
+    Key design 3: dynamic round robin). Reading: when every block has been
+    visited, the round restarts before selecting, and a round's last step sends
+    only the blocks still unvisited. Returns (selected indices ascending,
+    visited mask after the step)."""
+    visited = np.array(visited, dtype=bool, copy=True)
+    if visited.all():
+        visited[:] = False
+    cand = np.flatnonzero(~visited)
+    order = cand[np.lexsort((cand, -np.asarray(d)[cand]))]
+    sel = np.sort(order[:keep])
+    visited[sel] = True
+    return sel, visited
+
+
+def bs_block_tokens(i, grid_w):
+    """Token indices of block i (raster order inside the block)."""
+    nbx = grid_w // 8
+    by, bx = divmod(int(i), nbx)
+    return np.array([(by * 8 + dy) * grid_w + bx * 8 + dx for dy in range(8) for dx in range(8)])
+
+
 # ------------------------------------------------------------ packed layout
 # Per tensor, sections in this order, each starting at a multiple of 256 bytes;
 # tensors follow each other, each tensor's block a multiple of 256 bytes.
@@ -249,6 +285,9 @@ def lr_factors(r, q0, rank, iters):
 #       nibble t of a row-major [rows x k] INT4 matrix = element t; even t in
 #       the low nibble; two's complement.
 #   lr with bf16 factors: U bf16 [n*k] | V bf16 [m*k], row-major.
+#   bs: u32 [1 + keep] (count, then the sent block indices ascending, unused
+#       slots 0) | block values [keep][64 tokens][m] in the input dtype (bf16 bit
+#       patterns or fp32), tokens of a block in raster order, unused slots 0.
 ALIGN = 256
 
 
@@ -256,8 +295,10 @@ def _al(x):
     return (x + ALIGN - 1) // ALIGN * ALIGN
 
 
-def section_sizes(scheme, n, m, group=None, rank=None, factors="int4"):
+def section_sizes(scheme, n, m, group=None, rank=None, factors="int4", keep=None, in_bytes=2):
     N = n * m
+    if scheme == "bs":
+        return [4 * (1 + keep), keep * 64 * m * in_bytes]
     if scheme == "lr" and factors == "bf16":
         return [2 * n * rank, 2 * m * rank]
     if scheme == "q1":
@@ -271,14 +312,14 @@ def section_sizes(scheme, n, m, group=None, rank=None, factors="int4"):
     raise ValueError(scheme)
 
 
-def tensor_bytes(scheme, n, m, group=None, rank=None, factors="int4"):
-    return sum(_al(s) for s in section_sizes(scheme, n, m, group, rank, factors))
+def tensor_bytes(scheme, n, m, group=None, rank=None, factors="int4", keep=None, in_bytes=2):
+    return sum(_al(s) for s in section_sizes(scheme, n, m, group, rank, factors, keep, in_bytes))
 
 
-def _place(sections, scheme, n, m, group, rank, factors="int4"):
-    buf = np.zeros(tensor_bytes(scheme, n, m, group, rank, factors), np.uint8)
+def _place(sections, scheme, n, m, group, rank, factors="int4", keep=None, in_bytes=2):
+    buf = np.zeros(tensor_bytes(scheme, n, m, group, rank, factors, keep, in_bytes), np.uint8)
     off = 0
-    for raw, size in zip(sections, section_sizes(scheme, n, m, group, rank, factors)):
+    for raw, size in zip(sections, section_sizes(scheme, n, m, group, rank, factors, keep, in_bytes)):
         raw = np.ascontiguousarray(raw).view(np.uint8).ravel()
         assert raw.size == size, (raw.size, size)
         buf[off:off + size] = raw
@@ -286,9 +327,9 @@ def _place(sections, scheme, n, m, group, rank, factors="int4"):
     return buf
 
 
-def _split(buf, scheme, n, m, group, rank, factors="int4"):
+def _split(buf, scheme, n, m, group, rank, factors="int4", keep=None, in_bytes=2):
     out, off = [], 0
-    for size in section_sizes(scheme, n, m, group, rank, factors):
+    for size in section_sizes(scheme, n, m, group, rank, factors, keep, in_bytes):
         out.append(buf[off:off + size])
         off += _al(size)
     return out
@@ -351,6 +392,49 @@ def compress_tensor(scheme, a, ahat, *, group=None, rank=None, iters=None, q0=No
     e, ahat_new = ef_update(flat, c, ahat.ravel())
     return dict(packed=packed, c=c.reshape(n, m), e=e.reshape(n, m), ahat=ahat_new.reshape(n, m),
                 r=r)
+
+
+def bs_compress_tensor(a, ahat, *, grid_w, keep, visited, in_dtype="bf16"):
+    """One sender step of Otil-style block selection on one tensor.
+
+    The selected blocks are sent as they are (values of a_t in the input dtype)
+    and replace the receiver's copy, so after the step ahat = a_t there and
+    e = 0; elsewhere ahat is unchanged and e = fl(a_t - ahat) (the whole
+    residual stays on the sender). Returns dict(packed, e, ahat, visited,
+    selected, scores)."""
+    a = _f32(a)
+    ahat = _f32(ahat)
+    n, m = a.shape
+    d = bs_scores(a, ahat, grid_w)
+    sel, vis = bs_select(d, visited, keep)
+    e = residual(a, ahat).reshape(n, m).copy()
+    ahat_new = ahat.copy()
+    in_bytes = 2 if in_dtype == "bf16" else 4
+    head = np.zeros(1 + keep, np.uint32)
+    head[0] = sel.size
+    head[1:1 + sel.size] = sel
+    vals = np.zeros((keep, 64, m), np.uint16 if in_bytes == 2 else np.float32)
+    for j, i in enumerate(sel):
+        tok = bs_block_tokens(i, grid_w)
+        ahat_new[tok] = a[tok]
+        e[tok] = 0.0
+        vals[j] = bf16_bits(a[tok]) if in_bytes == 2 else a[tok]
+    packed = _place([head, vals], "bs", n, m, None, None, keep=keep, in_bytes=in_bytes)
+    return dict(packed=packed, e=e, ahat=ahat_new, visited=vis, selected=sel, scores=d)
+
+
+def bs_decompress_tensor(packed, ahat_r, *, grid_w, keep, in_dtype="bf16"):
+    """Receiver: put every sent block back at its place."""
+    n, m = ahat_r.shape
+    in_bytes = 2 if in_dtype == "bf16" else 4
+    head, vals = _split(np.asarray(packed, np.uint8), "bs", n, m, None, None, keep=keep,
+                        in_bytes=in_bytes)
+    head = head.view(np.uint32)
+    vals = (bf16_value(vals.view(np.uint16)) if in_bytes == 2 else vals.view(np.float32)).reshape(keep, 64, m)
+    out = _f32(ahat_r).copy()
+    for j in range(int(head[0])):
+        out[bs_block_tokens(head[1 + j], grid_w)] = vals[j]
+    return out
 
 
 def decode_tensor(scheme, packed, n, m, *, group=None, rank=None, factors="int4"):

@@ -392,3 +392,36 @@ int orc_lr_factors(int n, int m, int k, int iters, const float* r, const float* 
   free(sv);
   return nd;
 }
+
+/* ------------------------------------------------------------ block selection */
+/* Otil-style block selection ("Otil: Accelerating Diffusion Model Inference
+ * via Communication-Efficient Multi-GPU Parallelism", Key designs 1 and 2).
+ * Tokens form a grid of grid_w columns (raster order); a block is 8 x 8 tokens
+ * with all m channels, blocks numbered in raster order. For block i the
+ * dissimilarity is d = 1 - <A_i, B_i>_F / (|A_i|_F |B_i|_F) between the current
+ * activation A = a and the receiver's copy B = ahat (the block's value when it
+ * was last sent). Readings: both blocks zero -> d = 0; exactly one zero -> d = 1.
+ * Sums in fp64 over the block's tokens in raster order, channels innermost
+ * (products of two fp32 values are exact in fp64). */
+void orc_bs_scores(int n, int m, int grid_w, const float* a, const float* ahat, double* d) {
+  const int gh = n / grid_w, nbx = grid_w / 8, nby = gh / 8;
+  for (int by = 0; by < nby; ++by)
+    for (int bx = 0; bx < nbx; ++bx) {
+      double dot = 0.0, na = 0.0, nb = 0.0;
+      for (int dy = 0; dy < 8; ++dy)
+        for (int dx = 0; dx < 8; ++dx) {
+          const int64_t tok = (int64_t)(by * 8 + dy) * grid_w + bx * 8 + dx;
+          for (int c = 0; c < m; ++c) {
+            const double x = a[tok * m + c], y = ahat[tok * m + c];
+            dot += x * y;
+            na += x * x;
+            nb += y * y;
+          }
+        }
+      double v;
+      if (na == 0.0 && nb == 0.0) v = 0.0;
+      else if (na == 0.0 || nb == 0.0) v = 1.0;
+      else v = 1.0 - dot / sqrt(na * nb);
+      d[by * nbx + bx] = v;
+    }
+}
