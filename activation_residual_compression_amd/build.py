@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "lib", "librescomp.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["quant.hip", "nm.hip", "lowrank.hip", "probe.hip", "plan.cpp"]
+SOURCES = ["quant.hip", "nm.hip", "lowrank.hip", "blocksel.hip", "probe.hip", "plan.cpp"]
 ARCH = os.environ.get("RC_OFFLOAD_ARCH", "gfx950")
 FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

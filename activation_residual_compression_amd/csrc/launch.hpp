@@ -65,4 +65,21 @@ hipError_t launch_lr_compress(bool bf16_input, const void* a, float* ahat, float
 hipError_t launch_lr_decompress(const PeerSet& peers, int batch, const Layout& L,
                                 const LowRankWork& w, hipStream_t s);
 
+// Otil-style block selection: tokens on a grid of grid_w columns, 8 x 8-token
+// blocks (nblocks per tensor, raster order), keep blocks sent per step.
+constexpr int kBsMaxBlocks = 4096;
+struct BlockSel {
+  int64_t rows = 0, cols = 0;
+  int grid_w = 0, nblocks = 0, keep = 0;
+  Layout L;
+};
+// part: fp64 [batch][nblocks][8][3] scratch (row partial sums); visited: u8
+// [batch][nblocks] round state.
+hipError_t launch_bs_compress(bool bf16_input, const void* a, float* ahat, float* e,
+                              uint8_t* packed, int batch, const BlockSel& S, double* part,
+                              uint8_t* visited, hipStream_t s);
+hipError_t launch_bs_decompress(bool bf16_input, const PeerSet& peers, int batch, const BlockSel& S,
+                                hipStream_t s);
+hipError_t launch_bs_reset(uint8_t* visited, int64_t n, hipStream_t s);
+
 }  // namespace rc

@@ -23,6 +23,10 @@ struct rc_plan {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   rc::LowRankWork lr;
+  // block selection: fp64 row partial sums [B][K][8][3] (scratch) and round state, in ws
+  rc::BlockSel bs;
+  double* bs_score = nullptr;
+  uint8_t* bs_visited = nullptr;
   // chunk-done events of rc_compress_send, created on first use on ev_device
   std::vector<hipEvent_t> events;
   int ev_device = 0;
@@ -37,8 +41,8 @@ int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-rc_status_t make_layout(const rc_shape_t& sh, rc_scheme_t scheme, const rc_params_t& p,
-                        rc::Layout* L) {
+rc_status_t make_layout(const rc_shape_t& sh, rc_dtype_t dtype, rc_scheme_t scheme,
+                        const rc_params_t& p, rc::Layout* L) {
   L->rows = sh.rows;
   L->cols = sh.cols;
   L->n = (int64_t)sh.rows * sh.cols;
@@ -61,6 +65,11 @@ rc_status_t make_layout(const rc_shape_t& sh, rc_scheme_t scheme, const rc_param
       len[2] = 4 * (int64_t)p.rank;
       len[3] = 4 * (int64_t)p.rank;
       nsec = 4;
+      break;
+    case RC_BLOCKSEL:
+      len[0] = 4 * (1 + (int64_t)p.keep_blocks);
+      len[1] = (int64_t)p.keep_blocks * 64 * sh.cols * (dtype == RC_BF16 ? 2 : 4);
+      nsec = 2;
       break;
     default: return RC_ERR_INVALID_ARG;
   }
@@ -103,6 +112,15 @@ rc_status_t validate(const rc_shape_t& sh, rc_dtype_t dtype, rc_scheme_t scheme,
       if (p->rank > sh.rows || p->rank > sh.cols) return RC_ERR_INVALID_ARG;
       if (sh.cols % 64) return RC_ERR_INVALID_ARG;
       return RC_OK;
+    case RC_BLOCKSEL: {
+      if (p->grid_w < 8 || p->grid_w % 8 || sh.rows % p->grid_w || (sh.rows / p->grid_w) % 8)
+        return RC_ERR_INVALID_ARG;
+      if (sh.cols % 4) return RC_ERR_INVALID_ARG;
+      const int64_t K = (int64_t)sh.rows / 64;
+      if (K > rc::kBsMaxBlocks) return RC_ERR_UNSUPPORTED;
+      if (p->keep_blocks < 1 || p->keep_blocks > K) return RC_ERR_INVALID_ARG;
+      return RC_OK;
+    }
   }
   return RC_ERR_INVALID_ARG;
 }
@@ -165,6 +183,27 @@ rc_status_t setup_lowrank(rc_plan* pl, const float* q0) {
   return RC_OK;
 }
 
+// Block selection: fp64 scores and the round state (cleared), per tensor.
+rc_status_t setup_blocksel(rc_plan* pl) {
+  const int64_t B = pl->shape.batch, K = (int64_t)pl->shape.rows / 64;
+  rc::BlockSel& S = pl->bs;
+  S.rows = pl->shape.rows;
+  S.cols = pl->shape.cols;
+  S.grid_w = pl->params.grid_w;
+  S.nblocks = (int)K;
+  S.keep = pl->params.keep_blocks;
+  S.L = pl->layout;
+  const int64_t score_bytes = align_up(B * K * 8 * 3 * 8);  // fp64 row partial sums
+  const int64_t total = score_bytes + align_up(B * K);
+  if (hipGetDevice(&pl->device) != hipSuccess) return RC_ERR_HIP;
+  if (hipMalloc(&pl->ws, (size_t)total) != hipSuccess) { pl->ws = nullptr; return RC_ERR_HIP; }
+  pl->ws_bytes = (size_t)total;
+  pl->bs_score = static_cast<double*>(pl->ws);
+  pl->bs_visited = static_cast<uint8_t*>(pl->ws) + score_bytes;
+  if (hipMemset(pl->bs_visited, 0, (size_t)(B * K)) != hipSuccess) return RC_ERR_HIP;
+  return RC_OK;
+}
+
 // The low-rank workspace seen from tensor b0 on (every piece is per tensor).
 rc::LowRankWork lr_slice(const rc::LowRankWork& w, const rc::Layout& L, int64_t b0) {
   const int64_t n = L.rows, m = L.cols, k = w.rank;
@@ -202,6 +241,11 @@ hipError_t compress_range(rc_plan* pl, hipStream_t stream, const void* a_t, cons
     case RC_LOWRANK:
       return rc::launch_lr_compress(bf16, a, ahat, e, pk, nb, pl->layout,
                                     b0 ? lr_slice(pl->lr, pl->layout, b0) : pl->lr, stream);
+    case RC_BLOCKSEL: {
+      const int64_t K = pl->bs.nblocks;
+      return rc::launch_bs_compress(bf16, a, ahat, e, pk, nb, pl->bs, pl->bs_score + b0 * K * 24,
+                                    pl->bs_visited + b0 * K, stream);
+    }
   }
   return hipErrorInvalidValue;
 }
@@ -224,6 +268,8 @@ hipError_t decompress_peers(rc_plan* pl, hipStream_t stream, const uint8_t* cons
       return rc::launch_nm_decompress(ps, pl->shape.batch, pl->layout, stream);
     case RC_LOWRANK:
       return rc::launch_lr_decompress(ps, pl->shape.batch, pl->layout, pl->lr, stream);
+    case RC_BLOCKSEL:
+      return rc::launch_bs_decompress(pl->dtype == RC_BF16, ps, pl->shape.batch, pl->bs, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -245,11 +291,15 @@ rc_status_t rc_plan_create(rc_shape_t shape, rc_dtype_t dtype, rc_scheme_t schem
   pl->scheme = scheme;
   pl->params = *params;
   pl->params.q0 = nullptr;
-  st = make_layout(shape, scheme, *params, &pl->layout);
+  st = make_layout(shape, dtype, scheme, *params, &pl->layout);
   if (st != RC_OK) { delete pl; return st; }
   pl->packed_bytes = (size_t)(pl->layout.tstride * shape.batch);
   if (scheme == RC_LOWRANK) {
     st = setup_lowrank(pl, params->q0);
+    if (st != RC_OK) { rc_plan_destroy(pl); return st; }
+  }
+  if (scheme == RC_BLOCKSEL) {
+    st = setup_blocksel(pl);
     if (st != RC_OK) { rc_plan_destroy(pl); return st; }
   }
   *out = pl;
@@ -316,6 +366,14 @@ rc_status_t rc_decompress_many(rc_plan_t pl, hipStream_t stream, const void* con
     packed[p] = static_cast<const uint8_t*>(packed_in[p]);
   }
   const hipError_t err = decompress_peers(pl, stream, packed, recon_states, npeers);
+  return err == hipSuccess ? RC_OK : RC_ERR_HIP;
+}
+
+rc_status_t rc_plan_reset_state(rc_plan_t pl, hipStream_t stream) {
+  if (!pl) return RC_ERR_INVALID_ARG;
+  if (pl->scheme != RC_BLOCKSEL) return RC_OK;
+  const hipError_t err =
+      rc::launch_bs_reset(pl->bs_visited, (int64_t)pl->shape.batch * pl->bs.nblocks, stream);
   return err == hipSuccess ? RC_OK : RC_ERR_HIP;
 }
 

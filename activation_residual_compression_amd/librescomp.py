@@ -21,11 +21,11 @@ LIB_PATH = os.path.join(_HERE, "lib", "librescomp.so")
 
 RC_OK, RC_ERR_INVALID_ARG, RC_ERR_UNSUPPORTED, RC_ERR_ALIGNMENT, RC_ERR_HIP = 0, 1, 2, 3, 4
 RC_BF16, RC_F32 = 0, 1
-RC_Q1, RC_Q2, RC_NM, RC_LOWRANK = 0, 1, 2, 3
+RC_Q1, RC_Q2, RC_NM, RC_LOWRANK, RC_BLOCKSEL = 0, 1, 2, 3, 4
 RC_MAX_PEERS = 8
 RC_LR_BF16_FACTORS = 1  # rc_params_t.flags, RC_LOWRANK only
 
-SCHEMES = {"q1": RC_Q1, "q2": RC_Q2, "nm": RC_NM, "lr": RC_LOWRANK}
+SCHEMES = {"q1": RC_Q1, "q2": RC_Q2, "nm": RC_NM, "lr": RC_LOWRANK, "bs": RC_BLOCKSEL}
 DTYPES = {"bf16": RC_BF16, "f32": RC_F32}
 
 
@@ -36,7 +36,8 @@ class rc_shape_t(ctypes.Structure):
 class rc_params_t(ctypes.Structure):
     _fields_ = [("group", ctypes.c_int32), ("nm_keep", ctypes.c_int32),
                 ("nm_block", ctypes.c_int32), ("rank", ctypes.c_int32),
-                ("iters", ctypes.c_int32), ("q0", ctypes.c_void_p), ("flags", ctypes.c_uint32)]
+                ("iters", ctypes.c_int32), ("q0", ctypes.c_void_p), ("flags", ctypes.c_uint32),
+                ("grid_w", ctypes.c_int32), ("keep_blocks", ctypes.c_int32)]
 
 
 class rc_state_t(ctypes.Structure):
@@ -70,6 +71,8 @@ def _load():
     lib.rc_decompress_many.argtypes = [vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int]
     lib.rc_plan_destroy.restype = st
     lib.rc_plan_destroy.argtypes = [vp]
+    lib.rc_plan_reset_state.restype = st
+    lib.rc_plan_reset_state.argtypes = [vp, vp]
     for f in ("rc_packed_bytes", "rc_tensor_packed_bytes", "rc_workspace_bytes"):
         getattr(lib, f).restype = sz
         getattr(lib, f).argtypes = [vp]
@@ -156,6 +159,10 @@ def rc_decompress_many(plan, stream, packed_in, recon_states):
     _check(_lib.rc_decompress_many(plan, _stream(stream), pk, rs, n), "rc_decompress_many")
 
 
+def rc_plan_reset_state(plan, stream):
+    _check(_lib.rc_plan_reset_state(plan, _stream(stream)), "rc_plan_reset_state")
+
+
 def rc_plan_destroy(plan):
     _check(_lib.rc_plan_destroy(plan), "rc_plan_destroy")
 
@@ -172,11 +179,12 @@ def rc_workspace_bytes(plan) -> int:
     return int(_lib.rc_workspace_bytes(plan))
 
 
-def make_params(scheme, *, group=0, nm_keep=0, nm_block=0, rank=0, iters=0, q0=None, flags=0):
+def make_params(scheme, *, group=0, nm_keep=0, nm_block=0, rank=0, iters=0, q0=None, flags=0,
+                grid_w=0, keep_blocks=0):
     """rc_params_t for a scheme; q0 (host fp32 [batch][cols][rank]) is referenced, not copied,
     so keep it alive until rc_plan_create returns."""
     p = rc_params_t(int(group), int(nm_keep), int(nm_block), int(rank), int(iters), _ptr(q0),
-                    int(flags))
+                    int(flags), int(grid_w), int(keep_blocks))
     p._q0_ref = q0
     return p
 
@@ -223,6 +231,9 @@ class Plan:
 
     def decompress_many(self, packed_in, recon_states, stream=None):
         rc_decompress_many(self.handle, stream, packed_in, recon_states)
+
+    def reset_state(self, stream=None):
+        rc_plan_reset_state(self.handle, stream)
 
     def lowrank_workspace(self):
         """Device pointers (R, P, Pbt, Qt, Q0t, Qtb, gpart, chol) and rows_pad (diagnostics)."""

@@ -87,9 +87,16 @@ def hbm_probe(n, log):
 
 
 def algorithmic_bytes(scheme, n_elem, in_bytes, group=None, rank=None, rows=None, cols=None, iters=None,
-                      batch=None):
+                      batch=None, keep=None):
     """Bytes each call must move at minimum (all tensors): compress and decompress."""
     N = n_elem
+    if scheme == "bs":
+        # score pass reads a, ahat and writes e everywhere; the sent fraction of the
+        # blocks is copied into the packed stream and written to ahat (and e = 0);
+        # the receiver reads the sent blocks and writes them into its state
+        frac = keep / (rows // 64)
+        return dict(compress=N * (in_bytes + 8) + N * frac * (2 * in_bytes + 8),
+                    decompress=N * frac * (in_bytes + 4))
     if scheme == "q1":
         meta = N / 8 + 4 * N / group
     elif scheme == "q2":
@@ -211,7 +218,8 @@ def measure(config, steps, warmup, max_frames, log, exchange_chunks=()):
         t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if wl.dtype == "bf16" else \
             torch.from_numpy(a)
         frames.append(t.to(dev))
-    kw = {k: spec[k] for k in ("group", "nm_keep", "nm_block", "rank", "iters") if k in spec}
+    kw = {k: spec[k] for k in ("group", "nm_keep", "nm_block", "rank", "iters", "grid_w", "keep_blocks")
+          if k in spec}
     if spec["scheme"] == "lr":
         kw["q0"] = wl.q0(spec["rank"])
     plan = rc.Plan((B, n, m), wl.dtype, spec["scheme"], **kw)
@@ -242,7 +250,8 @@ def measure(config, steps, warmup, max_frames, log, exchange_chunks=()):
     in_bytes = 2 if wl.dtype == "bf16" else 4
     N = B * n * m
     alg = algorithmic_bytes(spec["scheme"], N, in_bytes, group=spec.get("group"), rank=spec.get("rank"),
-                            rows=n, cols=m, iters=spec.get("iters"), batch=B)
+                            rows=n, cols=m, iters=spec.get("iters"), batch=B,
+                            keep=spec.get("keep_blocks"))
     out = dict(config=config, scheme=spec["scheme"], shape=[B, n, m], dtype=wl.dtype,
                frames=nframes, steps=steps, ms_per_step=ms_step, compress_ms=c_ms,
                decompress_ms=d_ms, input_GBps=N * in_bytes / (ms_step * 1e6),
@@ -320,7 +329,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="flux_q2")
-    ap.add_argument("--also", default="flux_nm,video_q1,flux_lr,video_lr",
+    ap.add_argument("--also", default="flux_nm,video_q1,flux_lr,video_lr,latent_bs",
                     help="other workloads to measure ('' for none)")
     ap.add_argument("--also-frames", type=int, default=4,
                     help="distinct input frames for the other workloads (cycled)")

@@ -61,6 +61,7 @@ typedef enum {
   RC_Q2 = 1,      /* 2-bit uniform levels + per-group fp32 (min, step)   */
   RC_NM = 2,      /* keep 2 of every 16, bf16 values + 4-bit indices     */
   RC_LOWRANK = 3, /* rank-k subspace iteration, INT4 factors             */
+  RC_BLOCKSEL = 4 /* Otil-style: the k most-changed 8x8-token blocks     */
 } rc_scheme_t;
 
 typedef struct {
@@ -78,6 +79,8 @@ typedef struct {
   const float* q0;  /* RC_LOWRANK: HOST fp32 [batch][cols][rank] start matrices;  */
                     /*   copied at plan creation and reused every step           */
   uint32_t flags;   /* 0, or RC_LOWRANK with RC_LR_BF16_FACTORS                   */
+  int32_t grid_w;      /* RC_BLOCKSEL: tokens per row of the spatial token grid     */
+  int32_t keep_blocks; /* RC_BLOCKSEL: blocks sent per tensor and step (k)          */
 } rc_params_t;
 
 /* rc_params_t.flags for RC_LOWRANK: send the factors as bf16 (round to nearest
@@ -92,6 +95,21 @@ typedef struct {
   float* ahat; /* sender's copy of the receiver reconstruction, fp32 [batch][rows][cols] */
   float* e;    /* error-feedback buffer, fp32 [batch][rows][cols] (written every step)  */
 } rc_state_t;
+
+/* RC_BLOCKSEL ("Otil: Accelerating Diffusion Model Inference via
+ * Communication-Efficient Multi-GPU Parallelism", Key designs 1-3): the rows of
+ * a tensor are tokens of a spatial grid with grid_w tokens per row (raster
+ * order); the grid is cut into 8 x 8-token blocks (all channels), numbered in
+ * raster order. Each step every block is scored by its cosine dissimilarity
+ * 1 - <a, ahat> / (|a| |ahat|) to the receiver's copy (the block as last sent;
+ * both zero -> 0, one zero -> 1), and the keep_blocks highest-scoring blocks
+ * among those not yet sent in the current round (ties to the lower index) are
+ * sent; the round restarts once every block has been sent, so every block is
+ * sent once per round. Sent blocks carry the a_t values (input dtype) and
+ * replace the receiver's copy: after the step ahat = a_t and e = 0 there, and
+ * e = a_t - ahat on the other blocks. The round state lives in the plan
+ * (rc_plan_reset_state clears it). Requirements: rows % (8 grid_w) == 0,
+ * grid_w % 8 == 0, cols % 4 == 0, 1 <= keep_blocks <= blocks <= 4096. */
 
 /* Validate the request and build a plan. For RC_LOWRANK this allocates the
  * device workspace (rc_workspace_bytes) on the current device and uploads q0.
@@ -143,6 +161,11 @@ rc_status_t rc_decompress(rc_plan_t plan, hipStream_t stream, const void* packed
 rc_status_t rc_decompress_many(rc_plan_t plan, hipStream_t stream, const void* const* packed_in,
                                float* const* recon_states, int npeers);
 
+/* Clear the state a plan keeps across steps (RC_BLOCKSEL: the round of sent
+ * blocks), for a new sequence; asynchronous on stream; no effect for the other
+ * schemes. */
+rc_status_t rc_plan_reset_state(rc_plan_t plan, hipStream_t stream);
+
 /* Free the plan and its workspace. Waits for nothing: the caller must make sure
  * no launched work still uses the plan. NULL is accepted. */
 rc_status_t rc_plan_destroy(rc_plan_t plan);
@@ -156,11 +179,14 @@ rc_status_t rc_plan_destroy(rc_plan_t plan);
  *   LR: U nibbles [rows*rank/2] | V nibbles [cols*rank/2] | sU f32 [rank] | sV f32 [rank]
  *       (row-major INT4, element t in nibble t, even t low, two's complement);
  *       with RC_LR_BF16_FACTORS: U bf16 [rows*rank] | V bf16 [cols*rank]
+ *   BLOCKSEL: u32 [1 + keep] (count, then the sent block indices ascending, unused
+ *       slots 0) | values [keep][64 tokens][cols] in the dtype of a_t (tokens of a
+ *       block in raster order; unused slots 0)
  * Returns 0 for a NULL plan. */
 size_t rc_packed_bytes(rc_plan_t plan);
 size_t rc_tensor_packed_bytes(rc_plan_t plan);
 
-/* Device workspace owned by the plan (0 unless RC_LOWRANK). */
+/* Device workspace owned by the plan (0 for Q1, Q2, NM). */
 size_t rc_workspace_bytes(rc_plan_t plan);
 
 /* Static description of a status code. */

@@ -394,7 +394,7 @@ def compress_tensor(scheme, a, ahat, *, group=None, rank=None, iters=None, q0=No
                 r=r)
 
 
-def bs_compress_tensor(a, ahat, *, grid_w, keep, visited, in_dtype="bf16"):
+def bs_compress_tensor(a, ahat, *, grid_w, keep, visited, in_dtype="bf16", selected=None):
     """One sender step of Otil-style block selection on one tensor.
 
     The selected blocks are sent as they are (values of a_t in the input dtype)

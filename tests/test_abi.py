@@ -135,3 +135,19 @@ def test_send_and_many_reject_bad_arguments_without_launching(rc):
                 rc.rc_decompress_many(p.handle, 0, packed, states)
             assert ei.value.status == status
     assert rc.RC_MAX_PEERS == 8
+
+
+def test_blocksel_validation_without_gpu(rc):
+    def status(shape, dtype="bf16", **kw):
+        with pytest.raises(rc.RcError) as ei:
+            rc.rc_plan_create(shape, dtype, "bs", rc.make_params("bs", **kw))
+        return ei.value.status
+
+    # 64 x 128-token grid, 320 channels: 128 blocks
+    assert status((1, 8192, 320), grid_w=12, keep_blocks=4) == rc.RC_ERR_INVALID_ARG    # grid_w % 8
+    assert status((1, 8192, 320), grid_w=96, keep_blocks=4) == rc.RC_ERR_INVALID_ARG    # rows % grid_w
+    assert status((1, 8192, 322), grid_w=128, keep_blocks=4) == rc.RC_ERR_INVALID_ARG   # cols % 4
+    assert status((1, 8192, 320), grid_w=128, keep_blocks=0) == rc.RC_ERR_INVALID_ARG
+    assert status((1, 8192, 320), grid_w=128, keep_blocks=129) == rc.RC_ERR_INVALID_ARG
+    assert status((1, 4096 * 64 + 64 * 64, 8), grid_w=64, keep_blocks=4) == rc.RC_ERR_UNSUPPORTED
+    assert status((1, 8192 + 64 * 8, 320), grid_w=128, keep_blocks=4) == rc.RC_ERR_INVALID_ARG  # rows/grid_w % 8
