@@ -265,6 +265,25 @@ def measure(config, steps, warmup, max_frames, log, exchange_chunks=()):
         out["tensors_per_ms"] = B / ms_step
         out["mfma_flops"] = fl
         out["mfma_util_whole_compress"] = fl / (c_ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    # the same step captured once in a HIP graph and replayed (launch gaps removed)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            plan.compress(seq[0], ahat, e, packed, cap)
+            plan.decompress(packed, recon, cap)
+    stream.wait_stream(cap)
+    for _ in range(2):
+        g.replay()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    out["graph_ms_per_step"] = g0.elapsed_time(g1) / steps
+    del g
     if exchange_chunks:
         out["exchange"] = exchange_timing(plan, seq, ahat, e, packed, exchange_chunks)
         log("[bench] %s exchange: %s" % (config, json.dumps(out["exchange"])))
@@ -375,14 +394,16 @@ def main():
     ceiling = None if args.no_hbm_probe else hbm_probe(_wl.batch * _wl.n * _wl.m, log)
     main_res = measure(args.workload, args.steps, args.warmup, 64, log,
                        exchange_chunks=() if args.no_exchange else (4, 8, 19))
-    log("[bench] %s: %.3f ms/step, %.1f GB/s input, compress %.3f ms (%.0f GB/s alg)" % (
-        args.workload, main_res["ms_per_step"], main_res["input_GBps"], main_res["compress_ms"],
-        main_res["compress_GBps"]))
+    log("[bench] %s: %.3f ms/step, %.1f GB/s input, compress %.3f ms (%.0f GB/s alg), "
+        "graph replay %.3f ms/step" % (args.workload, main_res["ms_per_step"], main_res["input_GBps"],
+                                       main_res["compress_ms"], main_res["compress_GBps"],
+                                       main_res["graph_ms_per_step"]))
     others = {}
     for cfg in [c for c in args.also.split(",") if c and c != args.workload]:
         r = measure(cfg, args.steps, args.warmup, args.also_frames, log,
                     exchange_chunks=(8, 19) if (cfg == "flux_lr" and not args.no_exchange) else ())
-        log("[bench] %s: %.3f ms/step, %.1f GB/s input" % (cfg, r["ms_per_step"], r["input_GBps"]))
+        log("[bench] %s: %.3f ms/step, %.1f GB/s input (graph replay %.3f ms/step)" % (
+            cfg, r["ms_per_step"], r["input_GBps"], r["graph_ms_per_step"]))
         others[cfg] = r
 
     cpu = None
