@@ -411,9 +411,15 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
   constexpr int PCH = K * 4;  // 16-byte chunks of a [K x 32] bf16 P^T block
   __shared__ __attribute__((aligned(16))) uint16_t sR[2][32 * kRtpLd];
   __shared__ __attribute__((aligned(16))) uint16_t sP[2][K * kRtpPld];
-  const int b = blockIdx.z, split = blockIdx.y, c0 = blockIdx.x * kRtpCols;
+  // Tensors and row splits in reverse launch order: the R*Q pass before this one
+  // read R forwards, so its last tensors are still in the device's last-level
+  // cache when this pass starts (and the next forward pass finds this pass's).
+  const int b = gridDim.z - 1 - blockIdx.z, split = gridDim.y - 1 - blockIdx.y;
+  const int c0 = blockIdx.x * kRtpCols;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
-  const int ld_row = threadIdx.x >> 3, ld_col = (threadIdx.x & 7) * 16;
+  // R staging: each wave-wide load covers 4 whole 256-byte row pieces (16 lanes
+  // x 16 bytes per row); loads q = 0, 1 take rows ld_row and ld_row + 16
+  const int ld_row = threadIdx.x >> 4, ld_col = (threadIdx.x & 15) * 8;
   const bool col_ok = c0 + ld_col < m;
   const int i_begin = split * split_rows;
   const int i_end = min(rows_pad, i_begin + split_rows);
@@ -424,12 +430,12 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
   struct Stage { u32x4 r0, r1, p; };
   auto gload = [&](int i0) {
     Stage st;
-    int row = i0 + ld_row;
-    row = row < n ? row : n - 1;
+    const int row0 = min(i0 + ld_row, n - 1), row1 = min(i0 + ld_row + 16, n - 1);
     const u32x4 z = {0u, 0u, 0u, 0u};
-    const u32x4* src = reinterpret_cast<const u32x4*>(Rb + (size_t)row * m + c0 + ld_col);
-    st.r0 = col_ok ? src[0] : z;
-    st.r1 = col_ok ? src[1] : z;
+    const size_t col = (size_t)c0 + (col_ok ? ld_col : 0);
+    st.r0 = *reinterpret_cast<const u32x4*>(Rb + (size_t)row0 * m + col);
+    st.r1 = *reinterpret_cast<const u32x4*>(Rb + (size_t)row1 * m + col);
+    if (!col_ok) st.r0 = st.r1 = z;
     st.p = z;
     if (threadIdx.x < PCH) {
       const int j = threadIdx.x >> 2, q = threadIdx.x & 3;
@@ -446,9 +452,8 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
   Stage next = gload(i_begin);
   int buf = 0;
   for (int i0 = i_begin; i0 < i_end; i0 += 32, buf ^= 1) {
-    u32x4* dr = reinterpret_cast<u32x4*>(&sR[buf][ld_row * kRtpLd + ld_col]);
-    dr[0] = next.r0;
-    dr[1] = next.r1;
+    *reinterpret_cast<u32x4*>(&sR[buf][ld_row * kRtpLd + ld_col]) = next.r0;
+    *reinterpret_cast<u32x4*>(&sR[buf][(ld_row + 16) * kRtpLd + ld_col]) = next.r1;
     if (threadIdx.x < PCH)
       *reinterpret_cast<u32x4*>(&sP[buf][(threadIdx.x >> 2) * kRtpPld + 8 * (threadIdx.x & 3)]) = next.p;
     __syncthreads();
