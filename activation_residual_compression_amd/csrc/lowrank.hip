@@ -182,13 +182,18 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
 #pragma unroll
     for (int g = 0; g < NT; ++g) acc[f][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // R alone (2 B per element) is prefetched a step ahead; a_t and ahat (6 B per
+  // element) are loaded at the top of their own step, which keeps the register
+  // count low enough for more resident waves to cover the latency instead.
   Stage S;
-  gload(0, S);
+  if constexpr (!FROM_A) gload(0, S);
   for (int c0 = 0; c0 < m; c0 += kRqStep) {
+    if constexpr (FROM_A) gload(c0, S);
     __syncthreads();  // the previous tile has been read
     put(c0, S);
     __syncthreads();
-    if (c0 + kRqStep < m) gload(c0 + kRqStep, S);
+    if constexpr (!FROM_A)
+      if (c0 + kRqStep < m) gload(c0 + kRqStep, S);
     const int kc = c0 + 32 * w;
     if (kc < m) {
       u32x4 B[NT];
