@@ -273,12 +273,13 @@ __global__ __launch_bounds__(256) void lr_gram_reduce_kernel(const float* __rest
 }
 
 // ---------------------------------------------------------------- Cholesky
-// One wave per tensor, everything in registers: lane i holds row i of G (from
-// the upper triangle of gsum) and builds row i of L by the left-looking
-// recurrence; row j of L is read from lane j with v_readlane. Dead columns
-// (pivot <= 2^-23 * max(trace G, K * FLT_MIN)) get L[j][j] = 1 and a zero
-// column below the diagonal. Then lane c solves L y = e_c, giving column c of
-// L^{-1}; rows of dead columns are zeroed, so x = L^{-1} p has x_j = 0 there
+// One wave per tensor: lane i holds row i of G (from the upper triangle of
+// gsum) and builds row i of L by the left-looking recurrence. Each finished
+// column of L goes to LDS, so row j of L (needed by every lane at step j) is
+// read back as uniform-address broadcasts, four entries per LDS read. Dead
+// columns (pivot <= 2^-23 * max(trace G, K * FLT_MIN)) get L[j][j] = 1 and a
+// zero column below the diagonal. Then lane c solves L y = e_c, giving column c
+// of L^{-1}; rows of dead columns are zeroed, so x = L^{-1} p has x_j = 0 there
 // and the other entries are those of the forward substitution.
 __device__ __forceinline__ float lane_f32(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
@@ -287,6 +288,8 @@ __device__ __forceinline__ float lane_f32(float v, int lane) {
 template <int K>
 __global__ __launch_bounds__(64) void lr_chol_kernel(const float* __restrict__ gsum,
                                                      float* __restrict__ linv) {
+  constexpr int LDc = K + 4;  // 16-B aligned rows of L in LDS
+  __shared__ __attribute__((aligned(16))) float Ls[K * LDc];
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const float* gs = gsum + (size_t)b * K * K;
@@ -304,22 +307,36 @@ __global__ __launch_bounds__(64) void lr_chol_kernel(const float* __restrict__ g
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     float s = g[j];
+    const f32x4* Lj = reinterpret_cast<const f32x4*>(Ls + j * LDc);
 #pragma unroll
-    for (int p = 0; p < j; ++p) s -= L[p] * lane_f32(L[p], j);
+    for (int q = 0; q < (j + 3) / 4; ++q) {
+      const f32x4 v = Lj[q];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (4 * q + t < j) s -= L[4 * q + t] * v[t];
+    }
     const float piv = lane_f32(s, j);
     const bool dj = !(piv > tol);
     const float ljj = dj ? 1.0f : sqrtf(piv);
     L[j] = lane == j ? ljj : (lane > j && !dj ? s / ljj : 0.f);
     if (dj) dead |= (uint64_t)1 << j;
+    if (lane < K) Ls[lane * LDc + j] = L[j];
+    __syncthreads();
   }
   // column `lane` of L^{-1}
   float y[K];
 #pragma unroll
   for (int i = 0; i < K; ++i) {
     float s = (i == lane) ? 1.f : 0.f;
+    const f32x4* Li = reinterpret_cast<const f32x4*>(Ls + i * LDc);
 #pragma unroll
-    for (int q = 0; q < i; ++q) s -= lane_f32(L[q], i) * y[q];
-    y[i] = ((dead >> i) & 1) ? 0.f : s / lane_f32(L[i], i);
+    for (int q = 0; q < (i + 3) / 4; ++q) {
+      const f32x4 v = Li[q];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (4 * q + t < i) s -= v[t] * y[4 * q + t];
+    }
+    y[i] = ((dead >> i) & 1) ? 0.f : s / Ls[i * LDc + i];
   }
   if (lane < K) {
     float* out = linv + (size_t)b * K * K + lane;
@@ -329,69 +346,100 @@ __global__ __launch_bounds__(64) void lr_chol_kernel(const float* __restrict__ g
 }
 
 // ---------------------------------------------------------------- P <- P L^-T
-// One wave per 64-row tile: X = T L^{-T} with fp32 MFMA (T = the tile of P).
+// One 64-row tile per block of 4 waves: X = T L^{-T} with fp32 MFMA (T = the
+// tile of P), wave w producing rows 16w .. 16w+15. All global loads (L^{-1}
+// and the tile) are issued before the first LDS store. A wave reads only its
+// own 16 rows of T, so it writes X over them in place.
 // GRAM: also write the Gram partial of the solved tile (next CQR pass).
 // FINAL: also write the bf16 transposed panel used by the R^T P product
 // (rows n .. rows_pad-1 written as 0) and fold the column absmax of the tile
 // into amax[b][0][*] (the INT4 scales of U).
 template <int K, bool GRAM, bool FINAL>
-__global__ __launch_bounds__(64) void lr_solve_kernel(float* __restrict__ P,
-                                                      const float* __restrict__ linv,
-                                                      float* __restrict__ gpart,
-                                                      uint16_t* __restrict__ Pbt,
-                                                      uint32_t* __restrict__ amax, int n,
-                                                      int ntiles, int rows_pad) {
+__global__ __launch_bounds__(256) void lr_solve_kernel(float* __restrict__ P,
+                                                       const float* __restrict__ linv,
+                                                       float* __restrict__ gpart,
+                                                       uint16_t* __restrict__ Pbt,
+                                                       uint32_t* __restrict__ amax, int n,
+                                                       int ntiles, int rows_pad) {
   constexpr int NT = K / 16;
-  constexpr int LD = K + 1;
-  __shared__ float Li[K * LD];
-  __shared__ float T[kTile * LD];
-  __shared__ float X[kTile * LD];
+  constexpr int LD = K + 4;  // 16-B aligned rows; MFMA operand reads hit 64 distinct banks
+  constexpr int V4 = K / 4;  // f32x4 per row
+  constexpr int LI_IT = (K * V4 + 255) / 256;
+  constexpr int T_IT = kTile * V4 / 256;
+  static_assert(kTile * V4 % 256 == 0, "tile must split evenly over the block");
+  __shared__ __attribute__((aligned(16))) float Li[K * LD];
+  __shared__ __attribute__((aligned(16))) float T[kTile * LD];
   const int b = blockIdx.y, tile = blockIdx.x, row0 = tile * kTile;
-  const int lane = threadIdx.x, lr = lane & 15, lk = lane >> 4;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lk = lane >> 4;
   const float* li = linv + (size_t)b * K * K;
-  for (int idx = lane; idx < K * K; idx += 64) Li[(idx / K) * LD + idx % K] = li[idx];
   float* Pb = P + (size_t)b * n * K;
-  for (int idx = lane; idx < kTile * K / 4; idx += 64) {
-    const int r = (4 * idx) / K, j = (4 * idx) % K;
-    const f32x4 v = (row0 + r < n) ? *reinterpret_cast<const f32x4*>(Pb + (size_t)(row0 + r) * K + j)
-                                   : f32x4{0.f, 0.f, 0.f, 0.f};
-    T[r * LD + j] = v.x; T[r * LD + j + 1] = v.y; T[r * LD + j + 2] = v.z; T[r * LD + j + 3] = v.w;
+  f32x4 lv[LI_IT], tv[T_IT];
+#pragma unroll
+  for (int i = 0; i < LI_IT; ++i) {
+    const int idx = tid + 256 * i;
+    lv[i] = idx < K * V4 ? *reinterpret_cast<const f32x4*>(li + 4 * idx) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int i = 0; i < T_IT; ++i) {
+    const int idx = tid + 256 * i, r = idx / V4, j = 4 * (idx % V4);
+    tv[i] = row0 + r < n ? *reinterpret_cast<const f32x4*>(Pb + (size_t)(row0 + r) * K + j)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int i = 0; i < LI_IT; ++i) {
+    const int idx = tid + 256 * i;
+    if (idx < K * V4) *reinterpret_cast<f32x4*>(Li + (idx / V4) * LD + 4 * (idx % V4)) = lv[i];
+  }
+#pragma unroll
+  for (int i = 0; i < T_IT; ++i) {
+    const int idx = tid + 256 * i;
+    *reinterpret_cast<f32x4*>(T + (idx / V4) * LD + 4 * (idx % V4)) = tv[i];
   }
   __syncthreads();
   // X[r][i] = sum_c T[r][c] Linv[i][c]: A = T (rows r), B[c][i] = Linv[i][c]
+  f32x4 acc[NT];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int it = 0; it < NT; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float* Tw = T + 16 * w * LD;
 #pragma unroll
-    for (int it = 0; it < NT; ++it) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < K; k0 += 4) {
+    const float a = Tw[lr * LD + k0 + lk];
 #pragma unroll
-      for (int k0 = 0; k0 < K; k0 += 4)
-        acc = mfma_f32(T[(16 * rt + lr) * LD + k0 + lk], Li[(16 * it + lr) * LD + k0 + lk], acc);
+    for (int it = 0; it < NT; ++it) acc[it] = mfma_f32(a, Li[(16 * it + lr) * LD + k0 + lk], acc[it]);
+  }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) X[(16 * rt + 4 * lk + t) * LD + 16 * it + lr] = acc[t];
-    }
+  for (int it = 0; it < NT; ++it)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) Tw[(4 * lk + t) * LD + 16 * it + lr] = acc[it][t];
   __syncthreads();
-  for (int idx = lane; idx < kTile * K / 4; idx += 64) {
-    const int r = (4 * idx) / K, j = (4 * idx) % K;
+#pragma unroll
+  for (int i = 0; i < T_IT; ++i) {
+    const int idx = tid + 256 * i, r = idx / V4, j = 4 * (idx % V4);
     if (row0 + r < n)
       *reinterpret_cast<f32x4*>(Pb + (size_t)(row0 + r) * K + j) =
-          f32x4{X[r * LD + j], X[r * LD + j + 1], X[r * LD + j + 2], X[r * LD + j + 3]};
+          *reinterpret_cast<const f32x4*>(T + r * LD + j);
   }
   if constexpr (FINAL) {
-    // lane = row of the tile; rows past n are zero in X
+    // lane = row of the tile (rows past n are zero in X); wave w writes
+    // columns w, w + 4, ...
     const int row = row0 + lane;
-    if (row < rows_pad) {
-      uint16_t* dst = Pbt + (size_t)b * K * rows_pad + row;
+    uint16_t* dst = Pbt + (size_t)b * K * rows_pad + row;
 #pragma unroll
-      for (int j = 0; j < K; ++j) dst[(size_t)j * rows_pad] = (uint16_t)bf16_rne(X[lane * LD + j]);
-    }
+    for (int j = w; j < K; j += 4) dst[(size_t)j * rows_pad] = (uint16_t)bf16_rne(T[lane * LD + j]);
+    __shared__ float cm[4 * K];
     if (lane < K) {
       float mx = 0.f;
-      for (int r = 0; r < kTile; ++r) mx = fmaxf(mx, fabsf(X[r * LD + lane]));
-      atomicMax(amax + (size_t)b * 2 * K + lane, __float_as_uint(mx));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(Tw[r * LD + lane]));
+      cm[w * K + lane] = mx;
+    }
+    __syncthreads();
+    if (tid < K) {
+      const float mx = fmaxf(fmaxf(cm[tid], cm[K + tid]), fmaxf(cm[2 * K + tid], cm[3 * K + tid]));
+      atomicMax(amax + (size_t)b * 2 * K + tid, __float_as_uint(mx));
     }
   }
-  if constexpr (GRAM) tile_gram<K, LD>(X, gpart + ((size_t)b * ntiles + tile) * K * K, 1);
+  if constexpr (GRAM) tile_gram<K, LD>(T, gpart + ((size_t)b * ntiles + tile) * K * K, 4);
 }
 
 // ---------------------------------------------------------------- Q = R^T P
@@ -777,10 +825,10 @@ void cqr_pass(const LowRankWork& w, int n, int B, bool final_pass, hipStream_t s
                      w.gpart, w.gsum, nt);
   hipLaunchKernelGGL((lr_chol_kernel<K>), dim3(B), dim3(64), 0, s, w.gsum, w.linv);
   if (final_pass)
-    hipLaunchKernelGGL((lr_solve_kernel<K, false, true>), dim3(nt, B), dim3(64), 0, s, w.P, w.linv,
+    hipLaunchKernelGGL((lr_solve_kernel<K, false, true>), dim3(nt, B), dim3(256), 0, s, w.P, w.linv,
                        w.gpart, w.Pbt, w.amax, n, nt, rp);
   else
-    hipLaunchKernelGGL((lr_solve_kernel<K, true, false>), dim3(nt, B), dim3(64), 0, s, w.P, w.linv,
+    hipLaunchKernelGGL((lr_solve_kernel<K, true, false>), dim3(nt, B), dim3(256), 0, s, w.P, w.linv,
                        w.gpart, w.Pbt, w.amax, n, nt, rp);
 }
 

@@ -193,7 +193,11 @@ def exchange_timing(plan, seq, ahat, e, packed, chunks, reps=5):
     return out
 
 
-def measure(config, steps, warmup, max_frames, log, exchange_chunks=()):
+def _ms(x):
+    return "-" if x is None else "%.3f" % x
+
+
+def measure(config, steps, warmup, max_frames, log, exchange_chunks=(), overlap=True):
     import numpy as np
     import torch
 
@@ -265,6 +269,33 @@ def measure(config, steps, warmup, max_frames, log, exchange_chunks=()):
         out["tensors_per_ms"] = B / ms_step
         out["mfma_flops"] = fl
         out["mfma_util_whole_compress"] = fl / (c_ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    # Steady state of one GPU in a sequence-parallel group: its own compress of
+    # step t+1 (stream) runs while the receiver decodes step t (second stream);
+    # the two touch disjoint state, so only the packed buffer is double-buffered.
+    out["overlapped_ms_per_step"] = None
+    if overlap:
+        s2 = torch.cuda.Stream()
+        packed2 = torch.empty_like(packed)
+        bufs = (packed, packed2)
+        done_c = [torch.cuda.Event() for _ in range(2)]
+        done_d = [torch.cuda.Event() for _ in range(2)]
+        for ev in done_d:
+            ev.record(stream)
+        o0, o1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        o0.record(stream)
+        for i in range(steps):
+            k = i & 1
+            stream.wait_event(done_d[k])          # the decode that read this buffer is done
+            plan.compress(seq[warmup + i], ahat, e, bufs[k], stream)
+            done_c[k].record(stream)
+            s2.wait_event(done_c[k])
+            plan.decompress(bufs[k], recon, s2)
+            done_d[k].record(s2)
+        stream.wait_stream(s2)
+        o1.record(stream)
+        torch.cuda.synchronize()
+        out["overlapped_ms_per_step"] = o0.elapsed_time(o1) / steps
     # the same step captured once in a HIP graph and replayed (launch gaps removed)
     g = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
@@ -337,7 +368,16 @@ def cpu_baseline(config, budget_s, log):
                 break
     in_bytes = 2 if wl.dtype == "bf16" else 4
     gbps = done * wl.n * wl.m * in_bytes / elapsed / 1e9
-    return dict(value=gbps, unit="GB/s", cores=1, kind="oracle",
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return dict(value=gbps, unit="GB/s", cores=1, kind="oracle", cpu_model=model,
+                host_cpus=os.cpu_count(),
                 sample="%s: %d tensor-steps of %dx%d (tensors 0-23, steps 1-%d), compress+decompress, "
                        "%.1f s single-threaded" % (config, done, wl.n, wl.m, t, elapsed))
 
@@ -356,7 +396,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-probe", action="store_true")
     ap.add_argument("--no-exchange", action="store_true",
-                    help="skip the compress + hand-off pipeline timing")
+                    help="skip the compress + hand-off pipeline timing and the two-stream "
+                         "compress/decode overlap (both run kernels concurrently)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -393,17 +434,20 @@ def main():
     _wl = _synth.make(args.workload, tensors=[0])
     ceiling = None if args.no_hbm_probe else hbm_probe(_wl.batch * _wl.n * _wl.m, log)
     main_res = measure(args.workload, args.steps, args.warmup, 64, log,
-                       exchange_chunks=() if args.no_exchange else (4, 8, 19))
+                       exchange_chunks=() if args.no_exchange else (4, 8, 19),
+                       overlap=not args.no_exchange)
     log("[bench] %s: %.3f ms/step, %.1f GB/s input, compress %.3f ms (%.0f GB/s alg), "
-        "graph replay %.3f ms/step" % (args.workload, main_res["ms_per_step"], main_res["input_GBps"],
-                                       main_res["compress_ms"], main_res["compress_GBps"],
-                                       main_res["graph_ms_per_step"]))
+        "graph replay %.3f ms/step, compress/decode overlapped %s ms/step" % (
+            args.workload, main_res["ms_per_step"], main_res["input_GBps"], main_res["compress_ms"],
+            main_res["compress_GBps"], main_res["graph_ms_per_step"], _ms(main_res["overlapped_ms_per_step"])))
     others = {}
     for cfg in [c for c in args.also.split(",") if c and c != args.workload]:
         r = measure(cfg, args.steps, args.warmup, args.also_frames, log,
-                    exchange_chunks=(8, 19) if (cfg == "flux_lr" and not args.no_exchange) else ())
-        log("[bench] %s: %.3f ms/step, %.1f GB/s input (graph replay %.3f ms/step)" % (
-            cfg, r["ms_per_step"], r["input_GBps"], r["graph_ms_per_step"]))
+                    exchange_chunks=(8, 19) if (cfg == "flux_lr" and not args.no_exchange) else (),
+                    overlap=not args.no_exchange)
+        log("[bench] %s: %.3f ms/step, %.1f GB/s input (graph replay %.3f, compress/decode "
+            "overlapped %s ms/step)" % (cfg, r["ms_per_step"], r["input_GBps"],
+                                       r["graph_ms_per_step"], _ms(r["overlapped_ms_per_step"])))
         others[cfg] = r
 
     cpu = None
