@@ -92,6 +92,28 @@ __device__ __forceinline__ u32x4 pack_r(const F8& x, const F8& h) {
   return v;
 }
 
+// The device hands workgroup L (linear over the grid, x fastest) to XCD L % 8,
+// and each XCD has its own L2. This returns a logical index for L such that
+// every XCD runs one contiguous range of logical indices, so logical neighbours
+// (the blocks of one tensor, which read the same small operand) share an L2.
+// A bijection on [0, N): XCD x holds q + (x < r) blocks, q = N / 8, r = N % 8.
+__device__ __forceinline__ int xcd_contiguous(int L, int N) {
+  const int x = L & 7, i = L >> 3, q = N >> 3, r = N & 7;
+  return x * q + min(x, r) + i;
+}
+
+// R, the bf16 residual the products share, lives in the library's own
+// workspace in 32 x 128 tiles, each a contiguous 8 KiB row-major block, so that
+// every staged piece of it (a 32-row slice of a 128-column step) is one
+// contiguous run whichever way a product walks it. Tiles are ordered
+// row-tile-major; a tensor spans rows_pad x (128 * ceil(cols / 128)) elements.
+__device__ __forceinline__ size_t r_index(int row, int col, int ncb) {
+  return ((size_t)((row >> 5) * ncb + (col >> 7)) << 12) + (size_t)((row & 31) << 7) + (col & 127);
+}
+__device__ __forceinline__ size_t r_tensor_elems(int rows_pad, int m) {
+  return (size_t)rows_pad * (size_t)(((m + 127) >> 7) << 7);
+}
+
 // ---------------------------------------------------------------- P = R * Q
 // Block: 64 rows of one tensor, walked in steps of 128 columns. Each step's
 // 64 x 128 bf16 tile of R is staged in LDS: wave w loads rows 16w .. 16w+15,
@@ -104,7 +126,7 @@ __device__ __forceinline__ u32x4 pack_r(const F8& x, const F8& h) {
 // memory (each B operand serves the 4 row fragments). The four waves' partial
 // tiles are summed through LDS as (w0 + w2) + (w1 + w3).
 // FROM_A: R = bf16(a_t - ahat) is formed while staging and written out for the
-// later passes. Block (0, b) clears the tensor's INT4 absmax slots, which the
+// later passes. The block of tile 0 clears the tensor's INT4 absmax slots, which the
 // last solve and the last Q sum of the iteration fill.
 constexpr int kRqStep = 128;        // columns per step
 constexpr int kRqLd = kRqStep + 8;  // bf16 per staged row (272 B)
@@ -125,7 +147,8 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
   uint16_t* sR = reinterpret_cast<uint16_t*>(lds);
   float* red0 = lds;
   float* red1 = lds + kTile * LD;
-  const int b = blockIdx.y, tile = blockIdx.x, row0 = tile * kTile;
+  const int lin = xcd_contiguous(blockIdx.x + ntiles * blockIdx.y, ntiles * gridDim.y);
+  const int b = lin / ntiles, tile = lin % ntiles, row0 = tile * kTile;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
   const uint16_t* Qb = Qtb + (size_t)b * K * m;
   if (tile == 0 && threadIdx.x < 2 * K) amax[(size_t)b * 2 * K + threadIdx.x] = 0u;
@@ -138,20 +161,27 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
     u32x2 r[8];  // otherwise: R
   };
   const int srow = 16 * w + (lane >> 5), scol = 4 * (lane & 31);
-  // element offset of staged row i within the tensor (rows past n reread row n-1)
+  // offsets of staged row i in a_t / ahat (row-major) and in R (tiled); rows
+  // past n reread row n-1
+  const int ncb = (m + 127) >> 7;
+  uint16_t* Rb = R + (size_t)b * r_tensor_elems(kTile * ntiles, m);
   auto soff = [&](int c0, int i) -> size_t {
     const int row = min(row0 + srow + 2 * i, n - 1);
     return ((size_t)b * n + row) * m + (c0 + scol < m ? c0 + scol : 0);
   };
+  auto roff = [&](int c0, int i) -> size_t {
+    const int row = min(row0 + srow + 2 * i, n - 1);
+    return r_index(row, c0 + scol < m ? c0 + scol : 0, ncb);
+  };
   auto gload = [&](int c0, Stage& S) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const size_t off = soff(c0, i);
       if constexpr (FROM_A) {
+        const size_t off = soff(c0, i);
         S.x[i] = __builtin_nontemporal_load(reinterpret_cast<const Raw*>(a + off));
         S.h[i] = load4<float>(ahat + off);
       } else {
-        S.r[i] = *reinterpret_cast<const u32x2*>(R + off);
+        S.r[i] = *reinterpret_cast<const u32x2*>(Rb + roff(c0, i));
       }
     }
   };
@@ -168,10 +198,11 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
           x = S.x[i];
         v.x = bf16_rne(x[0] - S.h[i][0]) | (bf16_rne(x[1] - S.h[i][1]) << 16);
         v.y = bf16_rne(x[2] - S.h[i][2]) | (bf16_rne(x[3] - S.h[i][3]) << 16);
-        if (col_ok && row0 + srow + 2 * i < n) *reinterpret_cast<u32x2*>(R + soff(c0, i)) = v;
+        if (col_ok && row0 + srow + 2 * i < n) *reinterpret_cast<u32x2*>(Rb + roff(c0, i)) = v;
       } else {
         v = S.r[i];
       }
+      if (!col_ok) v = u32x2{0u, 0u};  // columns past m multiply as zeros
       *reinterpret_cast<u32x2*>(&sR[(srow + 2 * i) * kRqLd + scol]) = v;
     }
   };
@@ -185,29 +216,44 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
   // R alone (2 B per element) is prefetched a step ahead; a_t and ahat (6 B per
   // element) are loaded at the top of their own step, which keeps the register
   // count low enough for more resident waves to cover the latency instead.
+  // The Q^T operands of a step are loaded before any later load is issued, and
+  // neither is behind a branch: waits on loads complete in issue order, so the
+  // MFMAs then wait for Q^T alone, not for the prefetch behind it. (A wave
+  // whose columns lie past m reads column 0 of Q^T against staged zeros.)
+  auto bload = [&](int c0, u32x4 (&B)[NT]) {
+    const int kc = c0 + 32 * w < m ? c0 + 32 * w : 0;
+#pragma unroll
+    for (int g = 0; g < NT; ++g)
+      B[g] = *reinterpret_cast<const u32x4*>(Qb + (size_t)(16 * g + lr) * m + kc + 8 * lk);
+  };
   Stage S;
-  if constexpr (!FROM_A) gload(0, S);
-  for (int c0 = 0; c0 < m; c0 += kRqStep) {
-    if constexpr (FROM_A) gload(c0, S);
+  auto step = [&](int c0, auto prefetch) {
+    u32x4 B[NT];
+    if constexpr (FROM_A) {
+      bload(c0, B);
+      __builtin_amdgcn_sched_barrier(0);  // keep the Q^T loads first
+      gload(c0, S);
+    }
     __syncthreads();  // the previous tile has been read
     put(c0, S);
     __syncthreads();
-    if constexpr (!FROM_A)
-      if (c0 + kRqStep < m) gload(c0 + kRqStep, S);
-    const int kc = c0 + 32 * w;
-    if (kc < m) {
-      u32x4 B[NT];
-#pragma unroll
-      for (int g = 0; g < NT; ++g)
-        B[g] = *reinterpret_cast<const u32x4*>(Qb + (size_t)(16 * g + lr) * m + kc + 8 * lk);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const u32x4 A = *reinterpret_cast<const u32x4*>(&sR[(16 * f + lr) * kRqLd + 32 * w + 8 * lk]);
-#pragma unroll
-        for (int g = 0; g < NT; ++g) acc[f][g] = mfma_bf16(A, B[g], acc[f][g]);
-      }
+    if constexpr (!FROM_A) {
+      bload(c0, B);
+      __builtin_amdgcn_sched_barrier(0);  // keep the Q^T loads first
+      if constexpr (decltype(prefetch)::value) gload(c0 + kRqStep, S);
+      __builtin_amdgcn_sched_barrier(0);  // and the prefetch before the MFMAs
     }
-  }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const u32x4 A = *reinterpret_cast<const u32x4*>(&sR[(16 * f + lr) * kRqLd + 32 * w + 8 * lk]);
+#pragma unroll
+      for (int g = 0; g < NT; ++g) acc[f][g] = mfma_bf16(A, B[g], acc[f][g]);
+    }
+  };
+  if constexpr (!FROM_A) gload(0, S);
+  int c0 = 0;
+  for (; c0 + kRqStep < m; c0 += kRqStep) step(c0, std::true_type{});
+  step(c0, std::false_type{});
 
   // (w0 + w2) + (w1 + w3), rows past n zeroed, tile kept in red1
   auto store_acc = [&](float* dst) {
@@ -450,7 +496,8 @@ __global__ __launch_bounds__(256) void lr_solve_kernel(float* __restrict__ P,
 // ds_read_b64_tr_b16 (A[c][i] = R[i][c]); each P^T fragment read from LDS
 // feeds both column tiles of the wave. The split's partial Q^T goes to qpart;
 // lr_qfinish_kernel sums the splits. A last block of 64 columns (cols % 128 ==
-// 64) zero-fills the missing half and stores only valid columns.
+// 64) computes its missing half from reread valid columns and stores only the
+// valid ones.
 constexpr int kRtpCols = 128;
 constexpr int kRtpLd = kRtpCols + 8;  // bf16 per staged R row (272 B)
 constexpr int kRtpPld = 32 + 8;       // bf16 per staged P^T row (80 B)
@@ -464,11 +511,19 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
   constexpr int PCH = K * 4;  // 16-byte chunks of a [K x 32] bf16 P^T block
   __shared__ __attribute__((aligned(16))) uint16_t sR[2][32 * kRtpLd];
   __shared__ __attribute__((aligned(16))) uint16_t sP[2][K * kRtpPld];
-  // Tensors and row splits in reverse launch order: the R*Q pass before this one
-  // read R forwards, so its last tensors are still in the device's last-level
-  // cache when this pass starts (and the next forward pass finds this pass's).
-  const int b = gridDim.z - 1 - blockIdx.z, split = gridDim.y - 1 - blockIdx.y;
-  const int c0 = blockIdx.x * kRtpCols;
+  // Logical blocks (column block fastest, then split, then tensor) are spread
+  // over the XCDs in contiguous ranges, so the column blocks that share a P^T
+  // chunk share an L2. Tensors and row splits are taken in the reverse of that
+  // order: every XCD's range of the R*Q pass before this one ran forwards, so
+  // the tensors this pass starts with are the ones that pass read last and are
+  // still in the device's last-level cache (the next forward pass finds this
+  // pass's in turn).
+  const int nblk = gridDim.x * gridDim.y * gridDim.z;
+  int lin = xcd_contiguous(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), nblk);
+  const int cb = lin % gridDim.x;
+  lin /= gridDim.x;
+  const int b = gridDim.z - 1 - lin / gridDim.y, split = gridDim.y - 1 - lin % gridDim.y;
+  const int c0 = cb * kRtpCols;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
   // R staging: each wave-wide load covers 4 whole 256-byte row pieces (16 lanes
   // x 16 bytes per row); loads q = 0, 1 take rows ld_row and ld_row + 16
@@ -476,24 +531,29 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
   const bool col_ok = c0 + ld_col < m;
   const int i_begin = split * split_rows;
   const int i_end = min(rows_pad, i_begin + split_rows);
-  const uint16_t* Rb = R + (size_t)b * n * m;
+  const uint16_t* Rb = R + (size_t)b * r_tensor_elems(rows_pad, m);
+  const int ncb = (m + 127) >> 7;
   const uint16_t* Pb = Pbt + (size_t)b * K * rows_pad;
   const int tr_off = (8 * lk + (lr >> 2)) * kRtpLd + 32 * w + 4 * (lr & 3);
 
+  // Two steps are in flight while one is multiplied: the loop is unrolled by two
+  // so each step's registers keep their role, and every load is unconditional
+  // (past the last step the addresses are clamped to it, which the cache
+  // serves), so waits count only the older step's loads.
   struct Stage { u32x4 r0, r1, p; };
+  const int last = i_end - 32;
   auto gload = [&](int i0) {
+    i0 = min(i0, last);
     Stage st;
     const int row0 = min(i0 + ld_row, n - 1), row1 = min(i0 + ld_row + 16, n - 1);
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const size_t col = (size_t)c0 + (col_ok ? ld_col : 0);
-    st.r0 = *reinterpret_cast<const u32x4*>(Rb + (size_t)row0 * m + col);
-    st.r1 = *reinterpret_cast<const u32x4*>(Rb + (size_t)row1 * m + col);
-    if (!col_ok) st.r0 = st.r1 = z;
-    st.p = z;
-    if (threadIdx.x < PCH) {
-      const int j = threadIdx.x >> 2, q = threadIdx.x & 3;
-      st.p = *reinterpret_cast<const u32x4*>(Pb + (size_t)j * rows_pad + i0 + 8 * q);
-    }
+    // columns past m reread column c0; output row c of the product depends on
+    // column c of R alone, and rows past m are never stored
+    const int col = c0 + (col_ok ? ld_col : 0);
+    st.r0 = *reinterpret_cast<const u32x4*>(Rb + r_index(row0, col, ncb));
+    st.r1 = *reinterpret_cast<const u32x4*>(Rb + r_index(row1, col, ncb));
+    // lanes past the P^T chunk count reread chunk 0 and never store it
+    const int t = threadIdx.x < PCH ? threadIdx.x : 0;
+    st.p = *reinterpret_cast<const u32x4*>(Pb + (size_t)(t >> 2) * rows_pad + i0 + 8 * (t & 3));
     return st;
   };
   f32x4 acc[2][NT];
@@ -502,15 +562,13 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
 #pragma unroll
     for (int g = 0; g < NT; ++g) acc[ct][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  Stage next = gload(i_begin);
-  int buf = 0;
-  for (int i0 = i_begin; i0 < i_end; i0 += 32, buf ^= 1) {
-    *reinterpret_cast<u32x4*>(&sR[buf][ld_row * kRtpLd + ld_col]) = next.r0;
-    *reinterpret_cast<u32x4*>(&sR[buf][(ld_row + 16) * kRtpLd + ld_col]) = next.r1;
+  auto put = [&](const Stage& st, int buf) {
+    *reinterpret_cast<u32x4*>(&sR[buf][ld_row * kRtpLd + ld_col]) = st.r0;
+    *reinterpret_cast<u32x4*>(&sR[buf][(ld_row + 16) * kRtpLd + ld_col]) = st.r1;
     if (threadIdx.x < PCH)
-      *reinterpret_cast<u32x4*>(&sP[buf][(threadIdx.x >> 2) * kRtpPld + 8 * (threadIdx.x & 3)]) = next.p;
-    __syncthreads();
-    if (i0 + 32 < i_end) next = gload(i0 + 32);
+      *reinterpret_cast<u32x4*>(&sP[buf][(threadIdx.x >> 2) * kRtpPld + 8 * (threadIdx.x & 3)]) = st.p;
+  };
+  auto compute = [&](int buf) {
     u32x4 A[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -528,6 +586,26 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
       acc[0][g] = mfma_bf16(A[0], Bv, acc[0][g]);
       acc[1][g] = mfma_bf16(A[1], Bv, acc[1][g]);
     }
+  };
+
+  // LDS double buffer, one barrier per step: a buffer is refilled two steps
+  // after it was read, and every wave has passed the barrier in between.
+  Stage s0 = gload(i_begin), s1 = gload(i_begin + 32);
+  int i0 = i_begin;
+  for (; i0 + 32 < i_end; i0 += 64) {
+    put(s0, 0);
+    __syncthreads();
+    s0 = gload(i0 + 64);
+    compute(0);
+    put(s1, 1);
+    __syncthreads();
+    s1 = gload(i0 + 96);
+    compute(1);
+  }
+  if (i0 < i_end) {  // an odd number of steps
+    put(s0, 0);
+    __syncthreads();
+    compute(0);
   }
   // D[c][j]: lane holds c = c0 + 32w + 16ct + 4lk + t, j = 16g + lr
   float* qp = qpart + ((size_t)b * nsplit + split) * K * m;

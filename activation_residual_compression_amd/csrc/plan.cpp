@@ -149,7 +149,7 @@ rc_status_t setup_lowrank(rc_plan* pl, const float* q0) {
   w.split_rows = (int)(((w.rows_pad + split - 1) / split + 31) / 32 * 32);
   w.nsplit = (int)((w.rows_pad + w.split_rows - 1) / w.split_rows);
   Piece pieces[] = {
-      {(void**)&w.R, B * n * m * 2},
+      {(void**)&w.R, B * w.rows_pad * ((m + 127) / 128 * 128) * 2},
       {(void**)&w.P, B * n * k * 4},
       {(void**)&w.Pbt, B * k * w.rows_pad * 2},
       {(void**)&w.Qt, B * k * m * 4},
@@ -208,7 +208,7 @@ rc_status_t setup_blocksel(rc_plan* pl) {
 rc::LowRankWork lr_slice(const rc::LowRankWork& w, const rc::Layout& L, int64_t b0) {
   const int64_t n = L.rows, m = L.cols, k = w.rank;
   rc::LowRankWork s = w;
-  s.R += b0 * n * m;
+  s.R += b0 * w.rows_pad * ((m + 127) / 128 * 128);
   s.P += b0 * n * k;
   s.Pbt += b0 * k * w.rows_pad;
   s.Qt += b0 * k * m;

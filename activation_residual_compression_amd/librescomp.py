@@ -236,7 +236,7 @@ class Plan:
         rc_plan_reset_state(self.handle, stream)
 
     def lowrank_workspace(self):
-        """Device pointers (R, P, Pbt, Qt, Q0t, Qtb, gpart, chol) and rows_pad (diagnostics)."""
+        """Device pointers (R, P, Pbt, Qt, Q0t, Qtb, gsum, linv) and rows_pad (diagnostics)."""
         arr = (ctypes.c_void_p * 8)()
         rp = _lib.rcx_lowrank_workspace(self.handle, arr, 8)
         if rp < 0:
