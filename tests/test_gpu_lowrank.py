@@ -86,6 +86,13 @@ def test_lr_ragged_small(rank, iters):
     _run_lr(wl, rank, iters, check=[0, 1])
 
 
+def test_lr_several_tiles_ragged_both_ways():
+    # 200 rows: four 64-row tiles, the last one 8 rows long; 320 columns: two
+    # whole 128-column tiles of R and a half one
+    wl = synth.FluxWorkload(batch=3, n=200, m=320, steps=3)
+    _run_lr(wl, 32, 2, check=[0, 2])
+
+
 @pytest.mark.parametrize("rank,iters", [(16, 2), (32, 1)])
 def test_lr_bf16_factors_ragged(rank, iters):
     wl = synth.FluxWorkload(batch=2, n=100, m=192, steps=4)
