@@ -729,26 +729,26 @@ __global__ __launch_bounds__(256) void lr_bf16f_kernel(const float* __restrict__
 // ---------------------------------------------------------------- reconstruct
 // c = Uq Vq^T with fp32 MFMA, read straight from the packed factors (INT4 codes
 // times their column scale, or bf16), applied to the state arrays. A block owns
-// 256 columns (four 64-column strips, one per wave) of a chunk of rows of one
-// tensor of one peer and walks it in 16-row tiles:
-//   * once: each wave's V operands (4 MFMA column tiles x K) in registers;
-//   * per tile: each wave computes its 16 x 64 piece of c^T = Vq Uq^T with K
+// CW columns (CW = 256 or 128: four strips of CW/4 columns, one per wave) of a
+// chunk of rows of one tensor of one peer and walks it in 16-row tiles:
+//   * once: each wave's V operands (CW/64 MFMA column tiles x K) in registers;
+//   * per tile: each wave computes its 16 x CW/4 piece of c^T = Vq Uq^T with
 //     MFMAs and writes it to an LDS tile (two buffers, one barrier per tile);
 //     then wave w applies rows 4w .. 4w+3 of the tile, each lane owning 4
-//     consecutive columns, so every global access of a wave is one contiguous
-//     1 KiB run: r = a - ahat, e = r - c, ahat += c (SENDER) or ahat += c.
+//     consecutive columns, so every global access of a wave covers whole
+//     CW-column row pieces (one 1 KiB run, or two 512 B runs):
+//     r = a - ahat, e = r - c, ahat += c (SENDER) or ahat += c.
 //     The next tile's U operands and state rows are loaded before the current
 //     tile's MFMAs; the last tile has no successor to load.
 // MFMA step (j, i), j < K/16, i < 4: lane group g = l/16 covers contraction
 // index 16 j + 4 g + i, so both operands come from 4 consecutive factor
 // entries of one row (2 bytes of INT4 codes or 8 bytes of bf16). The M index mi
 // of column tile p is strip column 32 (p/2) + 8 (mi/4) + 4 (p%2) + mi%4, so each
-// lane's results are two runs of 8 columns of one row. Sender and receiver run
-// the same MFMA sequence on the same packed bytes, so both get the same c bit
-// for bit. Strips and lanes past m (m a multiple of 64 but not of 256) compute
-// and store nothing. Grid z = peer * batch + tensor.
-constexpr int kRcCols = 256;         // columns per block (4 waves x 64)
-constexpr int kRcLds = kRcCols + 4;  // LDS row stride, floats
+// lane's results are runs of 8 columns of one row. Sender and receiver run the
+// same MFMA sequence on the same packed bytes, so both get the same c bit for
+// bit (the column width changes which block computes an entry, not how).
+// Strips and lanes past m (m a multiple of 64) compute and store nothing.
+// Grid z = peer * batch + tensor.
 
 // Factor entries (row, k0 .. k0+3) as the encoder defined them: INT4 code times
 // the column scale (scale4 = the 4 scales of k0 .. k0+3), or the bf16 value.
@@ -769,12 +769,19 @@ __device__ __forceinline__ f32x4 factor4(const uint8_t* sec, const f32x4& scale4
   }
 }
 
-template <typename IN, bool SENDER, int K, bool BF16F>
+template <typename IN, bool SENDER, int K, bool BF16F, int CW>
 __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
                                                        float* __restrict__ e, PeerSet peers,
                                                        int batch, Layout L, int chunk_rows) {
+  static_assert(CW == 256 || CW == 128, "column width");
   constexpr int KJ = K / 16;
-  __shared__ float tile[2][16 * kRcLds];
+  constexpr int SW = CW / 4;       // strip columns per wave
+  constexpr int NP = SW / 16;      // MFMA column tiles per wave
+  constexpr int LPR = CW / 4;      // lanes per row when applying
+  constexpr int RPI = 64 / LPR;    // rows per wave-wide access
+  constexpr int NI = 4 / RPI;      // accesses per wave per tile
+  constexpr int LDSW = CW + 4;     // LDS row stride, floats
+  __shared__ float tile[2][16 * LDSW];
   const int n = (int)L.rows, m = (int)L.cols;
   const int peer = blockIdx.z / batch, b = blockIdx.z % batch;
   float* __restrict__ ahat = peers.state[peer];
@@ -782,10 +789,11 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
   const uint8_t* usec = pk + L.sec_off[0];
   const uint8_t* vsec = pk + L.sec_off[1];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
-  const int cb = blockIdx.x * kRcCols;
-  const int c0 = cb + 64 * w;
+  const int cb = blockIdx.x * CW;
+  const int c0 = cb + SW * w;
   const bool strip_ok = c0 < m;
-  const bool col_ok = cb + 4 * lane < m;
+  const int lc = 4 * (lane % LPR), ri = lane / LPR;  // apply: lane's columns and row in an access
+  const bool col_ok = cb + lc < m;
   const int rbeg = blockIdx.y * chunk_rows;
   const int rend = min(n, rbeg + chunk_rows);
 
@@ -799,19 +807,19 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
       sv[j] = *reinterpret_cast<const f32x4*>(pk + L.sec_off[3] + 4 * (16 * j + 4 * lk));
     }
   }
-  f32x4 av[4][KJ];
+  f32x4 av[NP][KJ];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
+  for (int p = 0; p < NP; ++p) {
     const int col = (strip_ok ? c0 : 0) + 32 * (p >> 1) + 8 * (lr >> 2) + 4 * (p & 1) + (lr & 3);
 #pragma unroll
     for (int j = 0; j < KJ; ++j) av[p][j] = factor4<K, BF16F>(vsec, sv[j], col, 16 * j + 4 * lk);
   }
-  const size_t tb = (size_t)b * n * m + (size_t)(col_ok ? cb + 4 * lane : 0);
+  const size_t tb = (size_t)b * n * m + (size_t)(col_ok ? cb + lc : 0);
 
   struct Rows {
     f32x4 u[KJ];  // U operands of the tile's 16 rows
-    f32x4 h[4];   // ahat of this wave's 4 rows, this lane's 4 columns
-    f32x4 x[4];   // a_t of the same (SENDER)
+    f32x4 h[NI];  // ahat of this lane's rows and 4 columns
+    f32x4 x[NI];  // a_t of the same (SENDER)
   };
   // Rows past the chunk reread its last row and are never stored.
   auto load = [&](int r0, Rows& R) {
@@ -819,33 +827,34 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
 #pragma unroll
     for (int j = 0; j < KJ; ++j) R.u[j] = factor4<K, BF16F>(usec, su[j], ru, 16 * j + 4 * lk);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t off = tb + (size_t)min(r0 + 4 * w + i, rend - 1) * m;
+    for (int i = 0; i < NI; ++i) {
+      const size_t off = tb + (size_t)min(r0 + 4 * w + RPI * i + ri, rend - 1) * m;
       R.h[i] = load4<float>(ahat + off);
       if constexpr (SENDER) R.x[i] = load4<IN>(a + off);
     }
   };
   auto apply = [&](int r0, int it, const Rows& T) {
-    f32x4 acc[4];
+    f32x4 acc[NP];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < NP; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (strip_ok) {
 #pragma unroll
       for (int j = 0; j < KJ; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int p = 0; p < 4; ++p) acc[p] = mfma_f32(av[p][j][i], T.u[j][i], acc[p]);
+          for (int p = 0; p < NP; ++p) acc[p] = mfma_f32(av[p][j][i], T.u[j][i], acc[p]);
     }
     float* S = tile[it & 1];
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-      *reinterpret_cast<f32x4*>(&S[lr * kRcLds + 64 * w + 32 * (p >> 1) + 8 * lk + 4 * (p & 1)]) = acc[p];
+    for (int p = 0; p < NP; ++p)
+      *reinterpret_cast<f32x4*>(&S[lr * LDSW + SW * w + 32 * (p >> 1) + 8 * lk + 4 * (p & 1)]) = acc[p];
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = r0 + 4 * w + i;
-      const f32x4 c = *reinterpret_cast<const f32x4*>(&S[(4 * w + i) * kRcLds + 4 * lane]);
+    for (int i = 0; i < NI; ++i) {
+      const int tr = 4 * w + RPI * i + ri;
+      const int row = r0 + tr;
+      const f32x4 c = *reinterpret_cast<const f32x4*>(&S[tr * LDSW + lc]);
       if (row < rend && col_ok) {
         const size_t off = tb + (size_t)row * m;
         f32x4 hn;
@@ -878,19 +887,42 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
   apply(r0, it, cur);
 }
 
-// Grid of the reconstruct kernel: 256-column blocks x row chunks x tensors.
+// Column width of the reconstruct blocks. 256 (1 KiB row runs) is faster on
+// whole blocks (flux 57 x 1152 x 3072: 503 us against 534 us at rank 32); where
+// the last 256-column block would be at most half used (m % 256 == 64 or 128),
+// 128-column blocks waste less (video 30 x 4444 x 1920: 634 us against 667 us).
+inline int rc_col_width(int m) {
+  const int tail = m % 256;
+  return (tail == 64 || tail == 128) ? 128 : 256;
+}
+
+// Grid of the reconstruct kernel: CW-column blocks x row chunks x tensors.
 // Short chunks keep the blocks that run together on neighbouring rows; the V
 // operands are loaded once per block, so chunks stay long enough (64 or 128
 // rows) to amortise them.
 struct RcGrid {
   dim3 grid;
   int chunk_rows;
+  int cw;
 };
 inline RcGrid rc_grid(int n, int m, int B, int k) {
   const int chunk_rows = k <= 32 ? 64 : 128;
-  return RcGrid{dim3((unsigned)((m + kRcCols - 1) / kRcCols), (unsigned)((n + chunk_rows - 1) / chunk_rows),
+  const int cw = rc_col_width(m);
+  return RcGrid{dim3((unsigned)((m + cw - 1) / cw), (unsigned)((n + chunk_rows - 1) / chunk_rows),
                      (unsigned)B),
-                chunk_rows};
+                chunk_rows, cw};
+}
+
+// One reconstruct launch with the column width chosen at run time.
+template <typename IN, bool SENDER, int K, bool BF16F>
+void launch_recon(const RcGrid& g, hipStream_t s, const IN* a, float* e, const PeerSet& peers,
+                  int batch, const Layout& L) {
+  if (g.cw == 128)
+    hipLaunchKernelGGL((lr_recon_kernel<IN, SENDER, K, BF16F, 128>), g.grid, dim3(256), 0, s, a, e,
+                       peers, batch, L, g.chunk_rows);
+  else
+    hipLaunchKernelGGL((lr_recon_kernel<IN, SENDER, K, BF16F, 256>), g.grid, dim3(256), 0, s, a, e,
+                       peers, batch, L, g.chunk_rows);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -950,17 +982,13 @@ hipError_t lr_compress_k(bool bf16, const void* a, float* ahat, float* e, uint8_
   self.count = 1;
   const RcGrid g = rc_grid(n, m, B, K);
   if (bf16 && w.bf16_factors)
-    hipLaunchKernelGGL((lr_recon_kernel<uint16_t, true, K, true>), g.grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(a), e, self, B, L, g.chunk_rows);
+    launch_recon<uint16_t, true, K, true>(g, s, static_cast<const uint16_t*>(a), e, self, B, L);
   else if (bf16)
-    hipLaunchKernelGGL((lr_recon_kernel<uint16_t, true, K, false>), g.grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(a), e, self, B, L, g.chunk_rows);
+    launch_recon<uint16_t, true, K, false>(g, s, static_cast<const uint16_t*>(a), e, self, B, L);
   else if (w.bf16_factors)
-    hipLaunchKernelGGL((lr_recon_kernel<float, true, K, true>), g.grid, dim3(256), 0, s,
-                       static_cast<const float*>(a), e, self, B, L, g.chunk_rows);
+    launch_recon<float, true, K, true>(g, s, static_cast<const float*>(a), e, self, B, L);
   else
-    hipLaunchKernelGGL((lr_recon_kernel<float, true, K, false>), g.grid, dim3(256), 0, s,
-                       static_cast<const float*>(a), e, self, B, L, g.chunk_rows);
+    launch_recon<float, true, K, false>(g, s, static_cast<const float*>(a), e, self, B, L);
   return hipGetLastError();
 }
 
@@ -981,11 +1009,9 @@ hipError_t lr_decompress_k(const PeerSet& peers, int B, const Layout& L, const L
     }
     g.grid.z = (unsigned)(B * sub.count);
     if (w.bf16_factors)
-      hipLaunchKernelGGL((lr_recon_kernel<float, false, K, true>), g.grid, dim3(256), 0, s,
-                         (const float*)nullptr, (float*)nullptr, sub, B, L, g.chunk_rows);
+      launch_recon<float, false, K, true>(g, s, nullptr, nullptr, sub, B, L);
     else
-      hipLaunchKernelGGL((lr_recon_kernel<float, false, K, false>), g.grid, dim3(256), 0, s,
-                         (const float*)nullptr, (float*)nullptr, sub, B, L, g.chunk_rows);
+      launch_recon<float, false, K, false>(g, s, nullptr, nullptr, sub, B, L);
   }
   return hipGetLastError();
 }
