@@ -320,13 +320,16 @@ __global__ __launch_bounds__(256) void lr_gram_reduce_kernel(const float* __rest
 
 // ---------------------------------------------------------------- Cholesky
 // One wave per tensor: lane i holds row i of G (from the upper triangle of
-// gsum) and builds row i of L by the left-looking recurrence. Each finished
-// column of L goes to LDS, so row j of L (needed by every lane at step j) is
-// read back as uniform-address broadcasts, four entries per LDS read. Dead
-// columns (pivot <= 2^-23 * max(trace G, K * FLT_MIN)) get L[j][j] = 1 and a
-// zero column below the diagonal. Then lane c solves L y = e_c, giving column c
-// of L^{-1}; rows of dead columns are zeroed, so x = L^{-1} p has x_j = 0 there
-// and the other entries are those of the forward substitution.
+// gsum) and builds row i of L by the left-looking recurrence; lane c builds
+// column c of L^{-1} by forward substitution. Step j of both needs row j of L
+// up to column j-1, which every lane reads from LDS as uniform-address
+// broadcasts, four entries per read, and the two dot products run as
+// independent chains. Dead columns (pivot <= 2^-23 * max(trace G, K *
+// FLT_MIN)) get L[j][j] = 1, a zero column below the diagonal and a zero row
+// j of L^{-1}, so x = L^{-1} p has x_j = 0 there and the other entries are
+// those of the forward substitution. Both dot products are fused multiply-add
+// chains in index order; divisions by L[j][j] are products with its correctly
+// rounded reciprocal.
 __device__ __forceinline__ float lane_f32(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
@@ -339,7 +342,8 @@ __global__ __launch_bounds__(64) void lr_chol_kernel(const float* __restrict__ g
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const float* gs = gsum + (size_t)b * K * K;
-  float g[K], L[K];
+  float* out = linv + (size_t)b * K * K + lane;  // column `lane` of L^{-1}
+  float g[K], L[K], y[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     g[j] = (lane < K && j <= lane) ? gs[j * K + lane] : 0.f;  // G[lane][j] = G[j][lane]
@@ -349,45 +353,32 @@ __global__ __launch_bounds__(64) void lr_chol_kernel(const float* __restrict__ g
 #pragma unroll
   for (int j = 0; j < K; ++j) tr += lane_f32(g[j], j);
   const float tol = ldexpf(fmaxf(tr, (float)K * FLT_MIN), -23);
-  uint64_t dead = 0;
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    float s = g[j];
+    float s = g[j];                       // G[lane][j] - sum_p L[lane][p] L[j][p]
+    float t = (j == lane) ? 1.f : 0.f;    // e_lane[j] - sum_q L[j][q] y[q]
     const f32x4* Lj = reinterpret_cast<const f32x4*>(Ls + j * LDc);
 #pragma unroll
     for (int q = 0; q < (j + 3) / 4; ++q) {
       const f32x4 v = Lj[q];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (4 * q + t < j) s -= L[4 * q + t] * v[t];
+      for (int u = 0; u < 4; ++u)
+        if (4 * q + u < j) {
+          s = fmaf(-L[4 * q + u], v[u], s);
+          t = fmaf(-v[u], y[4 * q + u], t);
+        }
     }
     const float piv = lane_f32(s, j);
     const bool dj = !(piv > tol);
     const float ljj = dj ? 1.0f : sqrtf(piv);
-    L[j] = lane == j ? ljj : (lane > j && !dj ? s / ljj : 0.f);
-    if (dj) dead |= (uint64_t)1 << j;
-    if (lane < K) Ls[lane * LDc + j] = L[j];
-    __syncthreads();
-  }
-  // column `lane` of L^{-1}
-  float y[K];
-#pragma unroll
-  for (int i = 0; i < K; ++i) {
-    float s = (i == lane) ? 1.f : 0.f;
-    const f32x4* Li = reinterpret_cast<const f32x4*>(Ls + i * LDc);
-#pragma unroll
-    for (int q = 0; q < (i + 3) / 4; ++q) {
-      const f32x4 v = Li[q];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (4 * q + t < i) s -= v[t] * y[4 * q + t];
+    const float inv = 1.0f / ljj;
+    L[j] = lane == j ? ljj : (lane > j && !dj ? s * inv : 0.f);
+    y[j] = dj ? 0.f : t * inv;
+    if (lane < K) {
+      Ls[lane * LDc + j] = L[j];
+      out[(size_t)j * K] = y[j];  // stored here, so the chain is not deferred to the end
     }
-    y[i] = ((dead >> i) & 1) ? 0.f : s / Ls[i * LDc + i];
-  }
-  if (lane < K) {
-    float* out = linv + (size_t)b * K * K + lane;
-#pragma unroll
-    for (int i = 0; i < K; ++i) out[(size_t)i * K] = y[i];
+    __syncthreads();
   }
 }
 
