@@ -311,6 +311,13 @@ __global__ __launch_bounds__(256) void lr_gram_reduce_kernel(const float* __rest
   const float* gp = gpart + (size_t)b * ntiles * K * K + idx;
   float s[4] = {0.f, 0.f, 0.f, 0.f};
   int p = 0;
+  for (; p + 16 <= ntiles; p += 16) {  // 16 loads in flight, same summation order
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = gp[(size_t)(p + q) * K * K];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) s[q & 3] += v[q];
+  }
   for (; p + 4 <= ntiles; p += 4)
 #pragma unroll
     for (int q = 0; q < 4; ++q) s[q] += gp[(size_t)(p + q) * K * K];
@@ -609,7 +616,7 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
   }
 }
 
-// Sum the row splits in split order: Qt (fp32, V of the factorisation), Qtb
+// Sum the row splits (at most 8) in split order: Qt (fp32, V of the factorisation), Qtb
 // (bf16 operand of the next product), and the column absmax of V folded into
 // amax[b][1][j]. Block: one j, 1024 columns (4 per lane).
 template <int K>
@@ -622,9 +629,17 @@ __global__ __launch_bounds__(256) void lr_qfinish_kernel(const float* __restrict
   const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
   float mx = 0.f;
   if (c < m) {
+    // every split's partial is loaded before the first add (nsplit <= 8;
+    // indices past nsplit reread the last split and are not added)
+    const float* base = qpart + ((size_t)b * nsplit * K + j) * m + c;
+    f32x4 v[8];
+#pragma unroll
+    for (int sp = 0; sp < 8; ++sp)
+      v[sp] = *reinterpret_cast<const f32x4*>(base + (size_t)min(sp, nsplit - 1) * K * m);
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < nsplit; ++sp)
-      s += *reinterpret_cast<const f32x4*>(qpart + (((size_t)b * nsplit + sp) * K + j) * m + c);
+#pragma unroll
+    for (int sp = 0; sp < 8; ++sp)
+      if (sp < nsplit) s += v[sp];
     const size_t o = ((size_t)b * K + j) * m + c;
     *reinterpret_cast<f32x4*>(Qt + o) = s;
     uint2 hb;
@@ -672,15 +687,27 @@ __global__ __launch_bounds__(256) void lr_int4_kernel(const float* __restrict__ 
   const bool isV = r >= n;
   const int i = isV ? r - n : r;
   const float* s = sc + (isV ? K : 0);
-  const float* src = isV ? Qt + (size_t)b * K * m + i : P + ((size_t)b * n + i) * K;
-  const size_t stride = isV ? (size_t)m : 1;
+  // the whole factor row is loaded before any of it is quantised
+  float x[K];
+  if (isV) {
+    const float* src = Qt + (size_t)b * K * m + i;
+#pragma unroll
+    for (int j = 0; j < K; ++j) x[j] = src[(size_t)j * m];
+  } else {
+    const f32x4* src = reinterpret_cast<const f32x4*>(P + ((size_t)b * n + i) * K);
+#pragma unroll
+    for (int j = 0; j < K / 4; ++j) {
+      const f32x4 v = src[j];
+      x[4 * j] = v.x; x[4 * j + 1] = v.y; x[4 * j + 2] = v.z; x[4 * j + 3] = v.w;
+    }
+  }
   uint32_t words[K / 8];
 #pragma unroll
   for (int q = 0; q < K / 8; ++q) words[q] = 0;
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     int qi = 0;
-    if (s[j] > 0.f) qi = (int)fminf(fmaxf(rintf(src[j * stride] / s[j]), -7.f), 7.f);
+    if (s[j] > 0.f) qi = (int)fminf(fmaxf(rintf(x[j] / s[j]), -7.f), 7.f);
     words[j / 8] |= ((uint32_t)qi & 0xFu) << (4 * (j % 8));
   }
   uint32_t* dst = reinterpret_cast<uint32_t*>(pk + (isV ? L.sec_off[1] : L.sec_off[0]) + (size_t)i * (K / 2));
