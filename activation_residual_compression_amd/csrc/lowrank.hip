@@ -616,10 +616,11 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
   }
 }
 
-// Sum the row splits (at most 8) in split order: Qt (fp32, V of the factorisation), Qtb
-// (bf16 operand of the next product), and the column absmax of V folded into
-// amax[b][1][j]. Block: one j, 1024 columns (4 per lane).
-template <int K>
+// Sum the row splits (at most 8) in split order. Before the last iteration the
+// sum is needed only as the bf16 operand of the next product (Qtb); after it,
+// only as V: Qt in fp32 and the column absmax of V folded into amax[b][1][j].
+// Block: one j, 1024 columns (4 per lane).
+template <int K, bool FINAL>
 __global__ __launch_bounds__(256) void lr_qfinish_kernel(const float* __restrict__ qpart,
                                                          float* __restrict__ Qt,
                                                          uint16_t* __restrict__ Qtb,
@@ -629,8 +630,8 @@ __global__ __launch_bounds__(256) void lr_qfinish_kernel(const float* __restrict
   const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
   float mx = 0.f;
   if (c < m) {
-    // every split's partial is loaded before the first add (nsplit <= 8;
-    // indices past nsplit reread the last split and are not added)
+    // every split's partial is loaded before the first add (indices past
+    // nsplit reread the last split and are not added)
     const float* base = qpart + ((size_t)b * nsplit * K + j) * m + c;
     f32x4 v[8];
 #pragma unroll
@@ -641,16 +642,21 @@ __global__ __launch_bounds__(256) void lr_qfinish_kernel(const float* __restrict
     for (int sp = 0; sp < 8; ++sp)
       if (sp < nsplit) s += v[sp];
     const size_t o = ((size_t)b * K + j) * m + c;
-    *reinterpret_cast<f32x4*>(Qt + o) = s;
-    uint2 hb;
-    hb.x = bf16_rne(s.x) | (bf16_rne(s.y) << 16);
-    hb.y = bf16_rne(s.z) | (bf16_rne(s.w) << 16);
-    *reinterpret_cast<uint2*>(Qtb + o) = hb;
-    mx = fmaxf(fmaxf(fabsf(s.x), fabsf(s.y)), fmaxf(fabsf(s.z), fabsf(s.w)));
+    if constexpr (FINAL) {
+      *reinterpret_cast<f32x4*>(Qt + o) = s;
+      mx = fmaxf(fmaxf(fabsf(s.x), fabsf(s.y)), fmaxf(fabsf(s.z), fabsf(s.w)));
+    } else {
+      uint2 hb;
+      hb.x = bf16_rne(s.x) | (bf16_rne(s.y) << 16);
+      hb.y = bf16_rne(s.z) | (bf16_rne(s.w) << 16);
+      *reinterpret_cast<uint2*>(Qtb + o) = hb;
+    }
   }
+  if constexpr (FINAL) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  if ((threadIdx.x & 63) == 0) atomicMax(amax + ((size_t)b * 2 + 1) * K + j, __float_as_uint(mx));
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((threadIdx.x & 63) == 0) atomicMax(amax + ((size_t)b * 2 + 1) * K + j, __float_as_uint(mx));
+  }
 }
 
 // ---------------------------------------------------------------- INT4 factors
@@ -985,8 +991,12 @@ hipError_t lr_compress_k(bool bf16, const void* a, float* ahat, float* e, uint8_
     cqr_pass<K>(w, n, B, true, s);
     hipLaunchKernelGGL((lr_rtp_kernel<K>), dim3((m + kRtpCols - 1) / kRtpCols, w.nsplit, B),
                        dim3(256), 0, s, w.R, w.Pbt, w.qpart, n, m, rp, w.nsplit, w.split_rows);
-    hipLaunchKernelGGL((lr_qfinish_kernel<K>), dim3(K, (m + 1023) / 1024, B), dim3(256), 0, s,
-                       w.qpart, w.Qt, w.Qtb, w.amax, m, w.nsplit);
+    if (it + 1 == w.iters)
+      hipLaunchKernelGGL((lr_qfinish_kernel<K, true>), dim3(K, (m + 1023) / 1024, B), dim3(256), 0,
+                         s, w.qpart, w.Qt, w.Qtb, w.amax, m, w.nsplit);
+    else
+      hipLaunchKernelGGL((lr_qfinish_kernel<K, false>), dim3(K, (m + 1023) / 1024, B), dim3(256), 0,
+                         s, w.qpart, w.Qt, w.Qtb, w.amax, m, w.nsplit);
   }
   if (w.bf16_factors)
     hipLaunchKernelGGL((lr_bf16f_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, w.P,
