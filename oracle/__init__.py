@@ -10,8 +10,10 @@ Method source: the paper-notes page "Accelerating Parallel Diffusion Model
 Serving with Residual Compression" (CompactFusion), sections Method / Overall
 framework, Key designs (Residual compression, Error feedback, Low-rank strategy
 for extreme compression, System co-design), Main experiment table and
-Limitations (warm-up). See ``oracle.c`` for the per-function citations and the
-readings taken where the page is silent.
+Limitations (warm-up); block selection follows the page "Otil: Accelerating
+Diffusion Model Inference via Communication-Efficient Multi-GPU Parallelism",
+Key designs 1-3. See ``oracle.c`` for the per-function citations and the
+readings taken where the pages are silent.
 
 Parity status: every scheme is pinned by the CPU tests (closed forms, brute
 force, library routines, invariants); the low-rank factors themselves are
