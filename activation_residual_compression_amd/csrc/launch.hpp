@@ -45,7 +45,7 @@ struct LowRankWork {
   bool bf16_factors = false;  // factors sent as bf16 instead of INT4 + scales
   int64_t ntiles = 0, rows_pad = 0;
   int nsplit = 1, split_rows = 0;
-  uint16_t* R = nullptr;     // bf16 residual, per tensor rows_pad x 128*ceil(cols/128) in 32 x 128 tiles
+  uint16_t* R = nullptr;     // bf16 residual: 64 x 128 tiles, column chunk, then tensor, then band (per launch)
   float* P = nullptr;        // fp32 panel [batch][rows][rank]
   uint16_t* Pbt = nullptr;   // bf16 orthonormal panel, transposed [batch][rank][rows_pad]
   float* Qt = nullptr;       // fp32 Q^T [batch][rank][cols]

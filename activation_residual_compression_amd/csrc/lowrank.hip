@@ -103,15 +103,16 @@ __device__ __forceinline__ int xcd_contiguous(int L, int N) {
 }
 
 // R, the bf16 residual the products share, lives in the library's own
-// workspace in 32 x 128 tiles, each a contiguous 8 KiB row-major block, so that
-// every staged piece of it (a 32-row slice of a 128-column step) is one
-// contiguous run whichever way a product walks it. Tiles are ordered
-// row-tile-major; a tensor spans rows_pad x (128 * ceil(cols / 128)) elements.
-__device__ __forceinline__ size_t r_index(int row, int col, int ncb) {
-  return ((size_t)((row >> 5) * ncb + (col >> 7)) << 12) + (size_t)((row & 31) << 7) + (col & 127);
-}
-__device__ __forceinline__ size_t r_tensor_elems(int rows_pad, int m) {
-  return (size_t)rows_pad * (size_t)(((m + 127) >> 7) << 7);
+// workspace in 64 x 128 tiles, each a contiguous 16 KiB row-major block (one
+// step of one band of the R*Q pass; its halves are the 32-row steps of the
+// R^T*P pass). Tiles are ordered column chunk first, then tensor, then band:
+// the blocks of the R*Q passes all work on the same column chunk at the same
+// time, so together they write (and read) one contiguous region per step
+// instead of a thousand scattered ones. The order is over the tensors of one
+// launch (its grid), so a launch over a sub-batch uses its own slice of R.
+__device__ __forceinline__ size_t r_index(int b, int row, int col, int batch, int bands) {
+  return (((size_t)(col >> 7) * batch + b) * bands + (row >> 6)) * 8192 + (size_t)((row & 63) << 7) +
+         (col & 127);
 }
 
 // ---------------------------------------------------------------- P = R * Q
@@ -163,15 +164,16 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
   const int srow = 16 * w + (lane >> 5), scol = 4 * (lane & 31);
   // offsets of staged row i in a_t / ahat (row-major) and in R (tiled); rows
   // past n reread row n-1
-  const int ncb = (m + 127) >> 7;
-  uint16_t* Rb = R + (size_t)b * r_tensor_elems(kTile * ntiles, m);
+  // R: this block's tile of column chunk c0/128 starts at rbase + (c0/128) * cstride
+  const size_t rbase = (size_t)(b * ntiles + tile) * 8192;
+  const size_t cstride = (size_t)gridDim.y * ntiles * 8192;
   auto soff = [&](int c0, int i) -> size_t {
     const int row = min(row0 + srow + 2 * i, n - 1);
     return ((size_t)b * n + row) * m + (c0 + scol < m ? c0 + scol : 0);
   };
   auto roff = [&](int c0, int i) -> size_t {
-    const int row = min(row0 + srow + 2 * i, n - 1);
-    return r_index(row, c0 + scol < m ? c0 + scol : 0, ncb);
+    const int r = min(row0 + srow + 2 * i, n - 1) - row0;
+    return (size_t)(c0 >> 7) * cstride + rbase + (size_t)(r * 128 + (c0 + scol < m ? scol : 0));
   };
   auto gload = [&](int c0, Stage& S) {
 #pragma unroll
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
         S.x[i] = __builtin_nontemporal_load(reinterpret_cast<const Raw*>(a + off));
         S.h[i] = load4<float>(ahat + off);
       } else {
-        S.r[i] = *reinterpret_cast<const u32x2*>(Rb + roff(c0, i));
+        S.r[i] = *reinterpret_cast<const u32x2*>(R + roff(c0, i));
       }
     }
   };
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
           x = S.x[i];
         v.x = bf16_rne(x[0] - S.h[i][0]) | (bf16_rne(x[1] - S.h[i][1]) << 16);
         v.y = bf16_rne(x[2] - S.h[i][2]) | (bf16_rne(x[3] - S.h[i][3]) << 16);
-        if (col_ok && row0 + srow + 2 * i < n) *reinterpret_cast<u32x2*>(Rb + roff(c0, i)) = v;
+        if (col_ok && row0 + srow + 2 * i < n) *reinterpret_cast<u32x2*>(R + roff(c0, i)) = v;
       } else {
         v = S.r[i];
       }
@@ -529,8 +531,7 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
   const bool col_ok = c0 + ld_col < m;
   const int i_begin = split * split_rows;
   const int i_end = min(rows_pad, i_begin + split_rows);
-  const uint16_t* Rb = R + (size_t)b * r_tensor_elems(rows_pad, m);
-  const int ncb = (m + 127) >> 7;
+  const int batch = gridDim.z, bands = rows_pad >> 6;
   const uint16_t* Pb = Pbt + (size_t)b * K * rows_pad;
   const int tr_off = (8 * lk + (lr >> 2)) * kRtpLd + 32 * w + 4 * (lr & 3);
 
@@ -547,8 +548,8 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
     // columns past m reread column c0; output row c of the product depends on
     // column c of R alone, and rows past m are never stored
     const int col = c0 + (col_ok ? ld_col : 0);
-    st.r0 = *reinterpret_cast<const u32x4*>(Rb + r_index(row0, col, ncb));
-    st.r1 = *reinterpret_cast<const u32x4*>(Rb + r_index(row1, col, ncb));
+    st.r0 = *reinterpret_cast<const u32x4*>(R + r_index(b, row0, col, batch, bands));
+    st.r1 = *reinterpret_cast<const u32x4*>(R + r_index(b, row1, col, batch, bands));
     // lanes past the P^T chunk count reread chunk 0 and never store it
     const int t = threadIdx.x < PCH ? threadIdx.x : 0;
     st.p = *reinterpret_cast<const u32x4*>(Pb + (size_t)(t >> 2) * rows_pad + i0 + 8 * (t & 3));
