@@ -27,7 +27,8 @@
  *     aligned. The library never allocates or frees them.
  *   - Calls are asynchronous on the given HIP stream and never synchronise the
  *     host. Calls on one plan must be serialised on one stream (the low-rank
- *     scheme keeps per-plan device workspace).
+ *     and block-selection schemes keep per-plan device workspace and state).
+ *     Separate plans share nothing and may run concurrently on separate streams.
  *   - On any error nothing is launched and no buffer is touched; the return
  *     value says why. RC_ERR_HIP reports a failed kernel launch.
  *   - Inputs holding NaN or Inf give unspecified (but memory-safe) results.
