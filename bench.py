@@ -385,8 +385,8 @@ def cpu_baseline(config, budget_s, log):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="flux_q2")
     ap.add_argument("--also", default="flux_nm,video_q1,flux_lr,video_lr,latent_bs",
                     help="other workloads to measure ('' for none)")
