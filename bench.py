@@ -136,12 +136,14 @@ def _probe_on(kind, a, b, c, n, reps=5):
     return e0.elapsed_time(e1) / reps
 
 
-def exchange_timing(plan, seq, ahat, e, packed, chunks, reps=5):
+def exchange_timing(plan, seq, ahat, e, packed, chunks, reps=7):
     """Sender step plus hand-off of the packed stream (rc_compress_send): compress
     alone, copy alone, both in sequence, and the chunked pipeline, to a device
     buffer (stand-in for a peer's receive buffer) and to pinned host memory (a
-    PCIe link). Times are averages over `reps` calls, from an event on the
-    compute stream before the call to an event on the copy stream after it."""
+    PCIe link). Times are medians over `reps` calls after two untimed ones, from
+    an event on the compute stream before the call to an event on the copy
+    stream after it (the first chunked copies into a fresh pinned buffer can
+    take several times longer than later ones)."""
     import torch
     stream = torch.cuda.current_stream()
     cs = torch.cuda.Stream()
@@ -150,6 +152,7 @@ def exchange_timing(plan, seq, ahat, e, packed, chunks, reps=5):
     out = {}
 
     def timed(fn):
+        fn(0)
         fn(0)
         torch.cuda.synchronize()
         t = []
@@ -161,7 +164,7 @@ def exchange_timing(plan, seq, ahat, e, packed, chunks, reps=5):
             e1.record(cs)
             torch.cuda.synchronize()
             t.append(e0.elapsed_time(e1))
-        return sum(t) / len(t)
+        return sorted(t)[len(t) // 2]
 
     def compress(i):
         plan.compress(seq[i % len(seq)], ahat, e, packed, stream)
