@@ -136,8 +136,11 @@ __global__ __launch_bounds__(kBsThreads) void bs_select_kernel(const double* __r
     if (!sv[i]) {
       const double di = sd[i];
       int rank = 0;
-      for (int j = 0; j < K; ++j)
-        rank += (!sv[j] && (sd[j] > di || (sd[j] == di && j < i))) ? 1 : 0;
+#pragma unroll 16
+      for (int j = 0; j < K; ++j) {  // branch-free and unrolled, so the LDS reads overlap
+        const double dj = sd[j];
+        rank += (int)(sv[j] == 0) & ((int)(dj > di) | ((int)(dj == di) & (int)(j < i)));
+      }
       sel = rank < S.keep;
     }
     sel_flag[i] = sel;
