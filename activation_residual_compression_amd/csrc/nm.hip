@@ -102,11 +102,11 @@ __global__ __launch_bounds__(kNmBlock) void nm_compress_kernel(const IN* __restr
     xs[j] = load4<IN>(a + off);
     hs[j] = load4<float>(ahat + off);
   }
+  f32x4 evs[NC], hns[NC];
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     const int64_t c = ((int64_t)blockIdx.x * NC + j) * kNmBlock + threadIdx.x;
     const bool valid = c < n4;
-    const int64_t off = base + (valid ? c : (int64_t)q) * 4;
     f32x4 r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) r[i] = xs[j][i] - hs[j][i];
@@ -140,22 +140,28 @@ __global__ __launch_bounds__(kNmBlock) void nm_compress_kernel(const IN* __restr
     const uint32_t lo_b = bf16_rne(swap ? t.v2 : t.v1), hi_b = bf16_rne(swap ? t.v1 : t.v2);
     const float lo_c = __uint_as_float(lo_b << 16), hi_c = __uint_as_float(hi_b << 16);
 
-    f32x4 ev, hn;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t g = 4 * q + i;
       const float cv = (g == lo_i) ? lo_c : ((g == hi_i) ? hi_c : 0.0f);
-      ev[i] = r[i] - cv;
-      hn[i] = hs[j][i] + cv;
+      evs[j][i] = r[i] - cv;
+      hns[j][i] = hs[j][i] + cv;
     }
-    if (valid) {
-      if (q == 0) {
-        vals[c >> 2] = lo_b | (hi_b << 16);
-        idxs[c >> 2] = (uint8_t)(lo_i | (hi_i << 4));
-      }
-      store4(ahat + off, hn);
-      store4(e + off, ev);
+    if (valid && q == 0) {
+      vals[c >> 2] = lo_b | (hi_b << 16);
+      idxs[c >> 2] = (uint8_t)(lo_i | (hi_i << 4));
     }
+  }
+  // every chunk's ahat, then every chunk's e (longer runs per array)
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int64_t c = ((int64_t)blockIdx.x * NC + j) * kNmBlock + threadIdx.x;
+    if (c < n4) store4(ahat + base + c * 4, hns[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int64_t c = ((int64_t)blockIdx.x * NC + j) * kNmBlock + threadIdx.x;
+    if (c < n4) store4(e + base + c * 4, evs[j]);
   }
 }
 

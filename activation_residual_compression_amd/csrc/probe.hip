@@ -53,20 +53,25 @@ __global__ __launch_bounds__(kProbeBlock) void probe_mix14(const uint16_t* __res
     xs[j] = load4<uint16_t>(a + cc * 4);
     hs[j] = load4<float>(h + cc * 4);
   }
+  f32x4 evs[kMixChunks], hns[kMixChunks];
 #pragma unroll
-  for (int j = 0; j < kMixChunks; ++j) {
-    const int64_t c = ((int64_t)blockIdx.x * kMixChunks + j) * kProbeBlock + threadIdx.x;
-    f32x4 ev, hn;
+  for (int j = 0; j < kMixChunks; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float r = xs[j][i] - hs[j][i];
-      ev[i] = r;
-      hn[i] = hs[j][i] + 0.5f * r;
+      evs[j][i] = r;
+      hns[j][i] = hs[j][i] + 0.5f * r;
     }
-    if (c < n4) {
-      store4(h + c * 4, hn);
-      store4(e + c * 4, ev);
-    }
+  // the kernels' store order: every chunk's h, then every chunk's e
+#pragma unroll
+  for (int j = 0; j < kMixChunks; ++j) {
+    const int64_t c = ((int64_t)blockIdx.x * kMixChunks + j) * kProbeBlock + threadIdx.x;
+    if (c < n4) store4(h + c * 4, hns[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < kMixChunks; ++j) {
+    const int64_t c = ((int64_t)blockIdx.x * kMixChunks + j) * kProbeBlock + threadIdx.x;
+    if (c < n4) store4(e + c * 4, evs[j]);
   }
 }
 
