@@ -875,28 +875,28 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
     for (int p = 0; p < NP; ++p)
       *reinterpret_cast<f32x4*>(&S[lr * LDSW + SW * w + 32 * (p >> 1) + 8 * lk + 4 * (p & 1)]) = acc[p];
     __syncthreads();
+    // every row's ahat, then (sender) every row's e: one array at a time
+    f32x4 hn[NI], ev[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int tr = 4 * w + RPI * i + ri;
-      const int row = r0 + tr;
       const f32x4 c = *reinterpret_cast<const f32x4*>(&S[tr * LDSW + lc]);
-      if (row < rend && col_ok) {
-        const size_t off = tb + (size_t)row * m;
-        f32x4 hn;
-        if constexpr (SENDER) {
-          f32x4 ev;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float r = T.x[i][t] - T.h[i][t];
-            ev[t] = r - c[t];
-            hn[t] = T.h[i][t] + c[t];
-          }
-          store4(e + off, ev);
-        } else {
+      for (int t = 0; t < 4; ++t) {
+        hn[i][t] = T.h[i][t] + c[t];
+        if constexpr (SENDER) ev[i][t] = (T.x[i][t] - T.h[i][t]) - c[t];
+      }
+    }
 #pragma unroll
-          for (int t = 0; t < 4; ++t) hn[t] = T.h[i][t] + c[t];
-        }
-        store4(ahat + off, hn);
+    for (int i = 0; i < NI; ++i) {
+      const int row = r0 + 4 * w + RPI * i + ri;
+      if (row < rend && col_ok) store4(ahat + tb + (size_t)row * m, hn[i]);
+    }
+    if constexpr (SENDER) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int row = r0 + 4 * w + RPI * i + ri;
+        if (row < rend && col_ok) store4(e + tb + (size_t)row * m, ev[i]);
       }
     }
   };
