@@ -40,8 +40,12 @@ hipError_t launch_nm_decompress(const PeerSet& peers, int batch, const Layout& L
 // Low-rank workspace, carved out of one device allocation by the plan.
 // ntiles = ceil(rows / 64); rows_pad = 64 * ntiles; the R^T P product splits
 // the rows into nsplit chunks of split_rows (a multiple of 32).
+// rank is the width the iteration runs at (every piece below is sized by it);
+// pay_rank (<= rank) is the rank the payload carries. Rank 8 runs at width 16
+// with start-matrix columns 8 .. 15 zero: those columns stay exactly zero, are
+// declared dead by every CholeskyQR pass and are not sent.
 struct LowRankWork {
-  int rank = 0, iters = 0;
+  int rank = 0, pay_rank = 0, iters = 0;
   bool bf16_factors = false;  // factors sent as bf16 instead of INT4 + scales
   int64_t ntiles = 0, rows_pad = 0;
   int nsplit = 1, split_rows = 0;

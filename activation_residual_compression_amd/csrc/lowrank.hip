@@ -343,7 +343,7 @@ __device__ __forceinline__ float lane_f32(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-template <int K>
+template <int K, int KP>
 __global__ __launch_bounds__(64) void lr_chol_kernel(const float* __restrict__ gsum,
                                                      float* __restrict__ linv) {
   constexpr int LDc = K + 4;  // 16-B aligned rows of L in LDS
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(64) void lr_chol_kernel(const float* __restrict__ g
   float tr = 0.f;
 #pragma unroll
   for (int j = 0; j < K; ++j) tr += lane_f32(g[j], j);
-  const float tol = ldexpf(fmaxf(tr, (float)K * FLT_MIN), -23);
+  const float tol = ldexpf(fmaxf(tr, (float)KP * FLT_MIN), -23);  // KP: the rank asked for
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     float s = g[j];                       // G[lane][j] - sum_p L[lane][p] L[j][p]
@@ -667,7 +667,7 @@ __global__ __launch_bounds__(256) void lr_qfinish_kernel(const float* __restrict
 // element t in nibble t (even t low), two's complement. Block 0 writes the
 // scale sections and zeroes the section padding. Sender and receiver both
 // reconstruct from these packed bytes (q * s_j, in the reconstruct kernel).
-template <int K>
+template <int K, int KP>
 __global__ __launch_bounds__(256) void lr_int4_kernel(const float* __restrict__ P,
                                                       const float* __restrict__ Qt,
                                                       const uint32_t* __restrict__ amax,
@@ -681,8 +681,8 @@ __global__ __launch_bounds__(256) void lr_int4_kernel(const float* __restrict__ 
   if (blockIdx.x == 0) {
     float* su = reinterpret_cast<float*>(pk + L.sec_off[2]);
     float* sv = reinterpret_cast<float*>(pk + L.sec_off[3]);
-    if (threadIdx.x < K) su[threadIdx.x] = sc[threadIdx.x];
-    else if (threadIdx.x < 2 * K) sv[threadIdx.x - K] = sc[threadIdx.x];
+    if (threadIdx.x < KP) su[threadIdx.x] = sc[threadIdx.x];
+    else if (threadIdx.x >= K && threadIdx.x < K + KP) sv[threadIdx.x - K] = sc[threadIdx.x];
     for (int s = 0; s < L.nsec; ++s) {
       const int64_t start = L.sec_off[s] + L.sec_len[s];
       const int64_t end = (s + 1 < L.nsec) ? L.sec_off[s + 1] : L.tstride;
@@ -694,39 +694,39 @@ __global__ __launch_bounds__(256) void lr_int4_kernel(const float* __restrict__ 
   const bool isV = r >= n;
   const int i = isV ? r - n : r;
   const float* s = sc + (isV ? K : 0);
-  // the whole factor row is loaded before any of it is quantised
-  float x[K];
+  // the whole factor row (its KP sent columns) is loaded before any of it is quantised
+  float x[KP];
   if (isV) {
     const float* src = Qt + (size_t)b * K * m + i;
 #pragma unroll
-    for (int j = 0; j < K; ++j) x[j] = src[(size_t)j * m];
+    for (int j = 0; j < KP; ++j) x[j] = src[(size_t)j * m];
   } else {
     const f32x4* src = reinterpret_cast<const f32x4*>(P + ((size_t)b * n + i) * K);
 #pragma unroll
-    for (int j = 0; j < K / 4; ++j) {
+    for (int j = 0; j < KP / 4; ++j) {
       const f32x4 v = src[j];
       x[4 * j] = v.x; x[4 * j + 1] = v.y; x[4 * j + 2] = v.z; x[4 * j + 3] = v.w;
     }
   }
-  uint32_t words[K / 8];
+  uint32_t words[KP / 8];
 #pragma unroll
-  for (int q = 0; q < K / 8; ++q) words[q] = 0;
+  for (int q = 0; q < KP / 8; ++q) words[q] = 0;
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
+  for (int j = 0; j < KP; ++j) {
     int qi = 0;
     if (s[j] > 0.f) qi = (int)fminf(fmaxf(rintf(x[j] / s[j]), -7.f), 7.f);
     words[j / 8] |= ((uint32_t)qi & 0xFu) << (4 * (j % 8));
   }
-  uint32_t* dst = reinterpret_cast<uint32_t*>(pk + (isV ? L.sec_off[1] : L.sec_off[0]) + (size_t)i * (K / 2));
+  uint32_t* dst = reinterpret_cast<uint32_t*>(pk + (isV ? L.sec_off[1] : L.sec_off[0]) + (size_t)i * (KP / 2));
 #pragma unroll
-  for (int q = 0; q < K / 8; ++q) dst[q] = words[q];
+  for (int q = 0; q < KP / 8; ++q) dst[q] = words[q];
 }
 
 // ---------------------------------------------------------------- bf16 factors
 // The factor-precision alternative: U and V sent as bf16 (round to nearest
 // even), row-major, no scales. One lane per factor row as above; sender and
 // receiver reconstruct from the bf16 values.
-template <int K>
+template <int K, int KP>
 __global__ __launch_bounds__(256) void lr_bf16f_kernel(const float* __restrict__ P,
                                                        const float* __restrict__ Qt,
                                                        uint8_t* __restrict__ packed, Layout L) {
@@ -746,9 +746,9 @@ __global__ __launch_bounds__(256) void lr_bf16f_kernel(const float* __restrict__
   const int i = isV ? r - n : r;
   const float* src = isV ? Qt + (size_t)b * K * m + i : P + ((size_t)b * n + i) * K;
   const size_t stride = isV ? (size_t)m : 1;
-  uint32_t* dst = reinterpret_cast<uint32_t*>(pk + (isV ? L.sec_off[1] : L.sec_off[0]) + (size_t)i * K * 2);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(pk + (isV ? L.sec_off[1] : L.sec_off[0]) + (size_t)i * KP * 2);
 #pragma unroll
-  for (int j = 0; j < K; j += 2) dst[j / 2] = bf16_rne(src[j * stride]) | (bf16_rne(src[(j + 1) * stride]) << 16);
+  for (int j = 0; j < KP; j += 2) dst[j / 2] = bf16_rne(src[j * stride]) | (bf16_rne(src[(j + 1) * stride]) << 16);
 }
 
 // ---------------------------------------------------------------- reconstruct
@@ -777,13 +777,15 @@ __global__ __launch_bounds__(256) void lr_bf16f_kernel(const float* __restrict__
 
 // Factor entries (row, k0 .. k0+3) as the encoder defined them: INT4 code times
 // the column scale (scale4 = the 4 scales of k0 .. k0+3), or the bf16 value.
-template <int K, bool BF16F>
+// Rows hold KP entries; columns k0 >= KP are not sent and are zero.
+template <int KP, bool BF16F>
 __device__ __forceinline__ f32x4 factor4(const uint8_t* sec, const f32x4& scale4, int row, int k0) {
+  if (k0 >= KP) return f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (BF16F) {
-    const u32x2 w = *reinterpret_cast<const u32x2*>(sec + ((size_t)row * K + k0) * 2);
+    const u32x2 w = *reinterpret_cast<const u32x2*>(sec + ((size_t)row * KP + k0) * 2);
     return f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
   } else {
-    const uint32_t w = *reinterpret_cast<const uint16_t*>(sec + ((size_t)row * K + k0) / 2);
+    const uint32_t w = *reinterpret_cast<const uint16_t*>(sec + ((size_t)row * KP + k0) / 2);
     f32x4 v;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -794,7 +796,7 @@ __device__ __forceinline__ f32x4 factor4(const uint8_t* sec, const f32x4& scale4
   }
 }
 
-template <typename IN, bool SENDER, int K, bool BF16F, int CW>
+template <typename IN, bool SENDER, int K, int KP, bool BF16F, int CW>
 __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
                                                        float* __restrict__ e, PeerSet peers,
                                                        int batch, Layout L, int chunk_rows) {
@@ -827,6 +829,8 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
   for (int j = 0; j < KJ; ++j) {
     if constexpr (BF16F) {
       su[j] = sv[j] = f32x4{1.f, 1.f, 1.f, 1.f};
+    } else if (16 * j + 4 * lk >= KP) {
+      su[j] = sv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     } else {
       su[j] = *reinterpret_cast<const f32x4*>(pk + L.sec_off[2] + 4 * (16 * j + 4 * lk));
       sv[j] = *reinterpret_cast<const f32x4*>(pk + L.sec_off[3] + 4 * (16 * j + 4 * lk));
@@ -837,7 +841,7 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
   for (int p = 0; p < NP; ++p) {
     const int col = (strip_ok ? c0 : 0) + 32 * (p >> 1) + 8 * (lr >> 2) + 4 * (p & 1) + (lr & 3);
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) av[p][j] = factor4<K, BF16F>(vsec, sv[j], col, 16 * j + 4 * lk);
+    for (int j = 0; j < KJ; ++j) av[p][j] = factor4<KP, BF16F>(vsec, sv[j], col, 16 * j + 4 * lk);
   }
   const size_t tb = (size_t)b * n * m + (size_t)(col_ok ? cb + lc : 0);
 
@@ -850,7 +854,7 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
   auto load = [&](int r0, Rows& R) {
     const int ru = min(r0 + lr, rend - 1);
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) R.u[j] = factor4<K, BF16F>(usec, su[j], ru, 16 * j + 4 * lk);
+    for (int j = 0; j < KJ; ++j) R.u[j] = factor4<KP, BF16F>(usec, su[j], ru, 16 * j + 4 * lk);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const size_t off = tb + (size_t)min(r0 + 4 * w + RPI * i + ri, rend - 1) * m;
@@ -939,26 +943,26 @@ inline RcGrid rc_grid(int n, int m, int B, int k) {
 }
 
 // One reconstruct launch with the column width chosen at run time.
-template <typename IN, bool SENDER, int K, bool BF16F>
+template <typename IN, bool SENDER, int K, int KP, bool BF16F>
 void launch_recon(const RcGrid& g, hipStream_t s, const IN* a, float* e, const PeerSet& peers,
                   int batch, const Layout& L) {
   if (g.cw == 128)
-    hipLaunchKernelGGL((lr_recon_kernel<IN, SENDER, K, BF16F, 128>), g.grid, dim3(256), 0, s, a, e,
+    hipLaunchKernelGGL((lr_recon_kernel<IN, SENDER, K, KP, BF16F, 128>), g.grid, dim3(256), 0, s, a, e,
                        peers, batch, L, g.chunk_rows);
   else
-    hipLaunchKernelGGL((lr_recon_kernel<IN, SENDER, K, BF16F, 256>), g.grid, dim3(256), 0, s, a, e,
+    hipLaunchKernelGGL((lr_recon_kernel<IN, SENDER, K, KP, BF16F, 256>), g.grid, dim3(256), 0, s, a, e,
                        peers, batch, L, g.chunk_rows);
 }
 
 // ---------------------------------------------------------------- launchers
 namespace {
 
-template <int K>
+template <int K, int KP>
 void cqr_pass(const LowRankWork& w, int n, int B, bool final_pass, hipStream_t s) {
   const int nt = (int)w.ntiles, rp = (int)w.rows_pad;
   hipLaunchKernelGGL((lr_gram_reduce_kernel<K>), dim3((K * K + 255) / 256, B), dim3(256), 0, s,
                      w.gpart, w.gsum, nt);
-  hipLaunchKernelGGL((lr_chol_kernel<K>), dim3(B), dim3(64), 0, s, w.gsum, w.linv);
+  hipLaunchKernelGGL((lr_chol_kernel<K, KP>), dim3(B), dim3(64), 0, s, w.gsum, w.linv);
   if (final_pass)
     hipLaunchKernelGGL((lr_solve_kernel<K, false, true>), dim3(nt, B), dim3(256), 0, s, w.P, w.linv,
                        w.gpart, w.Pbt, w.amax, n, nt, rp);
@@ -967,7 +971,7 @@ void cqr_pass(const LowRankWork& w, int n, int B, bool final_pass, hipStream_t s
                        w.gpart, w.Pbt, w.amax, n, nt, rp);
 }
 
-template <int K>
+template <int K, int KP>
 hipError_t lr_compress_k(bool bf16, const void* a, float* ahat, float* e, uint8_t* packed, int B,
                          const Layout& L, const LowRankWork& w, hipStream_t s) {
   const int n = (int)L.rows, m = (int)L.cols;
@@ -988,8 +992,8 @@ hipError_t lr_compress_k(bool bf16, const void* a, float* ahat, float* e, uint8_
                          (const uint16_t*)nullptr, (const float*)nullptr, w.R, w.Qtb, w.P, w.gpart,
                          w.amax, n, m, nt);
     }
-    cqr_pass<K>(w, n, B, false, s);
-    cqr_pass<K>(w, n, B, true, s);
+    cqr_pass<K, KP>(w, n, B, false, s);
+    cqr_pass<K, KP>(w, n, B, true, s);
     hipLaunchKernelGGL((lr_rtp_kernel<K>), dim3((m + kRtpCols - 1) / kRtpCols, w.nsplit, B),
                        dim3(256), 0, s, w.R, w.Pbt, w.qpart, n, m, rp, w.nsplit, w.split_rows);
     if (it + 1 == w.iters)
@@ -1000,10 +1004,10 @@ hipError_t lr_compress_k(bool bf16, const void* a, float* ahat, float* e, uint8_
                          s, w.qpart, w.Qt, w.Qtb, w.amax, m, w.nsplit);
   }
   if (w.bf16_factors)
-    hipLaunchKernelGGL((lr_bf16f_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, w.P,
+    hipLaunchKernelGGL((lr_bf16f_kernel<K, KP>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, w.P,
                        w.Qt, packed, L);
   else
-    hipLaunchKernelGGL((lr_int4_kernel<K>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, w.P,
+    hipLaunchKernelGGL((lr_int4_kernel<K, KP>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, w.P,
                        w.Qt, w.amax, packed, L);
   PeerSet self{};
   self.packed[0] = packed;
@@ -1011,19 +1015,19 @@ hipError_t lr_compress_k(bool bf16, const void* a, float* ahat, float* e, uint8_
   self.count = 1;
   const RcGrid g = rc_grid(n, m, B, K);
   if (bf16 && w.bf16_factors)
-    launch_recon<uint16_t, true, K, true>(g, s, static_cast<const uint16_t*>(a), e, self, B, L);
+    launch_recon<uint16_t, true, K, KP, true>(g, s, static_cast<const uint16_t*>(a), e, self, B, L);
   else if (bf16)
-    launch_recon<uint16_t, true, K, false>(g, s, static_cast<const uint16_t*>(a), e, self, B, L);
+    launch_recon<uint16_t, true, K, KP, false>(g, s, static_cast<const uint16_t*>(a), e, self, B, L);
   else if (w.bf16_factors)
-    launch_recon<float, true, K, true>(g, s, static_cast<const float*>(a), e, self, B, L);
+    launch_recon<float, true, K, KP, true>(g, s, static_cast<const float*>(a), e, self, B, L);
   else
-    launch_recon<float, true, K, false>(g, s, static_cast<const float*>(a), e, self, B, L);
+    launch_recon<float, true, K, KP, false>(g, s, static_cast<const float*>(a), e, self, B, L);
   return hipGetLastError();
 }
 
 // Receiver: every peer's tensors in one launch (grid z = peer * batch + tensor),
 // split into several launches only if that exceeds the grid's z limit.
-template <int K>
+template <int K, int KP>
 hipError_t lr_decompress_k(const PeerSet& peers, int B, const Layout& L, const LowRankWork& w,
                            hipStream_t s) {
   const int n = (int)L.rows, m = (int)L.cols;
@@ -1038,9 +1042,9 @@ hipError_t lr_decompress_k(const PeerSet& peers, int B, const Layout& L, const L
     }
     g.grid.z = (unsigned)(B * sub.count);
     if (w.bf16_factors)
-      launch_recon<float, false, K, true>(g, s, nullptr, nullptr, sub, B, L);
+      launch_recon<float, false, K, KP, true>(g, s, nullptr, nullptr, sub, B, L);
     else
-      launch_recon<float, false, K, false>(g, s, nullptr, nullptr, sub, B, L);
+      launch_recon<float, false, K, KP, false>(g, s, nullptr, nullptr, sub, B, L);
   }
   return hipGetLastError();
 }
@@ -1052,10 +1056,12 @@ hipError_t launch_lr_compress(bool bf16_input, const void* a, float* ahat, float
                               hipStream_t s) {
   if (L.cols % 64) return hipErrorInvalidValue;
   switch (w.rank) {
-    case 16: return lr_compress_k<16>(bf16_input, a, ahat, e, packed, batch, L, w, s);
-    case 32: return lr_compress_k<32>(bf16_input, a, ahat, e, packed, batch, L, w, s);
-    case 48: return lr_compress_k<48>(bf16_input, a, ahat, e, packed, batch, L, w, s);
-    case 64: return lr_compress_k<64>(bf16_input, a, ahat, e, packed, batch, L, w, s);
+    case 16:
+      return w.pay_rank == 8 ? lr_compress_k<16, 8>(bf16_input, a, ahat, e, packed, batch, L, w, s)
+                             : lr_compress_k<16, 16>(bf16_input, a, ahat, e, packed, batch, L, w, s);
+    case 32: return lr_compress_k<32, 32>(bf16_input, a, ahat, e, packed, batch, L, w, s);
+    case 48: return lr_compress_k<48, 48>(bf16_input, a, ahat, e, packed, batch, L, w, s);
+    case 64: return lr_compress_k<64, 64>(bf16_input, a, ahat, e, packed, batch, L, w, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1064,10 +1070,12 @@ hipError_t launch_lr_decompress(const PeerSet& peers, int batch, const Layout& L
                                 const LowRankWork& w, hipStream_t s) {
   if (L.cols % 64) return hipErrorInvalidValue;
   switch (w.rank) {
-    case 16: return lr_decompress_k<16>(peers, batch, L, w, s);
-    case 32: return lr_decompress_k<32>(peers, batch, L, w, s);
-    case 48: return lr_decompress_k<48>(peers, batch, L, w, s);
-    case 64: return lr_decompress_k<64>(peers, batch, L, w, s);
+    case 16:
+      return w.pay_rank == 8 ? lr_decompress_k<16, 8>(peers, batch, L, w, s)
+                             : lr_decompress_k<16, 16>(peers, batch, L, w, s);
+    case 32: return lr_decompress_k<32, 32>(peers, batch, L, w, s);
+    case 48: return lr_decompress_k<48, 48>(peers, batch, L, w, s);
+    case 64: return lr_decompress_k<64, 64>(peers, batch, L, w, s);
   }
   return hipErrorInvalidValue;
 }

@@ -108,7 +108,7 @@ rc_status_t validate(const rc_shape_t& sh, rc_dtype_t dtype, rc_scheme_t scheme,
       return RC_OK;
     case RC_LOWRANK:
       if (p->rank < 1 || p->iters < 1 || p->iters > 16 || !p->q0) return RC_ERR_INVALID_ARG;
-      if (p->rank % 16 || p->rank > 64) return RC_ERR_UNSUPPORTED;
+      if (p->rank != 8 && (p->rank % 16 || p->rank > 64)) return RC_ERR_UNSUPPORTED;
       if (p->rank > sh.rows || p->rank > sh.cols) return RC_ERR_INVALID_ARG;
       if (sh.cols % 64) return RC_ERR_INVALID_ARG;
       return RC_OK;
@@ -133,11 +133,13 @@ uint16_t host_bf16(float x) {
 }
 
 rc_status_t setup_lowrank(rc_plan* pl, const float* q0) {
-  const int64_t B = pl->shape.batch, n = pl->shape.rows, m = pl->shape.cols, k = pl->params.rank;
+  const int64_t B = pl->shape.batch, n = pl->shape.rows, m = pl->shape.cols;
+  const int64_t kp = pl->params.rank, k = kp < 16 ? 16 : kp;  // payload rank, iteration width
   // carve the workspace: every piece 256-byte aligned
   struct Piece { void** dst; int64_t bytes; };
   rc::LowRankWork& w = pl->lr;
   w.rank = (int)k;
+  w.pay_rank = (int)kp;
   w.iters = pl->params.iters;
   w.bf16_factors = (pl->params.flags & RC_LR_BF16_FACTORS) != 0;
   w.ntiles = (n + 63) / 64;
@@ -173,11 +175,12 @@ rc_status_t setup_lowrank(rc_plan* pl, const float* q0) {
     *pc.dst = (char*)pl->ws + off;
     off += align_up(pc.bytes);
   }
-  // Q0 [B][m][k] fp32 (host) -> bf16 Q0^T [B][k][m] (device), uploaded once.
-  std::vector<uint16_t> t((size_t)(B * k * m));
+  // Q0 [B][m][kp] fp32 (host) -> bf16 Q0^T [B][k][m] (device), uploaded once;
+  // rows kp .. k-1 of Q0^T stay zero.
+  std::vector<uint16_t> t((size_t)(B * k * m), 0);
   for (int64_t b = 0; b < B; ++b)
     for (int64_t c = 0; c < m; ++c)
-      for (int64_t j = 0; j < k; ++j) t[(size_t)((b * k + j) * m + c)] = host_bf16(q0[(b * m + c) * k + j]);
+      for (int64_t j = 0; j < kp; ++j) t[(size_t)((b * k + j) * m + c)] = host_bf16(q0[(b * m + c) * kp + j]);
   err = hipMemcpy(w.Q0t, t.data(), t.size() * 2, hipMemcpyHostToDevice);
   if (err != hipSuccess) return RC_ERR_HIP;
   return RC_OK;

@@ -17,7 +17,7 @@ the library on a synthetic workload and reports, per configuration:
   tensors_per_ms batch / ms_per_step
 
 Usage: python -m activation_residual_compression_amd.lr_sweep [--workload flux_lr]
-       [--ranks 16,32,48,64] [--iters 1,2,3,4] [--factors int4,bf16] [--md OUT]
+       [--ranks 8,16,32,48,64] [--iters 1,2,3,4] [--factors int4,bf16] [--md OUT]
 """
 from __future__ import annotations
 
@@ -108,7 +108,7 @@ def markdown(rows):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="flux_lr")
-    ap.add_argument("--ranks", default="16,32,48,64")
+    ap.add_argument("--ranks", default="8,16,32,48,64")
     ap.add_argument("--iters", default="1,2,3,4")
     ap.add_argument("--factors", default="int4,bf16")
     ap.add_argument("--frames", type=int, default=3)

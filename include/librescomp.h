@@ -75,7 +75,7 @@ typedef struct {
   int32_t group;    /* RC_Q1 / RC_Q2: group size along cols: 32, 64 or 128       */
   int32_t nm_keep;  /* RC_NM: kept per block, must be 2                           */
   int32_t nm_block; /* RC_NM: block size, must be 16                              */
-  int32_t rank;     /* RC_LOWRANK: 16, 32, 48 or 64                               */
+  int32_t rank;     /* RC_LOWRANK: 8, 16, 32, 48 or 64, at most rows and cols     */
   int32_t iters;    /* RC_LOWRANK: subspace iterations, 1..16                     */
   const float* q0;  /* RC_LOWRANK: HOST fp32 [batch][cols][rank] start matrices;  */
                     /*   copied at plan creation and reused every step           */

@@ -37,7 +37,8 @@ int rcx_hbm_probe(int kind, const void* a, void* b, void* c, int64_t n, hipStrea
 
 /* Device pointers of a low-rank plan's workspace pieces, in the order R, P,
  * Pbt, Qt, Q0t, Qtb, gsum, linv (count >= 8). Returns rows_pad, or -1 for a
- * NULL plan, another scheme, or count < 8. */
+ * NULL plan, another scheme, or count < 8. The pieces are as wide as the
+ * iteration: max(rank, 16) (rank 8 runs 16 wide with columns 8 .. 15 zero). */
 int rcx_lowrank_workspace(rc_plan_t plan, void** ptrs, int count);
 
 #ifdef __cplusplus

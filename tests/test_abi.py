@@ -50,6 +50,8 @@ def test_status_strings(rc):
     ("nm", dict(nm_keep=2, nm_block=16), dict(nm_block=1)),
     ("lr", dict(rank=32, iters=2), dict(q0=None)),
     ("lr", dict(rank=32, iters=2), dict(rank=24)),
+    ("lr", dict(rank=32, iters=2), dict(rank=4)),
+    ("lr", dict(rank=32, iters=2), dict(rank=80)),
     ("lr", dict(rank=32, iters=2), dict(iters=0)),
 ])
 def test_plan_validation(rc, scheme, kw, bad):
@@ -90,6 +92,15 @@ def test_packed_sizes_match_oracle_layout(rc, scheme, kw, shape):
         assert p.tensor_packed_bytes == want
         assert p.packed_bytes == b * want
         assert p.workspace_bytes == 0
+
+
+def test_lowrank_rank8_rejected_above_rows(rc):
+    # rank 8 is accepted (the GPU parity tests run it) but, as every rank,
+    # never above the rows or columns of the tensor; checked before allocating
+    q0 = np.zeros((2, 256, 8), np.float32)
+    with pytest.raises(rc.RcError) as ei:
+        rc.Plan((2, 6, 256), "bf16", "lr", rank=8, iters=2, q0=q0)   # rank > rows
+    assert ei.value.status == rc.RC_ERR_INVALID_ARG
 
 
 def test_lowrank_packed_size_formula():

@@ -80,7 +80,7 @@ def _run_lr(wl, rank, iters, check, steps=None, code_agree=0.8, factors="int4"):
         run.close()
 
 
-@pytest.mark.parametrize("rank,iters", [(16, 1), (16, 2), (32, 2)])
+@pytest.mark.parametrize("rank,iters", [(8, 2), (16, 1), (16, 2), (32, 2)])
 def test_lr_ragged_small(rank, iters):
     wl = synth.FluxWorkload(batch=2, n=100, m=192, steps=4)
     _run_lr(wl, rank, iters, check=[0, 1])
@@ -93,7 +93,7 @@ def test_lr_several_tiles_ragged_both_ways():
     _run_lr(wl, 32, 2, check=[0, 2])
 
 
-@pytest.mark.parametrize("rank,iters", [(16, 2), (32, 1)])
+@pytest.mark.parametrize("rank,iters", [(8, 2), (16, 2), (32, 1)])
 def test_lr_bf16_factors_ragged(rank, iters):
     wl = synth.FluxWorkload(batch=2, n=100, m=192, steps=4)
     _run_lr(wl, rank, iters, check=[0, 1], factors="bf16", code_agree=0.95)
