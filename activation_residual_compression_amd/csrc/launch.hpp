@@ -38,8 +38,7 @@ hipError_t launch_nm_compress(bool bf16_input, const void* a, float* ahat, float
 hipError_t launch_nm_decompress(const PeerSet& peers, int batch, const Layout& L, hipStream_t s);
 
 // Low-rank workspace, carved out of one device allocation by the plan.
-// ntiles = ceil(rows / 64); rows_pad = 64 * ntiles; the R^T P product splits
-// the rows into nsplit chunks of split_rows (a multiple of 32).
+// ntiles = ceil(rows / 64); rows_pad = 64 * ntiles.
 // rank is the width the iteration runs at (every piece below is sized by it);
 // pay_rank (<= rank) is the rank the payload carries. Rank 8 runs at width 16
 // with start-matrix columns 8 .. 15 zero: those columns stay exactly zero, are
@@ -48,7 +47,6 @@ struct LowRankWork {
   int rank = 0, pay_rank = 0, iters = 0;
   bool bf16_factors = false;  // factors sent as bf16 instead of INT4 + scales
   int64_t ntiles = 0, rows_pad = 0;
-  int nsplit = 1, split_rows = 0;
   uint16_t* R = nullptr;     // bf16 residual: 64 x 128 tiles, column chunk, then tensor, then band (per launch)
   float* P = nullptr;        // fp32 panel [batch][rows][rank]
   uint16_t* Pbt = nullptr;   // bf16 orthonormal panel, transposed [batch][rank][rows_pad]
@@ -58,7 +56,6 @@ struct LowRankWork {
   float* gpart = nullptr;    // per-64-row-tile Gram partials [batch][ntiles][rank][rank]
   float* gsum = nullptr;     // summed Gram matrices [batch][rank][rank]
   float* linv = nullptr;     // inverse Cholesky factor, dead rows zeroed [batch][rank][rank]
-  float* qpart = nullptr;    // R^T P partials [batch][nsplit][rank][cols]
   uint32_t* amax = nullptr;  // column absmax bits of U and V [batch][2][rank]
 };
 

@@ -14,7 +14,7 @@
 //     P = R * bf16(Q)        bf16 MFMA, fp32 accumulate            [lr_rq_kernel]
 //     P = CQR(CQR(P))        CholeskyQR2 of the n x k panel        [lr_gram_reduce_kernel,
 //                                                                    lr_chol_kernel, lr_solve_kernel]
-//     Q = R^T * bf16(P)      bf16 MFMA, R transposed through LDS   [lr_rtp_kernel, lr_qfinish_kernel]
+//     Q = R^T * bf16(P)      bf16 MFMA, R transposed through LDS   [lr_rtp_kernel]
 //   U = P, V = Q; per-column absmax INT4                          [lr_int4_kernel]
 //   c = Uq Vq^T (fp32 MFMA), e = r - c, ahat += c                 [lr_recon_kernel]
 // CQR(P): G = P^T P (fp32 MFMA on 64-row tiles, tile partials summed in tile
@@ -489,49 +489,53 @@ __global__ __launch_bounds__(256) void lr_solve_kernel(float* __restrict__ P,
 }
 
 // ---------------------------------------------------------------- Q = R^T P
-// Block: 128 columns x one row split of one tensor; wave w owns columns
+// Block: 128 columns of one tensor over all of its rows; wave w owns columns
 // 32w .. 32w+31 (two 16-column MFMA tiles). Per step of 32 rows the R tile
 // [32 x 128] and the matching P^T chunk [K x 32] are staged through LDS
 // (double buffered, one barrier per step). R is read back transposed with
 // ds_read_b64_tr_b16 (A[c][i] = R[i][c]); each P^T fragment read from LDS
-// feeds both column tiles of the wave. The split's partial Q^T goes to qpart;
-// lr_qfinish_kernel sums the splits. A last block of 64 columns (cols % 128 ==
-// 64) computes its missing half from reread valid columns and stores only the
-// valid ones.
+// feeds both column tiles of the wave. A last block of 64 columns (cols % 128
+// == 64) computes its missing half from reread valid columns and stores only
+// the valid ones.
+// The block writes its columns of Q^T itself. Before the last iteration Q is
+// needed only as the bf16 operand of the next product (Qtb); after it, only as
+// V: Qt in fp32 and the column absmax of V folded into amax[b][1][j] (FINAL).
+// Splitting the rows over several blocks (and summing the splits in a second
+// kernel) was measured slower on both low-rank workloads: the products gain
+// less from the larger grid than the sum costs.
 constexpr int kRtpCols = 128;
 constexpr int kRtpLd = kRtpCols + 8;  // bf16 per staged R row (272 B)
 constexpr int kRtpPld = 32 + 8;       // bf16 per staged P^T row (80 B)
 
-template <int K>
+template <int K, bool FINAL>
 __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict__ R,
                                                      const uint16_t* __restrict__ Pbt,
-                                                     float* __restrict__ qpart, int n, int m,
-                                                     int rows_pad, int nsplit, int split_rows) {
+                                                     float* __restrict__ Qt,
+                                                     uint16_t* __restrict__ Qtb,
+                                                     uint32_t* __restrict__ amax, int n, int m,
+                                                     int rows_pad) {
   constexpr int NT = K / 16;
   constexpr int PCH = K * 4;  // 16-byte chunks of a [K x 32] bf16 P^T block
   __shared__ __attribute__((aligned(16))) uint16_t sR[2][32 * kRtpLd];
   __shared__ __attribute__((aligned(16))) uint16_t sP[2][K * kRtpPld];
-  // Logical blocks (column block fastest, then split, then tensor) are spread
-  // over the XCDs in contiguous ranges, so the column blocks that share a P^T
-  // chunk share an L2. Tensors and row splits are taken in the reverse of that
-  // order: every XCD's range of the R*Q pass before this one ran forwards, so
-  // the tensors this pass starts with are the ones that pass read last and are
-  // still in the device's last-level cache (the next forward pass finds this
-  // pass's in turn).
-  const int nblk = gridDim.x * gridDim.y * gridDim.z;
-  int lin = xcd_contiguous(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), nblk);
+  // Logical blocks (column block fastest, then tensor) are spread over the
+  // XCDs in contiguous ranges, so the column blocks that share a P^T chunk
+  // share an L2. Tensors are taken in the reverse of that order: every XCD's
+  // range of the R*Q pass before this one ran forwards, so the tensors this
+  // pass starts with are the ones that pass read last and are still in the
+  // device's last-level cache (the next forward pass finds this pass's in turn).
+  const int nblk = gridDim.x * gridDim.y;
+  const int lin = xcd_contiguous(blockIdx.x + gridDim.x * blockIdx.y, nblk);
   const int cb = lin % gridDim.x;
-  lin /= gridDim.x;
-  const int b = gridDim.z - 1 - lin / gridDim.y, split = gridDim.y - 1 - lin % gridDim.y;
+  const int b = gridDim.y - 1 - lin / gridDim.x;
   const int c0 = cb * kRtpCols;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
   // R staging: each wave-wide load covers 4 whole 256-byte row pieces (16 lanes
   // x 16 bytes per row); loads q = 0, 1 take rows ld_row and ld_row + 16
   const int ld_row = threadIdx.x >> 4, ld_col = (threadIdx.x & 15) * 8;
   const bool col_ok = c0 + ld_col < m;
-  const int i_begin = split * split_rows;
-  const int i_end = min(rows_pad, i_begin + split_rows);
-  const int batch = gridDim.z, bands = rows_pad >> 6;
+  const int i_end = rows_pad;
+  const int batch = gridDim.y, bands = rows_pad >> 6;
   const uint16_t* Pb = Pbt + (size_t)b * K * rows_pad;
   const int tr_off = (8 * lk + (lr >> 2)) * kRtpLd + 32 * w + 4 * (lr & 3);
 
@@ -589,8 +593,8 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
 
   // LDS double buffer, one barrier per step: a buffer is refilled two steps
   // after it was read, and every wave has passed the barrier in between.
-  Stage s0 = gload(i_begin), s1 = gload(i_begin + 32);
-  int i0 = i_begin;
+  Stage s0 = gload(0), s1 = gload(32);
+  int i0 = 0;
   for (; i0 + 32 < i_end; i0 += 64) {
     put(s0, 0);
     __syncthreads();
@@ -607,56 +611,44 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
     compute(0);
   }
   // D[c][j]: lane holds c = c0 + 32w + 16ct + 4lk + t, j = 16g + lr
-  float* qp = qpart + ((size_t)b * nsplit + split) * K * m;
+  float mx[NT];
+#pragma unroll
+  for (int g = 0; g < NT; ++g) mx[g] = 0.f;
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int c = c0 + 32 * w + 16 * ct + 4 * lk;
-    if (c < m)
+    if (c < m) {
 #pragma unroll
-      for (int g = 0; g < NT; ++g) *reinterpret_cast<f32x4*>(qp + (size_t)(16 * g + lr) * m + c) = acc[ct][g];
-  }
-}
-
-// Sum the row splits (at most 8) in split order. Before the last iteration the
-// sum is needed only as the bf16 operand of the next product (Qtb); after it,
-// only as V: Qt in fp32 and the column absmax of V folded into amax[b][1][j].
-// Block: one j, 1024 columns (4 per lane).
-template <int K, bool FINAL>
-__global__ __launch_bounds__(256) void lr_qfinish_kernel(const float* __restrict__ qpart,
-                                                         float* __restrict__ Qt,
-                                                         uint16_t* __restrict__ Qtb,
-                                                         uint32_t* __restrict__ amax, int m,
-                                                         int nsplit) {
-  const int b = blockIdx.z, j = blockIdx.x;
-  const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
-  float mx = 0.f;
-  if (c < m) {
-    // every split's partial is loaded before the first add (indices past
-    // nsplit reread the last split and are not added)
-    const float* base = qpart + ((size_t)b * nsplit * K + j) * m + c;
-    f32x4 v[8];
-#pragma unroll
-    for (int sp = 0; sp < 8; ++sp)
-      v[sp] = *reinterpret_cast<const f32x4*>(base + (size_t)min(sp, nsplit - 1) * K * m);
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int sp = 0; sp < 8; ++sp)
-      if (sp < nsplit) s += v[sp];
-    const size_t o = ((size_t)b * K + j) * m + c;
-    if constexpr (FINAL) {
-      *reinterpret_cast<f32x4*>(Qt + o) = s;
-      mx = fmaxf(fmaxf(fabsf(s.x), fabsf(s.y)), fmaxf(fabsf(s.z), fabsf(s.w)));
-    } else {
-      uint2 hb;
-      hb.x = bf16_rne(s.x) | (bf16_rne(s.y) << 16);
-      hb.y = bf16_rne(s.z) | (bf16_rne(s.w) << 16);
-      *reinterpret_cast<uint2*>(Qtb + o) = hb;
+      for (int g = 0; g < NT; ++g) {
+        const f32x4 v = acc[ct][g];
+        const size_t o = ((size_t)b * K + 16 * g + lr) * m + c;
+        if constexpr (FINAL) {
+          *reinterpret_cast<f32x4*>(Qt + o) = v;
+          mx[g] = fmaxf(mx[g], fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        } else {
+          uint2 hb;
+          hb.x = bf16_rne(v.x) | (bf16_rne(v.y) << 16);
+          hb.y = bf16_rne(v.z) | (bf16_rne(v.w) << 16);
+          *reinterpret_cast<uint2*>(Qtb + o) = hb;
+        }
+      }
     }
   }
   if constexpr (FINAL) {
+    // column j's maximum over the wave's 32 columns, then over the 4 waves
+    __shared__ float cm[4 * K];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    if ((threadIdx.x & 63) == 0) atomicMax(amax + ((size_t)b * 2 + 1) * K + j, __float_as_uint(mx));
+    for (int g = 0; g < NT; ++g) {
+      mx[g] = fmaxf(mx[g], __shfl_xor(mx[g], 16));
+      mx[g] = fmaxf(mx[g], __shfl_xor(mx[g], 32));
+      if (lk == 0) cm[w * K + 16 * g + lr] = mx[g];
+    }
+    __syncthreads();
+    const int j = threadIdx.x;
+    if (j < K) {
+      const float v = fmaxf(fmaxf(cm[j], cm[K + j]), fmaxf(cm[2 * K + j], cm[3 * K + j]));
+      atomicMax(amax + ((size_t)b * 2 + 1) * K + j, __float_as_uint(v));
+    }
   }
 }
 
@@ -994,14 +986,13 @@ hipError_t lr_compress_k(bool bf16, const void* a, float* ahat, float* e, uint8_
     }
     cqr_pass<K, KP>(w, n, B, false, s);
     cqr_pass<K, KP>(w, n, B, true, s);
-    hipLaunchKernelGGL((lr_rtp_kernel<K>), dim3((m + kRtpCols - 1) / kRtpCols, w.nsplit, B),
-                       dim3(256), 0, s, w.R, w.Pbt, w.qpart, n, m, rp, w.nsplit, w.split_rows);
+    const dim3 rtp_grid((m + kRtpCols - 1) / kRtpCols, B);
     if (it + 1 == w.iters)
-      hipLaunchKernelGGL((lr_qfinish_kernel<K, true>), dim3(K, (m + 1023) / 1024, B), dim3(256), 0,
-                         s, w.qpart, w.Qt, w.Qtb, w.amax, m, w.nsplit);
+      hipLaunchKernelGGL((lr_rtp_kernel<K, true>), rtp_grid, dim3(256), 0, s, w.R, w.Pbt, w.Qt,
+                         w.Qtb, w.amax, n, m, rp);
     else
-      hipLaunchKernelGGL((lr_qfinish_kernel<K, false>), dim3(K, (m + 1023) / 1024, B), dim3(256), 0,
-                         s, w.qpart, w.Qt, w.Qtb, w.amax, m, w.nsplit);
+      hipLaunchKernelGGL((lr_rtp_kernel<K, false>), rtp_grid, dim3(256), 0, s, w.R, w.Pbt, w.Qt,
+                         w.Qtb, w.amax, n, m, rp);
   }
   if (w.bf16_factors)
     hipLaunchKernelGGL((lr_bf16f_kernel<K, KP>), dim3((n + m + 255) / 256, B), dim3(256), 0, s, w.P,

@@ -144,12 +144,6 @@ rc_status_t setup_lowrank(rc_plan* pl, const float* q0) {
   w.bf16_factors = (pl->params.flags & RC_LR_BF16_FACTORS) != 0;
   w.ntiles = (n + 63) / 64;
   w.rows_pad = 64 * w.ntiles;
-  // split the rows of the R^T P product so that the launch has >= ~2048 blocks
-  const int64_t col_blocks = ((m + 127) / 128) * B;
-  int64_t split = (2048 + col_blocks - 1) / col_blocks;
-  split = split < 1 ? 1 : (split > 8 ? 8 : split);
-  w.split_rows = (int)(((w.rows_pad + split - 1) / split + 31) / 32 * 32);
-  w.nsplit = (int)((w.rows_pad + w.split_rows - 1) / w.split_rows);
   Piece pieces[] = {
       {(void**)&w.R, B * w.rows_pad * ((m + 127) / 128 * 128) * 2},
       {(void**)&w.P, B * n * k * 4},
@@ -160,7 +154,6 @@ rc_status_t setup_lowrank(rc_plan* pl, const float* q0) {
       {(void**)&w.gpart, B * w.ntiles * k * k * 4},
       {(void**)&w.gsum, B * k * k * 4},
       {(void**)&w.linv, B * k * k * 4},
-      {(void**)&w.qpart, B * w.nsplit * k * m * 4},
       {(void**)&w.amax, B * 2 * k * 4},
   };
   int64_t total = 0;
@@ -220,7 +213,6 @@ rc::LowRankWork lr_slice(const rc::LowRankWork& w, const rc::Layout& L, int64_t 
   s.gpart += b0 * w.ntiles * k * k;
   s.gsum += b0 * k * k;
   s.linv += b0 * k * k;
-  s.qpart += b0 * w.nsplit * k * m;
   s.amax += b0 * 2 * k;
   return s;
 }
