@@ -328,17 +328,17 @@ __global__ __launch_bounds__(256) void lr_gram_reduce_kernel(const float* __rest
 }
 
 // ---------------------------------------------------------------- Cholesky
-// One wave per tensor: lane i holds row i of G (from the upper triangle of
-// gsum) and builds row i of L by the left-looking recurrence; lane c builds
-// column c of L^{-1} by forward substitution. Step j of both needs row j of L
-// up to column j-1, which every lane reads from LDS as uniform-address
-// broadcasts, four entries per read, and the two dot products run as
-// independent chains. Dead columns (pivot <= 2^-23 * max(trace G, K *
-// FLT_MIN)) get L[j][j] = 1, a zero column below the diagonal and a zero row
-// j of L^{-1}, so x = L^{-1} p has x_j = 0 there and the other entries are
-// those of the forward substitution. Both dot products are fused multiply-add
-// chains in index order; divisions by L[j][j] are products with its correctly
-// rounded reciprocal.
+// One wave per tensor, no LDS and no barriers: lane i holds row i of G (from
+// the upper triangle of gsum) and builds row i of L by the left-looking
+// recurrence; lane c builds column c of L^{-1} by forward substitution. Step j
+// of both needs row j of L up to column j-1, which lives in lane j's
+// registers: each entry is broadcast with one readlane and feeds both dot
+// products, which run as independent chains. Dead columns (pivot <= 2^-23 *
+// max(trace G, K * FLT_MIN)) get L[j][j] = 1, a zero column below the diagonal
+// and a zero row j of L^{-1}, so x = L^{-1} p has x_j = 0 there and the other
+// entries are those of the forward substitution. Both dot products are fused
+// multiply-add chains in index order; divisions by L[j][j] are products with
+// its correctly rounded reciprocal.
 __device__ __forceinline__ float lane_f32(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
@@ -346,8 +346,6 @@ __device__ __forceinline__ float lane_f32(float v, int lane) {
 template <int K, int KP>
 __global__ __launch_bounds__(64) void lr_chol_kernel(const float* __restrict__ gsum,
                                                      float* __restrict__ linv) {
-  constexpr int LDc = K + 4;  // 16-B aligned rows of L in LDS
-  __shared__ __attribute__((aligned(16))) float Ls[K * LDc];
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const float* gs = gsum + (size_t)b * K * K;
@@ -364,18 +362,13 @@ __global__ __launch_bounds__(64) void lr_chol_kernel(const float* __restrict__ g
   const float tol = ldexpf(fmaxf(tr, (float)KP * FLT_MIN), -23);  // KP: the rank asked for
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    float s = g[j];                       // G[lane][j] - sum_p L[lane][p] L[j][p]
-    float t = (j == lane) ? 1.f : 0.f;    // e_lane[j] - sum_q L[j][q] y[q]
-    const f32x4* Lj = reinterpret_cast<const f32x4*>(Ls + j * LDc);
+    float s = g[j];                     // G[lane][j] - sum_p L[lane][p] L[j][p]
+    float t = (j == lane) ? 1.f : 0.f;  // e_lane[j] - sum_p L[j][p] y[p]
 #pragma unroll
-    for (int q = 0; q < (j + 3) / 4; ++q) {
-      const f32x4 v = Lj[q];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (4 * q + u < j) {
-          s = fmaf(-L[4 * q + u], v[u], s);
-          t = fmaf(-v[u], y[4 * q + u], t);
-        }
+    for (int p = 0; p < j; ++p) {
+      const float ljp = lane_f32(L[p], j);  // L[j][p]
+      s = fmaf(-L[p], ljp, s);
+      t = fmaf(-ljp, y[p], t);
     }
     const float piv = lane_f32(s, j);
     const bool dj = !(piv > tol);
@@ -383,11 +376,7 @@ __global__ __launch_bounds__(64) void lr_chol_kernel(const float* __restrict__ g
     const float inv = 1.0f / ljj;
     L[j] = lane == j ? ljj : (lane > j && !dj ? s * inv : 0.f);
     y[j] = dj ? 0.f : t * inv;
-    if (lane < K) {
-      Ls[lane * LDc + j] = L[j];
-      out[(size_t)j * K] = y[j];  // stored here, so the chain is not deferred to the end
-    }
-    __syncthreads();
+    if (lane < K) out[(size_t)j * K] = y[j];  // stored here, so the chain is not deferred to the end
   }
 }
 

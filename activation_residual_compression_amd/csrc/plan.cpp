@@ -23,6 +23,12 @@ struct rc_plan {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   rc::LowRankWork lr;
+  // low rank, batch >= 2: rc_compress runs the second half of the batch on a
+  // stream of the plan's own, forked from and joined back to the caller's
+  // stream with these events, so that one half's latency-bound factorisation
+  // kernels overlap the other half's streaming kernels
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
   // block selection: fp64 row partial sums [B][K][8][3] (scratch) and round state, in ws
   rc::BlockSel bs;
   double* bs_score = nullptr;
@@ -176,6 +182,20 @@ rc_status_t setup_lowrank(rc_plan* pl, const float* q0) {
       for (int64_t j = 0; j < kp; ++j) t[(size_t)((b * k + j) * m + c)] = host_bf16(q0[(b * m + c) * kp + j]);
   err = hipMemcpy(w.Q0t, t.data(), t.size() * 2, hipMemcpyHostToDevice);
   if (err != hipSuccess) return RC_ERR_HIP;
+  if (B >= 2) {
+    if (hipStreamCreateWithFlags(&pl->side, hipStreamNonBlocking) != hipSuccess) {
+      pl->side = nullptr;
+      return RC_ERR_HIP;
+    }
+    if (hipEventCreateWithFlags(&pl->fork, hipEventDisableTiming) != hipSuccess) {
+      pl->fork = nullptr;
+      return RC_ERR_HIP;
+    }
+    if (hipEventCreateWithFlags(&pl->join, hipEventDisableTiming) != hipSuccess) {
+      pl->join = nullptr;
+      return RC_ERR_HIP;
+    }
+  }
   return RC_OK;
 }
 
@@ -306,8 +326,22 @@ rc_status_t rc_compress(rc_plan_t pl, hipStream_t stream, const void* a_t, const
   if (!pl || !a_t || !state || !state->ahat || !state->e || !packed_out) return RC_ERR_INVALID_ARG;
   if (!aligned16(a_t) || !aligned16(state->ahat) || !aligned16(state->e) || !aligned16(packed_out))
     return RC_ERR_ALIGNMENT;
-  const hipError_t err = compress_range(pl, stream, a_t, state, static_cast<uint8_t*>(packed_out), 0,
-                                        pl->shape.batch);
+  uint8_t* packed = static_cast<uint8_t*>(packed_out);
+  const int B = pl->shape.batch;
+  if (!pl->side) {
+    const hipError_t err = compress_range(pl, stream, a_t, state, packed, 0, B);
+    return err == hipSuccess ? RC_OK : RC_ERR_HIP;
+  }
+  // low rank: first half on the caller's stream, second half on the plan's
+  // stream, which starts after everything already on `stream` and which
+  // `stream` waits for before anything enqueued after this call
+  const int h = (B + 1) / 2;
+  if (hipEventRecord(pl->fork, stream) != hipSuccess) return RC_ERR_HIP;
+  if (hipStreamWaitEvent(pl->side, pl->fork, 0) != hipSuccess) return RC_ERR_HIP;
+  hipError_t err = compress_range(pl, stream, a_t, state, packed, 0, h);
+  if (err == hipSuccess) err = compress_range(pl, pl->side, a_t, state, packed, h, B - h);
+  if (hipEventRecord(pl->join, pl->side) != hipSuccess) return RC_ERR_HIP;
+  if (hipStreamWaitEvent(stream, pl->join, 0) != hipSuccess) return RC_ERR_HIP;
   return err == hipSuccess ? RC_OK : RC_ERR_HIP;
 }
 
@@ -386,6 +420,9 @@ rc_status_t rc_plan_destroy(rc_plan_t pl) {
     if (pl->ws) {
       if (hipSetDevice(pl->device) != hipSuccess) st = RC_ERR_HIP;
       if (hipFree(pl->ws) != hipSuccess) st = RC_ERR_HIP;
+      if (pl->side && hipStreamDestroy(pl->side) != hipSuccess) st = RC_ERR_HIP;
+      if (pl->fork && hipEventDestroy(pl->fork) != hipSuccess) st = RC_ERR_HIP;
+      if (pl->join && hipEventDestroy(pl->join) != hipSuccess) st = RC_ERR_HIP;
     }
     (void)hipSetDevice(cur);
   }

@@ -29,8 +29,10 @@
  *     host. Calls on one plan must be serialised on one stream (the low-rank
  *     and block-selection schemes keep per-plan device workspace and state).
  *     Separate plans share nothing and may run concurrently on separate streams.
- *   - On any error nothing is launched and no buffer is touched; the return
- *     value says why. RC_ERR_HIP reports a failed kernel launch.
+ *   - A rejected request (RC_ERR_INVALID_ARG, RC_ERR_UNSUPPORTED,
+ *     RC_ERR_ALIGNMENT) launches nothing and touches no buffer. RC_ERR_HIP
+ *     reports a failed HIP call or kernel launch; the outputs of that call are
+ *     then unspecified.
  *   - Inputs holding NaN or Inf give unspecified (but memory-safe) results.
  */
 #ifndef LIBRESCOMP_H
@@ -125,7 +127,11 @@ rc_status_t rc_plan_create(rc_shape_t shape, rc_dtype_t dtype, rc_scheme_t schem
  * them, so a receiver that applies packed_out stays bit-identical to ahat.
  * a_t: [batch][rows][cols] of the plan's dtype. state->ahat is read and
  * updated in place, state->e is written. packed_out: rc_packed_bytes(plan)
- * bytes, written completely (padding included). */
+ * bytes, written completely (padding included).
+ * RC_LOWRANK with batch >= 2 runs the second half of the batch on a stream the
+ * plan owns: it starts after the work already enqueued on `stream`, and
+ * `stream` waits for it before the work enqueued after this call (events; this
+ * also holds under stream capture). The results are those of one stream. */
 rc_status_t rc_compress(rc_plan_t plan, hipStream_t stream, const void* a_t, const rc_state_t* state,
                         void* packed_out);
 
