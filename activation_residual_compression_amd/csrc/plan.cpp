@@ -97,7 +97,7 @@ rc_status_t validate(const rc_shape_t& sh, rc_dtype_t dtype, rc_scheme_t scheme,
   if (sh.batch > 65535) return RC_ERR_UNSUPPORTED;  // one grid row per tensor
   if ((int64_t)sh.batch * sh.rows * sh.cols >= kMaxElems) return RC_ERR_UNSUPPORTED;
   if (dtype != RC_BF16 && dtype != RC_F32) return RC_ERR_INVALID_ARG;
-  const uint32_t allowed = scheme == RC_LOWRANK ? RC_LR_BF16_FACTORS : 0u;
+  const uint32_t allowed = scheme == RC_LOWRANK ? (RC_LR_BF16_FACTORS | RC_LR_ONE_STREAM) : 0u;
   if (p->flags & ~allowed) return RC_ERR_INVALID_ARG;
   switch (scheme) {
     case RC_Q1:
@@ -182,7 +182,7 @@ rc_status_t setup_lowrank(rc_plan* pl, const float* q0) {
       for (int64_t j = 0; j < kp; ++j) t[(size_t)((b * k + j) * m + c)] = host_bf16(q0[(b * m + c) * kp + j]);
   err = hipMemcpy(w.Q0t, t.data(), t.size() * 2, hipMemcpyHostToDevice);
   if (err != hipSuccess) return RC_ERR_HIP;
-  if (B >= 2) {
+  if (B >= 2 && !(pl->params.flags & RC_LR_ONE_STREAM)) {
     if (hipStreamCreateWithFlags(&pl->side, hipStreamNonBlocking) != hipSuccess) {
       pl->side = nullptr;
       return RC_ERR_HIP;

@@ -24,6 +24,7 @@ RC_BF16, RC_F32 = 0, 1
 RC_Q1, RC_Q2, RC_NM, RC_LOWRANK, RC_BLOCKSEL = 0, 1, 2, 3, 4
 RC_MAX_PEERS = 8
 RC_LR_BF16_FACTORS = 1  # rc_params_t.flags, RC_LOWRANK only
+RC_LR_ONE_STREAM = 2    # rc_params_t.flags, RC_LOWRANK only: no second stream in rc_compress
 
 SCHEMES = {"q1": RC_Q1, "q2": RC_Q2, "nm": RC_NM, "lr": RC_LOWRANK, "bs": RC_BLOCKSEL}
 DTYPES = {"bf16": RC_BF16, "f32": RC_F32}

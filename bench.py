@@ -200,7 +200,8 @@ def _ms(x):
     return "-" if x is None else "%.3f" % x
 
 
-def measure(config, steps, warmup, max_frames, log, exchange_chunks=(), overlap=True):
+def measure(config, steps, warmup, max_frames, log, exchange_chunks=(), overlap=True,
+            lr_one_stream=False):
     import numpy as np
     import torch
 
@@ -229,6 +230,8 @@ def measure(config, steps, warmup, max_frames, log, exchange_chunks=(), overlap=
           if k in spec}
     if spec["scheme"] == "lr":
         kw["q0"] = wl.q0(spec["rank"])
+        if lr_one_stream:
+            kw["flags"] = rc.RC_LR_ONE_STREAM
     plan = rc.Plan((B, n, m), wl.dtype, spec["scheme"], **kw)
     ahat = frames[0].float().clone()
     recon = ahat.clone()
@@ -270,6 +273,7 @@ def measure(config, steps, warmup, max_frames, log, exchange_chunks=(), overlap=
     if spec["scheme"] == "lr":
         fl = lr_flops(n, m, spec["rank"], spec["iters"], B)
         out["tensors_per_ms"] = B / ms_step
+        out["compress_streams"] = 1 if (lr_one_stream or B < 2) else 2
         out["mfma_flops"] = fl
         out["mfma_util_whole_compress"] = fl / (c_ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
     # Steady state of one GPU in a sequence-parallel group: its own compress of
@@ -401,6 +405,9 @@ def main():
     ap.add_argument("--no-exchange", action="store_true",
                     help="skip the compress + hand-off pipeline timing and the two-stream "
                          "compress/decode overlap (both run kernels concurrently)")
+    ap.add_argument("--lr-one-stream", action="store_true",
+                    help="low-rank plans keep every compress kernel on one stream (per-kernel "
+                         "traces without the two half-batch streams overlapping)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -438,7 +445,7 @@ def main():
     ceiling = None if args.no_hbm_probe else hbm_probe(_wl.batch * _wl.n * _wl.m, log)
     main_res = measure(args.workload, args.steps, args.warmup, 64, log,
                        exchange_chunks=() if args.no_exchange else (4, 8, 19),
-                       overlap=not args.no_exchange)
+                       overlap=not args.no_exchange, lr_one_stream=args.lr_one_stream)
     log("[bench] %s: %.3f ms/step, %.1f GB/s input, compress %.3f ms (%.0f GB/s alg), "
         "graph replay %.3f ms/step, compress/decode overlapped %s ms/step" % (
             args.workload, main_res["ms_per_step"], main_res["input_GBps"], main_res["compress_ms"],
@@ -447,7 +454,7 @@ def main():
     for cfg in [c for c in args.also.split(",") if c and c != args.workload]:
         r = measure(cfg, args.steps, args.warmup, args.also_frames, log,
                     exchange_chunks=(8, 19) if (cfg == "flux_lr" and not args.no_exchange) else (),
-                    overlap=not args.no_exchange)
+                    overlap=not args.no_exchange, lr_one_stream=args.lr_one_stream)
         log("[bench] %s: %.3f ms/step, %.1f GB/s input (graph replay %.3f, compress/decode "
             "overlapped %s ms/step)" % (cfg, r["ms_per_step"], r["input_GBps"],
                                        r["graph_ms_per_step"], _ms(r["overlapped_ms_per_step"])))

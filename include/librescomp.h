@@ -81,7 +81,7 @@ typedef struct {
   int32_t iters;    /* RC_LOWRANK: subspace iterations, 1..16                     */
   const float* q0;  /* RC_LOWRANK: HOST fp32 [batch][cols][rank] start matrices;  */
                     /*   copied at plan creation and reused every step           */
-  uint32_t flags;   /* 0, or RC_LOWRANK with RC_LR_BF16_FACTORS                   */
+  uint32_t flags;   /* 0, or RC_LOWRANK: RC_LR_BF16_FACTORS | RC_LR_ONE_STREAM     */
   int32_t grid_w;      /* RC_BLOCKSEL: tokens per row of the spatial token grid     */
   int32_t keep_blocks; /* RC_BLOCKSEL: blocks sent per tensor and step (k)          */
 } rc_params_t;
@@ -93,6 +93,13 @@ typedef struct {
  * factors of rank 4k). Packed layout per tensor: U bf16 [rows*rank] | V bf16
  * [cols*rank], row-major, each section 256-byte aligned. */
 #define RC_LR_BF16_FACTORS 1u
+
+/* rc_params_t.flags for RC_LOWRANK: keep every kernel of rc_compress on the
+ * caller's stream. By default a plan with batch >= 2 owns a second stream and
+ * runs half of the batch there (see rc_compress); the results are the same bit
+ * for bit either way. For callers that want one stream, and for per-kernel
+ * traces without overlapping kernels. */
+#define RC_LR_ONE_STREAM 2u
 
 typedef struct {
   float* ahat; /* sender's copy of the receiver reconstruction, fp32 [batch][rows][cols] */

@@ -53,6 +53,8 @@ def test_status_strings(rc):
     ("lr", dict(rank=32, iters=2), dict(rank=4)),
     ("lr", dict(rank=32, iters=2), dict(rank=80)),
     ("lr", dict(rank=32, iters=2), dict(iters=0)),
+    ("lr", dict(rank=32, iters=2), dict(flags=4)),                # unknown flag
+    ("q2", dict(group=128), dict(flags=2)),                       # a low-rank flag
 ])
 def test_plan_validation(rc, scheme, kw, bad):
     kw = dict(kw)

@@ -67,3 +67,33 @@ def test_plans_on_separate_streams_match_sequential_run():
             assert np.array_equal(bits(a[key]) if key != "packed" else a[key],
                                   bits(b[key]) if key != "packed" else b[key]), (scheme, key)
         assert np.array_equal(bits(a["recon"]), bits(a["ahat"])), scheme
+
+
+def test_lowrank_two_stream_compress_matches_one_stream():
+    # batch >= 2: by default half of the batch runs on the plan's own stream;
+    # RC_LR_ONE_STREAM keeps it on the caller's. Both must give the same bits,
+    # and an odd batch splits unevenly (3 + 2 tensors).
+    wl = synth.FluxWorkload(batch=5, n=200, m=320, steps=STEPS + 1)
+    fr = _frames(wl)
+    q0 = wl.q0(32)
+    out = []
+    for flags in (0, rc.RC_LR_ONE_STREAM):
+        say("[gpu] streams: low rank flags %d" % flags)
+        s = torch.cuda.Stream()
+        with rc.Plan((wl.nb, wl.n, wl.m), wl.dtype, "lr", rank=32, iters=2, q0=q0, flags=flags) as p:
+            ahat = fr[0].float().clone()
+            e = torch.zeros_like(ahat)
+            recon = ahat.clone()
+            packed = torch.zeros(p.packed_bytes, dtype=torch.uint8, device=DEV)
+            steps = []
+            for t in range(1, STEPS + 1):
+                p.compress(fr[t], ahat, e, packed, s)
+                p.decompress(packed, recon, s)
+                s.synchronize()
+                steps.append((packed.cpu().numpy(), bits(ahat.cpu().numpy()), bits(e.cpu().numpy()),
+                              bits(recon.cpu().numpy())))
+            out.append(steps)
+    for t, (a, b) in enumerate(zip(*out)):
+        for i, key in enumerate(("packed", "ahat", "e", "recon")):
+            assert np.array_equal(a[i], b[i]), (t, key)
+        assert np.array_equal(a[1], a[3]), t
