@@ -35,11 +35,11 @@ SENDER_KERNEL = {
     "video_q1": "q_compress_kernel<unsigned short, 64, 1,",
     "tiny_q1": "q_compress_kernel<float, 64, 1,",
 }
-LR_CONTRACTIONS = {  # (kernel, launches per step) of the bf16 MFMA products
+LR_CONTRACTIONS = {  # (kernel, launches per step) of the bf16 MFMA products, whole-batch launches
     "flux_lr": [("lr_rq_kernel<unsigned short, true, 32>", 1), ("lr_rq_kernel<unsigned short, false, 32>", 1),
-                ("lr_rtp_kernel<32>", 2)],
+                ("lr_rtp_kernel<32, false>", 1), ("lr_rtp_kernel<32, true>", 1)],
     "video_lr": [("lr_rq_kernel<unsigned short, true, 48>", 1), ("lr_rq_kernel<unsigned short, false, 48>", 1),
-                 ("lr_rtp_kernel<48>", 2)],
+                 ("lr_rtp_kernel<48, false>", 1), ("lr_rtp_kernel<48, true>", 1)],
 }
 
 
@@ -474,7 +474,9 @@ def main():
         if len(hits) == 1:
             kname = hits[0]
             traffic = pmc["kernels"][kname]["bytes"]
-    trace = _fresh_profile("bench_workloads_kernel_trace.json")
+    # the low-rank products' durations come from the one-stream trace (one
+    # launch per kernel for the whole batch, nothing overlapping)
+    trace = _fresh_profile("lowrank_flux_video_kernel_trace.json")
     for cfg, res in others.items():
         if cfg in LR_CONTRACTIONS and trace:
             ks = LR_CONTRACTIONS[cfg]
