@@ -43,15 +43,31 @@ LR_CONTRACTIONS = {  # (kernel, launches per step) of the bf16 MFMA products, wh
 }
 
 
-def _fresh_profile(name):
-    """A committed profile JSON, or None when the kernel sources changed since it was taken."""
+# Sources a kernel's traffic and duration depend on: its own file, the shared
+# device headers, and the host code that lays out the packed stream and drives
+# the launches.
+COMMON_SOURCES = ("device_common.hpp", "launch.hpp", "plan.cpp")
+KERNEL_SOURCES = {"q_": "quant.hip", "nm_": "nm.hip", "lr_": "lowrank.hip", "bs_": "blocksel.hip"}
+
+
+def _fresh_profile(name, kernel_prefix=None):
+    """A committed profile JSON, or None when sources it depends on changed since
+    it was taken: every kernel source, or (kernel_prefix) only that kernel's file
+    and the common ones."""
     import json as _json
     path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
     data = _json.load(open(path))
     from activation_residual_compression_amd.profsummary import source_hashes
-    return data if data.get("sources") == source_hashes() else None
+    now, then = source_hashes(), data.get("sources") or {}
+    if kernel_prefix is None:
+        return data if then == now else None
+    own = [f for p, f in KERNEL_SOURCES.items() if kernel_prefix.startswith(p)]
+    files = list(COMMON_SOURCES) + own
+    if len(own) != 1 or any(f not in now or then.get(f) != now[f] for f in files):
+        return None
+    return data
 
 
 def hbm_probe(n, log):
@@ -466,17 +482,17 @@ def main():
 
     ach = main_res["compress_GBps"]
     traffic = None
-    pmc = _fresh_profile("bench_workloads_hbm_traffic.json")
-    kname = None
     prefix = SENDER_KERNEL.get(args.workload)
-    if pmc and prefix:
+    pmc = _fresh_profile("bench_workloads_hbm_traffic.json", prefix) if prefix else None
+    kname = None
+    if pmc:
         hits = [k for k in pmc["kernels"] if k.startswith(prefix)]
         if len(hits) == 1:
             kname = hits[0]
             traffic = pmc["kernels"][kname]["bytes"]
     # the low-rank products' durations come from the one-stream trace (one
     # launch per kernel for the whole batch, nothing overlapping)
-    trace = _fresh_profile("lowrank_flux_video_kernel_trace.json")
+    trace = _fresh_profile("lowrank_flux_video_kernel_trace.json", "lr_")
     for cfg, res in others.items():
         if cfg in LR_CONTRACTIONS and trace:
             ks = LR_CONTRACTIONS[cfg]
