@@ -759,14 +759,28 @@ __global__ __launch_bounds__(256) void lr_bf16f_kernel(const float* __restrict__
 // Factor entries (row, k0 .. k0+3) as the encoder defined them: INT4 code times
 // the column scale (scale4 = the 4 scales of k0 .. k0+3), or the bf16 value.
 // Rows hold KP entries; columns k0 >= KP are not sent and are zero.
+// The raw bytes (factor_raw: 4 INT4 codes in the low 16 bits, or 4 bf16) are
+// loaded first and decoded at use (factor_decode), so loads in flight hold as
+// few registers as possible.
+template <bool BF16F>
+using FactorRaw = typename std::conditional<BF16F, u32x2, uint32_t>::type;
+
 template <int KP, bool BF16F>
-__device__ __forceinline__ f32x4 factor4(const uint8_t* sec, const f32x4& scale4, int row, int k0) {
-  if (k0 >= KP) return f32x4{0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ FactorRaw<BF16F> factor_raw(const uint8_t* sec, int row, int k0) {
   if constexpr (BF16F) {
-    const u32x2 w = *reinterpret_cast<const u32x2*>(sec + ((size_t)row * KP + k0) * 2);
+    if (k0 >= KP) return u32x2{0u, 0u};
+    return *reinterpret_cast<const u32x2*>(sec + ((size_t)row * KP + k0) * 2);
+  } else {
+    if (k0 >= KP) return 0u;
+    return *reinterpret_cast<const uint16_t*>(sec + ((size_t)row * KP + k0) / 2);
+  }
+}
+
+template <bool BF16F>
+__device__ __forceinline__ f32x4 factor_decode(const FactorRaw<BF16F>& w, const f32x4& scale4) {
+  if constexpr (BF16F) {
     return f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
   } else {
-    const uint32_t w = *reinterpret_cast<const uint16_t*>(sec + ((size_t)row * KP + k0) / 2);
     f32x4 v;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -775,6 +789,29 @@ __device__ __forceinline__ f32x4 factor4(const uint8_t* sec, const f32x4& scale4
     }
     return v;
   }
+}
+
+template <int KP, bool BF16F>
+__device__ __forceinline__ f32x4 factor4(const uint8_t* sec, const f32x4& scale4, int row, int k0) {
+  return factor_decode<BF16F>(factor_raw<KP, BF16F>(sec, row, k0), scale4);
+}
+
+// a_t as loaded (bf16 pairs or fp32), widened to fp32 at use.
+template <typename IN>
+using InRaw = typename std::conditional<std::is_same<IN, uint16_t>::value, u32x2, f32x4>::type;
+
+template <typename IN>
+__device__ __forceinline__ InRaw<IN> load_raw4(const IN* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const InRaw<IN>*>(p));
+}
+
+template <typename IN>
+__device__ __forceinline__ f32x4 widen4(const InRaw<IN>& w) {
+  if constexpr (std::is_same<IN, uint16_t>::value)
+    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+  else
+    return w;
 }
 
 template <typename IN, bool SENDER, int K, int KP, bool BF16F, int CW>
@@ -826,21 +863,30 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
   }
   const size_t tb = (size_t)b * n * m + (size_t)(col_ok ? cb + lc : 0);
 
+  // The receiver keeps the next tile's U operands as packed bytes until use
+  // (fewer registers: one more block per CU for k 48); the sender decodes them
+  // as they arrive (measured faster there).
+  using URow = typename std::conditional<SENDER, f32x4, FactorRaw<BF16F>>::type;
   struct Rows {
-    f32x4 u[KJ];  // U operands of the tile's 16 rows
-    f32x4 h[NI];  // ahat of this lane's rows and 4 columns
-    f32x4 x[NI];  // a_t of the same (SENDER)
+    URow u[KJ];              // U operands of the tile's 16 rows
+    f32x4 h[NI];             // ahat of this lane's rows and 4 columns
+    InRaw<IN> x[NI];         // a_t of the same, as loaded (SENDER)
   };
   // Rows past the chunk reread its last row and are never stored.
   auto load = [&](int r0, Rows& R) {
     const int ru = min(r0 + lr, rend - 1);
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) R.u[j] = factor4<KP, BF16F>(usec, su[j], ru, 16 * j + 4 * lk);
+    for (int j = 0; j < KJ; ++j) {
+      if constexpr (SENDER)
+        R.u[j] = factor4<KP, BF16F>(usec, su[j], ru, 16 * j + 4 * lk);
+      else
+        R.u[j] = factor_raw<KP, BF16F>(usec, ru, 16 * j + 4 * lk);
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const size_t off = tb + (size_t)min(r0 + 4 * w + RPI * i + ri, rend - 1) * m;
       R.h[i] = load4<float>(ahat + off);
-      if constexpr (SENDER) R.x[i] = load4<IN>(a + off);
+      if constexpr (SENDER) R.x[i] = load_raw4<IN>(a + off);
     }
   };
   auto apply = [&](int r0, int it, const Rows& T) {
@@ -849,11 +895,17 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
     for (int p = 0; p < NP; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (strip_ok) {
 #pragma unroll
-      for (int j = 0; j < KJ; ++j)
+      for (int j = 0; j < KJ; ++j) {
+        f32x4 u;
+        if constexpr (SENDER)
+          u = T.u[j];
+        else
+          u = factor_decode<BF16F>(T.u[j], su[j]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int p = 0; p < NP; ++p) acc[p] = mfma_f32(av[p][j][i], T.u[j][i], acc[p]);
+          for (int p = 0; p < NP; ++p) acc[p] = mfma_f32(av[p][j][i], u[i], acc[p]);
+      }
     }
     float* S = tile[it & 1];
 #pragma unroll
@@ -866,10 +918,12 @@ __global__ __launch_bounds__(256) void lr_recon_kernel(const IN* __restrict__ a,
     for (int i = 0; i < NI; ++i) {
       const int tr = 4 * w + RPI * i + ri;
       const f32x4 c = *reinterpret_cast<const f32x4*>(&S[tr * LDSW + lc]);
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (SENDER) x = widen4<IN>(T.x[i]);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         hn[i][t] = T.h[i][t] + c[t];
-        if constexpr (SENDER) ev[i][t] = (T.x[i][t] - T.h[i][t]) - c[t];
+        if constexpr (SENDER) ev[i][t] = (x[t] - T.h[i][t]) - c[t];
       }
     }
 #pragma unroll
