@@ -353,8 +353,9 @@ def measure(config, steps, warmup, max_frames, log, exchange_chunks=(), overlap=
     return out
 
 
-def cpu_baseline(config, budget_s, log):
-    """The oracle, untuned, single-threaded, on a bounded sample of the workload."""
+def cpu_baseline(config, budget_s, log, ntensors=24):
+    """The oracle, untuned, single-threaded, on a bounded sample of the workload
+    (its first ntensors tensors, step after step, until budget_s is spent)."""
     import numpy as np
 
     import oracle
@@ -365,7 +366,7 @@ def cpu_baseline(config, budget_s, log):
     if spec["scheme"] == "lr":
         kw.update(rank=spec["rank"], iters=spec["iters"])
     oracle.build(force=False)
-    tensors = list(range(24))
+    tensors = list(range(ntensors))
     wl = synth.make(config, tensors=tensors)
     _, a0 = wl.next()
     f32 = lambda a: (a.astype(np.uint32) << 16).view(np.float32) if wl.dtype == "bf16" else a
@@ -400,9 +401,9 @@ def cpu_baseline(config, budget_s, log):
     except OSError:
         pass
     return dict(value=gbps, unit="GB/s", cores=1, kind="oracle", cpu_model=model,
-                host_cpus=os.cpu_count(),
-                sample="%s: %d tensor-steps of %dx%d (tensors 0-23, steps 1-%d), compress+decompress, "
-                       "%.1f s single-threaded" % (config, done, wl.n, wl.m, t, elapsed))
+                host_cpus=os.cpu_count(), tensors_per_s=done / elapsed,
+                sample="%s: %d tensor-steps of %dx%d (tensors 0-%d, steps 1-%d), compress+decompress, "
+                       "%.1f s single-threaded" % (config, done, wl.n, wl.m, ntensors - 1, t, elapsed))
 
 
 def main():
@@ -416,6 +417,9 @@ def main():
     ap.add_argument("--also-frames", type=int, default=4,
                     help="distinct input frames for the other workloads (cycled)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--lr-cpu-budget", type=float, default=8.0,
+                    help="seconds of oracle time on the flux low-rank workload (reported "
+                         "under workloads.flux_lr.cpu_baseline; 0 to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-probe", action="store_true")
     ap.add_argument("--no-exchange", action="store_true",
@@ -479,6 +483,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.workload, args.cpu_budget, log)
+        if "flux_lr" in others and args.lr_cpu_budget > 0:
+            others["flux_lr"]["cpu_baseline"] = cpu_baseline("flux_lr", args.lr_cpu_budget, log,
+                                                             ntensors=6)
 
     ach = main_res["compress_GBps"]
     traffic = None
