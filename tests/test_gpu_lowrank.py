@@ -104,6 +104,15 @@ def test_lr_fp32_input_rank48():
     _run_lr(wl, 48, 2, check=[0, 1])
 
 
+@pytest.mark.parametrize("factors", ["int4", "bf16"])
+def test_lr_rank64_several_tiles(factors):
+    # the widest panel: four 16-column MFMA tiles; 200 rows (a ragged fourth
+    # 64-row tile), 320 columns (a half 128-column block of R)
+    wl = synth.FluxWorkload(batch=3, n=200, m=320, steps=3)
+    _run_lr(wl, 64, 2, check=[0, 2], factors=factors,
+            code_agree=0.95 if factors == "bf16" else 0.8)
+
+
 def test_lr_zero_and_rank_deficient_residuals():
     n, m, k = 70, 128, 16
     rng = np.random.default_rng(5)
