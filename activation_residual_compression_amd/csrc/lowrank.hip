@@ -22,6 +22,8 @@
 // the product P (L^{-1})^T (fp32 MFMA).
 // A pivot <= 2^-23 * max(trace G, k * FLT_MIN) marks a dead column, whose P
 // column is zeroed, so zero or rank-deficient residuals never produce NaN.
+// Rank 8 runs 16 wide with start columns 8 .. 15 zero (dead in every pass, k in
+// the pivot threshold is the rank asked for); only 8 columns are sent.
 //
 // MFMA register layouts (gfx950):
 //   v_mfma_f32_16x16x32_bf16: A lane l holds A[l%16][8(l/16) .. +7],
@@ -128,7 +130,7 @@ __device__ __forceinline__ size_t r_index(int b, int row, int col, int batch, in
 // tiles are summed through LDS as (w0 + w2) + (w1 + w3).
 // FROM_A: R = bf16(a_t - ahat) is formed while staging and written out for the
 // later passes. The block of tile 0 clears the tensor's INT4 absmax slots, which the
-// last solve and the last Q sum of the iteration fill.
+// iteration's last solve (U) and last R^T P pass (V) fill.
 constexpr int kRqStep = 128;        // columns per step
 constexpr int kRqLd = kRqStep + 8;  // bf16 per staged row (272 B)
 
