@@ -213,6 +213,10 @@ class Plan:
             import numpy as np
             q0 = np.ascontiguousarray(q0, dtype=np.float32)
             params["q0"] = q0
+            want = self.shape[0] * self.shape[2] * int(params.get("rank", 0))
+            if SCHEMES.get(scheme, scheme) == RC_LOWRANK and q0.size != want:
+                # the library reads batch * cols * rank floats through the pointer
+                raise ValueError("q0 holds %d floats; [batch][cols][rank] needs %d" % (q0.size, want))
         self._params = make_params(scheme, **params)
         self.handle = rc_plan_create(self.shape, dtype, scheme, self._params)
         self.packed_bytes = rc_packed_bytes(self.handle)

@@ -58,9 +58,9 @@ def test_status_strings(rc):
 ])
 def test_plan_validation(rc, scheme, kw, bad):
     kw = dict(kw)
-    if scheme == "lr":
-        kw["q0"] = np.zeros((2, 256, 32), np.float32)
     kw.update(bad)
+    if scheme == "lr" and "q0" not in bad:  # start matrices of the rank asked for
+        kw["q0"] = np.zeros((2, 256, max(kw["rank"], 1)), np.float32)
     with pytest.raises(rc.RcError) as ei:
         rc.Plan((2, 128, 256), "bf16", scheme, **kw)
     assert ei.value.status in (rc.RC_ERR_INVALID_ARG, rc.RC_ERR_UNSUPPORTED)
@@ -104,8 +104,15 @@ def test_lowrank_rank8_rejected_above_rows(rc):
         rc.Plan((2, 6, 256), "bf16", "lr", rank=8, iters=2, q0=q0)   # rank > rows
     assert ei.value.status == rc.RC_ERR_INVALID_ARG
     with pytest.raises(rc.RcError) as ei:                            # reconstruct grid limit
-        rc.Plan((1, 65535 * 64 + 1, 64), "bf16", "lr", rank=8, iters=2, q0=q0)
+        rc.Plan((1, 65535 * 64 + 1, 64), "bf16", "lr", rank=8, iters=2, q0=q0[:1, :64])
     assert ei.value.status == rc.RC_ERR_UNSUPPORTED
+
+
+def test_lowrank_q0_size_checked_by_binding(rc):
+    # the C library reads batch * cols * rank floats through the q0 pointer; the
+    # binding refuses an array of another size before the call
+    with pytest.raises(ValueError):
+        rc.Plan((2, 128, 256), "bf16", "lr", rank=16, iters=2, q0=np.zeros((2, 256, 8), np.float32))
 
 
 def test_lowrank_packed_size_formula():
