@@ -102,6 +102,30 @@ def _ptr(x):
     raise TypeError("cannot take a device pointer of %r" % type(x))
 
 
+def _dev_buffer(x, nbytes, what):
+    """Device pointer of x, checked when x is a tensor: on a GPU, contiguous and
+    at least nbytes long (the kernels would otherwise read or write past it, or
+    dereference host memory). Raw integers pass through unchecked."""
+    if hasattr(x, "data_ptr") and hasattr(x, "is_cuda"):
+        if not x.is_cuda:
+            raise ValueError("%s must be a device tensor" % what)
+        if not x.is_contiguous():
+            raise ValueError("%s must be contiguous" % what)
+        have = x.numel() * x.element_size()
+        if have < nbytes:
+            raise ValueError("%s holds %d bytes, the call needs %d" % (what, have, nbytes))
+    return _ptr(x)
+
+
+def _sized(x, nbytes, what):
+    """Pointer of x (device or pinned host), checked for size when x is a tensor."""
+    if hasattr(x, "numel") and hasattr(x, "element_size"):
+        have = x.numel() * x.element_size()
+        if have < nbytes:
+            raise ValueError("%s holds %d bytes, the call needs %d" % (what, have, nbytes))
+    return _ptr(x)
+
+
 def _stream(s):
     if s is None:
         import torch
@@ -223,19 +247,34 @@ class Plan:
         self.tensor_packed_bytes = rc_tensor_packed_bytes(self.handle)
         self.workspace_bytes = rc_workspace_bytes(self.handle)
 
+    def _elems(self):
+        return self.shape[0] * self.shape[1] * self.shape[2]
+
+    def _in_bytes(self):
+        return self._elems() * (2 if DTYPES.get(self.dtype, self.dtype) == RC_BF16 else 4)
+
     def compress(self, a_t, ahat, e, packed_out, stream=None):
-        st = rc_state_t(_ptr(ahat), _ptr(e))
-        rc_compress(self.handle, stream, a_t, st, packed_out)
+        st = rc_state_t(_dev_buffer(ahat, 4 * self._elems(), "ahat"),
+                        _dev_buffer(e, 4 * self._elems(), "e"))
+        rc_compress(self.handle, stream, _dev_buffer(a_t, self._in_bytes(), "a_t"), st,
+                    _dev_buffer(packed_out, self.packed_bytes, "packed_out"))
 
     def decompress(self, packed_in, recon_state, stream=None):
-        rc_decompress(self.handle, stream, packed_in, recon_state)
+        rc_decompress(self.handle, stream, _dev_buffer(packed_in, self.packed_bytes, "packed_in"),
+                      _dev_buffer(recon_state, 4 * self._elems(), "recon_state"))
 
     def compress_send(self, a_t, ahat, e, packed_out, packed_dst, chunk, copy_stream, stream=None):
-        st = rc_state_t(_ptr(ahat), _ptr(e))
-        rc_compress_send(self.handle, stream, copy_stream, a_t, st, packed_out, packed_dst, chunk)
+        st = rc_state_t(_dev_buffer(ahat, 4 * self._elems(), "ahat"),
+                        _dev_buffer(e, 4 * self._elems(), "e"))
+        rc_compress_send(self.handle, stream, copy_stream,
+                         _dev_buffer(a_t, self._in_bytes(), "a_t"), st,
+                         _dev_buffer(packed_out, self.packed_bytes, "packed_out"),
+                         _sized(packed_dst, self.packed_bytes, "packed_dst"), chunk)
 
     def decompress_many(self, packed_in, recon_states, stream=None):
-        rc_decompress_many(self.handle, stream, packed_in, recon_states)
+        rc_decompress_many(self.handle, stream,
+                           [_dev_buffer(p, self.packed_bytes, "packed_in") for p in packed_in],
+                           [_dev_buffer(r, 4 * self._elems(), "recon_state") for r in recon_states])
 
     def reset_state(self, stream=None):
         rc_plan_reset_state(self.handle, stream)

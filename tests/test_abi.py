@@ -174,3 +174,17 @@ def test_blocksel_validation_without_gpu(rc):
     assert status((1, 8192, 320), grid_w=128, keep_blocks=129) == rc.RC_ERR_INVALID_ARG
     assert status((1, 4096 * 64 + 64 * 64, 8), grid_w=64, keep_blocks=4) == rc.RC_ERR_UNSUPPORTED
     assert status((1, 8192 + 64 * 8, 320), grid_w=128, keep_blocks=4) == rc.RC_ERR_INVALID_ARG  # rows/grid_w % 8
+
+
+def test_binding_refuses_host_or_short_tensors(rc):
+    # host memory or a short buffer handed to the kernels would fault the GPU;
+    # the binding checks torch tensors before the call (no GPU needed here)
+    import torch
+    with rc.Plan((2, 8, 128), "bf16", "q2", group=128) as p:
+        a = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+        st = torch.zeros(2, 8, 128)
+        pk = torch.zeros(p.packed_bytes, dtype=torch.uint8)
+        with pytest.raises(ValueError, match="device tensor"):
+            p.compress(a, st, st.clone(), pk)
+        with pytest.raises(ValueError, match="device tensor"):
+            p.decompress(pk, st)

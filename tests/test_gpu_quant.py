@@ -178,3 +178,24 @@ def test_full_size_sampled_tensors(config):
     mid = wl.nb // 2
     _run_sequence(wl, spec["scheme"], group, tensors_checked=[0, mid, wl.nb - 1])
     torch.cuda.empty_cache()
+
+
+def test_binding_refuses_short_device_buffers():
+    # a short or strided state buffer would be written past its end; the binding
+    # checks torch tensors before calling the library, so nothing is launched
+    from gpu_harness import DEV
+    from activation_residual_compression_amd import librescomp as rc
+    with rc.Plan((2, 8, 128), "bf16", "q2", group=128) as p:
+        a = torch.zeros(2, 8, 128, dtype=torch.bfloat16, device=DEV)
+        ahat = torch.zeros(2, 8, 128, device=DEV)
+        e = torch.zeros(2, 8, 128, device=DEV)
+        pk = torch.zeros(p.packed_bytes, dtype=torch.uint8, device=DEV)
+        with pytest.raises(ValueError, match="needs"):
+            p.compress(a, ahat[:1], e, pk)
+        with pytest.raises(ValueError, match="needs"):
+            p.compress(a, ahat, e, pk[:-1])
+        with pytest.raises(ValueError, match="contiguous"):
+            p.compress(a, ahat.transpose(1, 2), e, pk)
+        p.compress(a, ahat, e, pk)  # the full-size call goes through
+        torch.cuda.synchronize()
+        assert int(ahat.abs().sum().item()) == 0
