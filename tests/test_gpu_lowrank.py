@@ -104,6 +104,14 @@ def test_lr_fp32_input_rank48():
     _run_lr(wl, 48, 2, check=[0, 1])
 
 
+@pytest.mark.parametrize("n,m,rank", [(40, 64, 16), (16, 64, 16), (64, 64, 32), (9, 128, 8)])
+def test_lr_smallest_shapes(n, m, rank):
+    # one partial 64-row tile, a single half-used 128-column block, rank up to
+    # the row count
+    wl = synth.FluxWorkload(batch=2, n=n, m=m, steps=3)
+    _run_lr(wl, rank, 2, check=[0, 1])
+
+
 @pytest.mark.parametrize("factors", ["int4", "bf16"])
 def test_lr_rank64_several_tiles(factors):
     # the widest panel: four 16-column MFMA tiles; 200 rows (a ragged fourth
