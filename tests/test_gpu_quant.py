@@ -68,6 +68,16 @@ def test_nm_ragged_shapes(dtype):
     _run_sequence(wl, "nm", None)
 
 
+@pytest.mark.parametrize("scheme,group,shape", [("q1", 32, (1, 1, 32)), ("q2", 128, (1, 1, 128)),
+                                                ("nm", None, (1, 1, 16)), ("q1", 32, (2, 3, 96)),
+                                                ("q2", 64, (5, 1, 64)), ("nm", None, (3, 2, 48))])
+def test_smallest_shapes(scheme, group, shape):
+    # a single group or block, and batches of one-row tensors: far less than
+    # one wave of the kernels' lane layout
+    b, n, m = shape
+    _run_sequence(synth.WalkWorkload(batch=b, n=n, m=m, steps=4), scheme, group)
+
+
 def _crafted(n, m, seed):
     """fp32 activations and a state whose residuals hold zeros of both signs,
     subnormals, exact ties, constant groups and equal-magnitude blocks (rows
