@@ -96,6 +96,13 @@ def test_latent_keep_sizes(keep):
     _run(wl, 64, keep, steps=5)
 
 
+@pytest.mark.parametrize("n,m,grid_w,keep", [(64, 4, 8, 1), (128, 8, 16, 1), (128, 4, 8, 2)])
+def test_smallest_grids(n, m, grid_w, keep):
+    # one 8 x 8 block (sent every step), one row of two blocks, and a column
+    # of two blocks sent together; 4 to 8 channels
+    _run(synth.WalkWorkload(batch=2, n=n, m=m, steps=4), grid_w, keep, steps=4)
+
+
 def test_fp32_input_and_ragged_round():
     # 24 x 48 grid: 3 x 6 = 18 blocks, keep 7: rounds of 7, 7, 4
     wl = synth.WalkWorkload(batch=3, n=24 * 48, m=36, steps=6)
