@@ -4,7 +4,8 @@ One tensor's two steps come from the seeded flux generator; the batch repeats
 them (640 copies of 1152 x 3072 = 2.26e9 elements, about 32 GB of state), so
 every tensor must produce the same packed bytes and state. Sampled tensors
 (first, middle, last) are checked against the oracle: bit for bit for the
-quantisers and the sparsifier, by the low-rank tolerance for low rank.
+quantisers, the sparsifier and block selection, by the low-rank tolerance
+for low rank.
 """
 import numpy as np
 import pytest
@@ -31,7 +32,8 @@ def frames():
 
 @pytest.mark.parametrize("scheme,kw", [("q2", dict(group=128)), ("q1", dict(group=64)),
                                        ("nm", dict(nm_keep=2, nm_block=16)),
-                                       ("lr", dict(rank=32, iters=2))])
+                                       ("lr", dict(rank=32, iters=2)),
+                                       ("bs", dict(grid_w=144, keep_blocks=5))])
 def test_batch_past_2_31_elements(frames, scheme, kw):
     assert B * N_ROWS * N_COLS > 2 ** 31
     a0, a1 = frames
@@ -54,8 +56,13 @@ def test_batch_past_2_31_elements(frames, scheme, kw):
         ref_ah = ahat[0].cpu().numpy()
         ref_e = e[0].cpu().numpy()
         af, pf = lib_view_f32(a1, "bf16"), lib_view_f32(a0, "bf16")
-        okw = {"group": kw["group"]} if "group" in kw else ({"rank": 32, "iters": 2, "q0": q0[0]} if scheme == "lr" else {})
-        o = oracle.compress_tensor(scheme, af, pf, **okw)
+        if scheme == "bs":  # 144-token grid rows: 8 x 18 blocks of 8 x 8 tokens per tensor
+            o = oracle.bs_compress_tensor(af, pf, grid_w=144, keep=5,
+                                          visited=np.zeros(N_ROWS // 64, bool), in_dtype="bf16")
+        else:
+            okw = {"group": kw["group"]} if "group" in kw else \
+                ({"rank": 32, "iters": 2, "q0": q0[0]} if scheme == "lr" else {})
+            o = oracle.compress_tensor(scheme, af, pf, **okw)
         if scheme == "lr":
             assert abs(relF(af, ref_ah) - relF(af, o["ahat"])) <= 1e-3
         else:
