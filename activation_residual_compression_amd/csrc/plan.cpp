@@ -117,7 +117,7 @@ rc_status_t validate(const rc_shape_t& sh, rc_dtype_t dtype, rc_scheme_t scheme,
       if (p->rank != 8 && (p->rank % 16 || p->rank > 64)) return RC_ERR_UNSUPPORTED;
       if (p->rank > sh.rows || p->rank > sh.cols) return RC_ERR_INVALID_ARG;
       if (sh.cols % 64) return RC_ERR_INVALID_ARG;
-      if (sh.rows > 65535 * 64) return RC_ERR_UNSUPPORTED;  // reconstruct grid: 64-row chunks in y
+      if (sh.rows > 65535 * 32) return RC_ERR_UNSUPPORTED;  // reconstruct grid: 32-row chunks in y
       return RC_OK;
     case RC_BLOCKSEL: {
       if (p->grid_w < 8 || p->grid_w % 8 || sh.rows % p->grid_w || (sh.rows / p->grid_w) % 8)

@@ -124,7 +124,7 @@ typedef struct {
 /* Validate the request and build a plan. For RC_LOWRANK this allocates the
  * device workspace (rc_workspace_bytes) on the current device and uploads q0.
  * Cols must be a multiple of the group (Q1/Q2), of 16 (NM) or of 64 (LR);
- * LR rows at most 65535 * 64; rows*cols*batch must stay below 2^40. */
+ * LR rows at most 65535 * 32; rows*cols*batch must stay below 2^40. */
 rc_status_t rc_plan_create(rc_shape_t shape, rc_dtype_t dtype, rc_scheme_t scheme,
                            const rc_params_t* params, rc_plan_t* out);
 

@@ -104,7 +104,7 @@ def test_lowrank_rank8_rejected_above_rows(rc):
         rc.Plan((2, 6, 256), "bf16", "lr", rank=8, iters=2, q0=q0)   # rank > rows
     assert ei.value.status == rc.RC_ERR_INVALID_ARG
     with pytest.raises(rc.RcError) as ei:                            # reconstruct grid limit
-        rc.Plan((1, 65535 * 64 + 1, 64), "bf16", "lr", rank=8, iters=2, q0=q0[:1, :64])
+        rc.Plan((1, 65535 * 32 + 1, 64), "bf16", "lr", rank=8, iters=2, q0=q0[:1, :64])
     assert ei.value.status == rc.RC_ERR_UNSUPPORTED
 
 
