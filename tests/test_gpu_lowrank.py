@@ -104,6 +104,14 @@ def test_lr_fp32_input_rank48():
     _run_lr(wl, 48, 2, check=[0, 1])
 
 
+@pytest.mark.parametrize("rank,factors", [(8, "bf16"), (16, "int4"), (64, "bf16")])
+def test_lr_fp32_input_other_ranks(rank, factors):
+    # fp32 a_t with each factor precision (the fp32 reconstruct widens nothing)
+    wl = synth.WalkWorkload(batch=3, n=150, m=320, steps=3)
+    _run_lr(wl, rank, 2, check=[0, 2], factors=factors,
+            code_agree=0.95 if factors == "bf16" else 0.8)
+
+
 @pytest.mark.parametrize("n,m,rank", [(40, 64, 16), (16, 64, 16), (64, 64, 32), (9, 128, 8)])
 def test_lr_smallest_shapes(n, m, rank):
     # one partial 64-row tile, a single half-used 128-column block, rank up to
