@@ -138,6 +138,31 @@ def test_lr_zero_and_rank_deficient_residuals():
     assert np.count_nonzero(np.abs(U).max(axis=0)) == 2
 
 
+def test_lr_zero_start_columns_are_dead_and_change_nothing():
+    # Rank k from a start matrix padded with zero columns to width k' > k gives
+    # exactly the rank-k result: the zero columns stay zero through every
+    # product, every CholeskyQR pass declares them dead, and the live columns
+    # see the same arithmetic (the products only add exact zeros). A rank-8
+    # request may therefore run 16 wide.
+    n, m = 40, 48
+    A = RNG.standard_normal((n, 10)) * np.linspace(3, 0.2, 10)
+    r = (A @ RNG.standard_normal((10, m)) + 0.05 * RNG.standard_normal((n, m))).astype(np.float32)
+    q0 = RNG.standard_normal((m, 8)).astype(np.float32)
+    q0w = np.concatenate([q0, np.zeros((m, 8), np.float32)], axis=1)
+    U8, V8, nd8 = oracle.lr_factors(r, q0, 8, 2)
+    U16, V16, nd16 = oracle.lr_factors(r, q0w, 16, 2)
+    assert nd8 == 0 and nd16 == 8
+    assert np.array_equal(U16[:, :8], U8) and np.array_equal(V16[:, :8], V8)
+    assert not U16[:, 8:].any() and not V16[:, 8:].any()
+    qu8, qv8, su8, sv8, _ = oracle.lr_encode(r, q0, 8, 2)
+    qu16, qv16, su16, sv16, _ = oracle.lr_encode(r, q0w, 16, 2)
+    assert np.array_equal(qu16[:, :8], qu8) and np.array_equal(qv16[:, :8], qv8)
+    assert np.array_equal(su16[:8], su8) and not su16[8:].any() and not qu16[:, 8:].any()
+    c8 = oracle.lr_decode(qu8, qv8, su8, sv8)
+    c16 = oracle.lr_decode(qu16, qv16, su16, sv16)
+    assert np.array_equal(c16.view(np.uint32), c8.view(np.uint32))
+
+
 def test_lr_bf16_factors_rounding_and_bound():
     # factor-precision alternative: the same factors, each element sent as bf16
     import torch
