@@ -507,6 +507,19 @@ def main():
                 us = sum(trace["kernels"][k]["avg_us"] * cnt for k, cnt in ks)
                 res["mfma_util_contractions"] = res["mfma_flops"] / (us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
                 res["contraction_us_per_step"] = us
+            # HBM fraction of the streaming passes (whole-batch launches):
+            # algorithmic bytes per element x elements / average duration
+            B, n, m = res["shape"]
+            k = int(ks[0][0].split(",")[-1].strip(" >"))
+            passes = {"first_product": ("lr_rq_kernel<unsigned short, true, %d>" % k, 8),
+                      "reconstruct_sender": ("lr_recon_kernel<unsigned short, true, %d, %d, false," % (k, k), 14),
+                      "reconstruct_receiver": ("lr_recon_kernel<float, false, %d, %d, false," % (k, k), 8)}
+            frac = {}
+            for name, (prefix, bpe) in passes.items():
+                hits = [v for kn, v in trace["kernels"].items() if kn.startswith(prefix)]
+                if len(hits) == 1:
+                    frac[name] = bpe * B * n * m / (hits[0]["avg_us"] * 1e3) / HBM_PEAK_GBS
+            res["streaming_pass_hbm_frac"] = frac
     roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
             "kernel": kname or ((prefix + " ...>") if prefix else "sender kernel (rc_compress)"),
