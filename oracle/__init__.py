@@ -244,7 +244,8 @@ def lr_factors(r, q0, rank, iters):
 
 # ------------------------------------------------------------ block selection
 def bs_scores(a, ahat, grid_w):
-    """Cosine dissimilarity of every 8x8-token block (raster order), fp64."""
+    """Cosine dissimilarity between a and ahat of every 8x8-token block
+    (raster order), fp64."""
     a, ahat = _f32(a), _f32(ahat)
     n, m = a.shape
     K = (n // grid_w // 8) * (grid_w // 8)
@@ -281,7 +282,7 @@ def bs_block_tokens(i, grid_w):
 # Per tensor, sections in this order, each starting at a multiple of 256 bytes;
 # tensors follow each other, each tensor's block a multiple of 256 bytes.
 #   q1: sign bits [N/8]            | scales f32 [N/G]
-#   q2: 2-bit codes [N/4]          | (mn f32, d f32) pairs [N/G]
+#   q2: 2-bit codes [N/4]          | group minima mn f32 [N/G] | steps d f32 [N/G]
 #   nm: (v_i0, v_i1) bf16 pairs [N/16] | index bytes i0 | i1<<4 [N/16]
 #   lr: U nibbles [n*k/2] | V nibbles [m*k/2] | s_U f32 [k] | s_V f32 [k]
 #       nibble t of a row-major [rows x k] INT4 matrix = element t; even t in
@@ -306,7 +307,7 @@ def section_sizes(scheme, n, m, group=None, rank=None, factors="int4", keep=None
     if scheme == "q1":
         return [N // 8, 4 * (N // group)]
     if scheme == "q2":
-        return [N // 4, 8 * (N // group)]
+        return [N // 4, 4 * (N // group), 4 * (N // group)]
     if scheme == "nm":
         return [4 * (N // 16), N // 16]
     if scheme == "lr":
@@ -372,8 +373,7 @@ def compress_tensor(scheme, a, ahat, *, group=None, rank=None, iters=None, q0=No
     elif scheme == "q2":
         codes, mn, d = q2_encode(flat, group)
         c = q2_decode(codes, mn, d, flat.size, group)
-        meta = np.stack([mn, d], axis=1)
-        packed = _place([codes, meta], scheme, n, m, group, rank)
+        packed = _place([codes, mn, d], scheme, n, m, group, rank)
     elif scheme == "nm":
         vals, idx = nm_encode(flat)
         c = nm_decode(vals, idx, flat.size)
@@ -396,19 +396,41 @@ def compress_tensor(scheme, a, ahat, *, group=None, rank=None, iters=None, q0=No
                 r=r)
 
 
-def bs_compress_tensor(a, ahat, *, grid_w, keep, visited, in_dtype="bf16", selected=None):
+def bs_compress_tensor(a, ahat, *, grid_w, keep, visited, prev=None, score="prev",
+                       in_dtype="bf16", selected=None):
     """One sender step of Otil-style block selection on one tensor.
 
+    Scores (Otil page, Key design 2): the cosine dissimilarity of each block
+    between this step's activation `a` and the previous step's activation
+    `prev` (the same block one denoising step apart). After the warm-up the
+    sender's reconstruction equals the previous activation exactly, so
+    prev=None means prev = ahat. score="last_sent" instead compares `a` with
+    the receiver's copy `ahat` (the block as last sent): an alternative, not
+    the page's rule.
     The selected blocks are sent as they are (values of a_t in the input dtype)
     and replace the receiver's copy, so after the step ahat = a_t there and
     e = 0; elsewhere ahat is unchanged and e = fl(a_t - ahat) (the whole
-    residual stays on the sender). Returns dict(packed, e, ahat, visited,
-    selected, scores)."""
+    residual stays on the sender). `selected` (ascending block indices) replaces
+    the top-k choice, e.g. to follow another implementation's choice among
+    near-equal scores. Returns dict(packed, e, ahat, visited, selected,
+    scores)."""
     a = _f32(a)
     ahat = _f32(ahat)
     n, m = a.shape
-    d = bs_scores(a, ahat, grid_w)
+    if score == "prev":
+        ref = ahat if prev is None else _f32(prev)
+    elif score == "last_sent":
+        ref = ahat
+    else:
+        raise ValueError(score)
+    d = bs_scores(a, ref, grid_w)
     sel, vis = bs_select(d, visited, keep)
+    if selected is not None:
+        vis = np.array(visited, dtype=bool, copy=True)
+        if vis.all():
+            vis[:] = False
+        sel = np.sort(np.asarray(selected, np.int64))
+        vis[sel] = True
     e = residual(a, ahat).reshape(n, m).copy()
     ahat_new = ahat.copy()
     in_bytes = 2 if in_dtype == "bf16" else 4
@@ -449,8 +471,8 @@ def decode_tensor(scheme, packed, n, m, *, group=None, rank=None, factors="int4"
     if scheme == "q1":
         return q1_decode(secs[0], secs[1].view(np.float32), N, group).reshape(n, m)
     if scheme == "q2":
-        meta = secs[1].view(np.float32).reshape(-1, 2)
-        return q2_decode(secs[0], meta[:, 0].copy(), meta[:, 1].copy(), N, group).reshape(n, m)
+        return q2_decode(secs[0], secs[1].view(np.float32), secs[2].view(np.float32), N,
+                         group).reshape(n, m)
     if scheme == "nm":
         return nm_decode(secs[0].view(np.uint16), secs[1], N).reshape(n, m)
     if scheme == "lr":
@@ -475,8 +497,7 @@ def unpack_fields(scheme, packed, n, m, *, group=None, rank=None, factors="int4"
     if scheme == "q1":
         return dict(bits=secs[0], scale=secs[1].view(np.float32))
     if scheme == "q2":
-        meta = secs[1].view(np.float32).reshape(-1, 2)
-        return dict(codes=secs[0], mn=meta[:, 0], d=meta[:, 1])
+        return dict(codes=secs[0], mn=secs[1].view(np.float32), d=secs[2].view(np.float32))
     if scheme == "nm":
         return dict(vals=secs[0].view(np.uint16), idx=secs[1])
     if scheme == "lr":

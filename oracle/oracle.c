@@ -104,31 +104,72 @@ void orc_accumulate_f64(int64_t count, const double* c, float* ahat) {
  * compression; Main experiment table, "1bit (16x)"). Per group of `group`
  * contiguous elements: one sign bit per element and one fp32 magnitude.
  * Readings: the magnitude is the mean of |r| over the group (the value that
- * minimises the squared error for fixed signs), computed as an fp64 sum
- * rounded once to fp32 after dividing by the group size; the bit is 1 when
- * r >= 0 (so -0 and +0 both give 1). Bits are LSB-first: element k of the
- * array is bit k%8 of byte k/8.
- * The pages fix no summation order, and an fp64 sum of fp32 magnitudes is
- * exact only while they span less than about 2^23, so the order is part of the
- * reading: each run of 4 contiguous elements is summed left to right, then the
- * run sums are added pairwise, neighbours first (a balanced binary tree). */
-static double q1_abs_sum(const float* r, int group) {
-  double part[64]; /* group <= 256: at most 64 runs of 4 */
-  const int runs = group / 4;
-  for (int j = 0; j < runs; ++j) {
-    double s = fabs((double)r[4 * j]);
-    for (int i = 1; i < 4; ++i) s += fabs((double)r[4 * j + i]);
-    part[j] = s;
+ * minimises the squared error for fixed signs), rounded once to fp32 (nearest,
+ * ties to even): the exact mean, not the result of any particular order of
+ * floating-point additions. The bit is 1 when r >= 0 (so -0 and +0 both give
+ * 1). Bits are LSB-first: element k of the array is bit k%8 of byte k/8.
+ *
+ * Exact mean: every finite fp32 value is an integer multiple of 2^-149 below
+ * 2^128, so the sum of at most 256 magnitudes is an integer S below 2^285 in
+ * units of 2^-149. It is accumulated exactly in ten 32-bit limbs (a plain
+ * multi-word integer), and the mean S * 2^-149 / group is rounded to fp32 bit
+ * by bit from S. */
+#define Q1_LIMBS 10
+
+/* S += m * 2^pos (m < 2^24): schoolbook addition with carry. */
+static void limbs_add(uint32_t* S, uint64_t m, int pos) {
+  uint64_t carry = m << (pos % 32); /* at most 55 bits */
+  for (int w = pos / 32; w < Q1_LIMBS && carry; ++w) {
+    const uint64_t t = (uint64_t)S[w] + (carry & 0xFFFFFFFFu);
+    S[w] = (uint32_t)t;
+    carry = (carry >> 32) + (t >> 32);
   }
-  for (int len = runs; len > 1; len /= 2)
-    for (int j = 0; j < len / 2; ++j) part[j] = part[2 * j] + part[2 * j + 1];
-  return part[0];
+}
+
+static int limbs_bit(const uint32_t* S, int i) { return (int)((S[i / 32] >> (i % 32)) & 1u); }
+
+/* fp32 nearest to S * 2^(-149 - g), ties to even, for an integer S >= 0. */
+static float limbs_round(const uint32_t* S, int g) {
+  int top = -1; /* index of the highest set bit */
+  for (int i = 32 * Q1_LIMBS - 1; i >= 0; --i)
+    if (limbs_bit(S, i)) { top = i; break; }
+  if (top < 0) return 0.0f;
+  /* Bits below `drop` do not fit the result: 24 significant bits for a normal
+   * result, or the subnormal grid 2^-149 = 2^g units of S. */
+  int drop = top - 23;
+  if (drop < g) drop = g;
+  uint64_t q = 0; /* S >> drop (at most 24 bits) */
+  for (int i = top; i >= drop; --i) q = (q << 1) | (uint64_t)limbs_bit(S, i);
+  if (drop > 0) {
+    const int half = limbs_bit(S, drop - 1);
+    int below = 0;
+    for (int i = 0; i < drop - 1; ++i) below |= limbs_bit(S, i);
+    if (half && (below || (q & 1u))) q += 1; /* round to nearest, ties to even */
+  }
+  /* q * 2^(drop - 149 - g) is an fp32 value (q <= 2^24), so both conversions
+   * below are exact. */
+  return (float)ldexp((double)q, drop - 149 - g);
+}
+
+static float q1_mean_abs(const float* r, int group) {
+  uint32_t S[Q1_LIMBS] = {0};
+  int g = 0;
+  while ((1 << g) < group) ++g; /* group is a power of two */
+  for (int i = 0; i < group; ++i) {
+    uint32_t u;
+    memcpy(&u, &r[i], 4);
+    const uint32_t ex = (u >> 23) & 0xFFu, frac = u & 0x7FFFFFu;
+    if (ex == 0xFFu) continue; /* NaN / Inf: unspecified */
+    /* |r| = mant * 2^(max(ex,1) - 150) = mant * 2^(max(ex,1) - 1) units of 2^-149 */
+    const uint64_t mant = ex ? (frac | 0x800000u) : frac;
+    limbs_add(S, mant, (ex ? (int)ex : 1) - 1);
+  }
+  return limbs_round(S, g);
 }
 
 void orc_q1_encode(int64_t count, int group, const float* r, uint8_t* bits, float* scale) {
   memset(bits, 0, (size_t)(count / 8));
-  for (int64_t g = 0; g < count / group; ++g)
-    scale[g] = (float)(q1_abs_sum(r + g * group, group) / (double)group);
+  for (int64_t g = 0; g < count / group; ++g) scale[g] = q1_mean_abs(r + g * group, group);
   for (int64_t k = 0; k < count; ++k)
     if (r[k] >= 0.0f) bits[k / 8] |= (uint8_t)(1u << (k % 8));
 }
@@ -398,12 +439,12 @@ int orc_lr_factors(int n, int m, int k, int iters, const float* r, const float* 
  * via Communication-Efficient Multi-GPU Parallelism", Key designs 1 and 2).
  * Tokens form a grid of grid_w columns (raster order); a block is 8 x 8 tokens
  * with all m channels, blocks numbered in raster order. For block i the
- * dissimilarity is d = 1 - <A_i, B_i>_F / (|A_i|_F |B_i|_F) between the current
- * activation A = a and the receiver's copy B = ahat (the block's value when it
- * was last sent). Readings: both blocks zero -> d = 0; exactly one zero -> d = 1.
- * Sums in fp64 over the block's tokens in raster order, channels innermost
- * (products of two fp32 values are exact in fp64). */
-void orc_bs_scores(int n, int m, int grid_w, const float* a, const float* ahat, double* d) {
+ * dissimilarity is d = 1 - <A_i, B_i>_F / (|A_i|_F |B_i|_F) between two
+ * activations A and B; the scheme passes the same block at two consecutive
+ * denoising steps. Readings: both blocks zero -> d = 0; exactly one zero ->
+ * d = 1. Sums in fp64 over the block's tokens in raster order, channels
+ * innermost (products of two fp32 values are exact in fp64). */
+void orc_bs_scores(int n, int m, int grid_w, const float* A, const float* B, double* d) {
   const int gh = n / grid_w, nbx = grid_w / 8, nby = gh / 8;
   for (int by = 0; by < nby; ++by)
     for (int bx = 0; bx < nbx; ++bx) {
@@ -412,7 +453,7 @@ void orc_bs_scores(int n, int m, int grid_w, const float* a, const float* ahat, 
         for (int dx = 0; dx < 8; ++dx) {
           const int64_t tok = (int64_t)(by * 8 + dy) * grid_w + bx * 8 + dx;
           for (int c = 0; c < m; ++c) {
-            const double x = a[tok * m + c], y = ahat[tok * m + c];
+            const double x = A[tok * m + c], y = B[tok * m + c];
             dot += x * y;
             na += x * x;
             nb += y * y;

@@ -125,3 +125,55 @@ def test_state_update_and_receiver(in_dtype):
     assert np.array_equal(rec.view(np.uint32), o["ahat"].view(np.uint32))
     in_bytes = 2 if in_dtype == "bf16" else 4
     assert o["packed"].size == oracle.tensor_bytes("bs", n, m, keep=keep, in_bytes=in_bytes)
+
+
+def test_page_rule_scores_against_the_previous_step_not_the_last_sent_copy():
+    # Two steps on three blocks, one block sent per step. Step 1: block 2
+    # changes most (its sign flips) and is sent; block 0 changes a lot too (it
+    # turns by 90 degrees) but is not sent, so the receiver keeps its step-0
+    # copy. Step 2: block 0 does not change any more, block 1 turns by 45
+    # degrees. The page compares each block with the same block one step
+    # earlier: block 0 scores 0, block 1 scores 1 - cos 45, so block 1 is sent.
+    # Comparing with the copy last sent instead would score block 0 at 1
+    # (orthogonal to the receiver's copy) and send it.
+    n, gw, m = _grid(1, 3, 8)
+    tok = [oracle.bs_block_tokens(i, gw) for i in range(3)]
+    u = np.zeros(m, np.float32)
+    u[0] = 1.0
+    w = np.zeros(m, np.float32)
+    w[1] = 1.0
+    a0 = np.zeros((n, m), np.float32)
+    for i in range(3):
+        a0[tok[i]] = u
+    a1 = a0.copy()
+    a1[tok[0]] = w                    # turned by 90 degrees: 1 - cos = 1
+    a1[tok[2]] = -u                   # flipped: 1 - cos = 2
+    a2 = a1.copy()
+    a2[tok[1]] = u + w                # 45 degrees from a1's block 1
+    vis = np.zeros(3, bool)
+    s1 = oracle.bs_compress_tensor(a1, a0, grid_w=gw, keep=1, visited=vis, prev=a0, in_dtype="f32")
+    assert s1["selected"].tolist() == [2]
+    s2 = oracle.bs_compress_tensor(a2, s1["ahat"], grid_w=gw, keep=1, visited=s1["visited"],
+                                   prev=a1, in_dtype="f32")
+    assert s2["scores"][0] == 0.0
+    assert s2["scores"][1] == pytest.approx(1 - np.sqrt(0.5), abs=1e-12)
+    assert s2["selected"].tolist() == [1]
+    alt = oracle.bs_compress_tensor(a2, s1["ahat"], grid_w=gw, keep=1, visited=s1["visited"],
+                                    score="last_sent", in_dtype="f32")
+    assert alt["scores"][0] == 1.0 and alt["selected"].tolist() == [0]
+    # after the warm-up the reconstruction is the previous activation, so the
+    # first step may pass prev=None
+    s1b = oracle.bs_compress_tensor(a1, a0, grid_w=gw, keep=1, visited=vis, in_dtype="f32")
+    assert np.array_equal(s1b["packed"], s1["packed"])
+
+
+def test_selected_override_follows_the_given_blocks():
+    n, gw, m = _grid(2, 2, 8)
+    a = RNG.standard_normal((n, m)).astype(np.float32)
+    ahat = RNG.standard_normal((n, m)).astype(np.float32)
+    o = oracle.bs_compress_tensor(a, ahat, grid_w=gw, keep=2, visited=np.zeros(4, bool),
+                                  in_dtype="f32", selected=np.array([3, 0]))
+    assert o["selected"].tolist() == [0, 3]
+    assert o["visited"].tolist() == [True, False, False, True]
+    head = o["packed"][:12].view(np.uint32)
+    assert head.tolist() == [2, 0, 3]

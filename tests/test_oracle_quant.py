@@ -73,24 +73,45 @@ def test_q1_scale_exactly_rounded_when_small_terms_decide(group):
         assert scale[0] == np.float32((1 + 2.0 ** -23) * 2.0 ** k)
 
 
-@pytest.mark.parametrize("group", [32, 64, 128])
-def test_q1_scale_wide_magnitude_span_within_summation_bound(group):
-    # Magnitudes spread over 2^-45 .. 2 make the fp64 partial sums round, so
-    # the summation order matters in the last bits. Whatever the order, an fp64
-    # sum of `group` terms with at most log2(group) + 1 roundings on any path
-    # lies within (log2(group) + 1) * 2^-53 * sum|r| of the exact sum; the
-    # scale is then one fp32 rounding of sum/group.
-    depth = int(np.log2(group)) + 1
-    for trial in range(200):
-        mag = RNG.uniform(1.0, 2.0, group) * 2.0 ** -RNG.integers(0, 46, group).astype(np.float64)
+@pytest.mark.parametrize("group", [32, 64, 128, 256])
+def test_q1_scale_exactly_rounded_on_wide_magnitude_spans(group):
+    # Magnitudes with random exponents over the whole fp32 range (subnormals
+    # included) make every floating-point summation order round somewhere;
+    # the scale must still be the exactly rounded mean (Fractions).
+    for trial in range(60):
+        lo = int(RNG.integers(-149, 100))
+        span = int(RNG.integers(20, 127 - lo + 1)) if lo < 100 else 20
+        ex = RNG.integers(lo, min(lo + span, 127) + 1, group)
+        mag = np.ldexp(RNG.uniform(1.0, 2.0, group), ex)
         r = (mag * RNG.choice([-1.0, 1.0], group)).astype(np.float32)
+        r[RNG.random(group) < 0.1] = 0.0
         _, scale = oracle.q1_encode(r, group)
-        total = sum(Fraction(float(abs(v))) for v in r)
-        exact = total / group
-        slack = Fraction(depth) * Fraction(2) ** -53 * total / group
-        lo = round_fraction_to_f32(exact - slack)
-        hi = round_fraction_to_f32(exact + slack)
-        assert lo <= scale[0] <= hi, trial
+        exact = sum(Fraction(float(abs(v))) for v in r) / group
+        assert f32_bits(scale[0]) == f32_bits(round_fraction_to_f32(exact)), trial
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_q1_scale_on_the_subnormal_grid(group):
+    # Means below the smallest normal fp32 round on the subnormal grid 2^-149:
+    # k terms of 2^-149 give k/group * 2^-149, which rounds to 0 below one half,
+    # ties to even (0) at exactly one half, and to 2^-149 above it.
+    tiny = np.float32(2.0 ** -149)
+    for k, want in ((1, 0.0), (group // 2, 0.0), (group // 2 + 1, float(tiny)),
+                    (3 * group // 2 // 2, float(tiny)), (group, float(tiny))):
+        r = np.zeros(group, np.float32)
+        r[:k] = tiny
+        _, scale = oracle.q1_encode(r, group)
+        assert scale[0] == np.float32(want), k
+    # one and a half grid steps (3/4 of the group at 2^-148): a tie between
+    # 2^-149 and 2^-148, which goes to the even one, 2^-148
+    r = np.zeros(group, np.float32)
+    r[:3 * group // 4] = np.float32(2.0 ** -148)
+    _, scale = oracle.q1_encode(r, group)
+    assert scale[0] == np.float32(2.0 ** -148)
+    # the largest finite magnitudes do not overflow the exact sum
+    r = np.full(group, np.float32(3.4028235e38), np.float32)
+    _, scale = oracle.q1_encode(r, group)
+    assert scale[0] == np.float32(3.4028235e38)
 
 
 def test_q1_scale_minimises_squared_error_for_fixed_signs():
