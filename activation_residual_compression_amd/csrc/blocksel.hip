@@ -3,21 +3,29 @@
 // Method: "Otil: Accelerating Diffusion Model Inference via
 // Communication-Efficient Multi-GPU Parallelism", Key designs 1-3: the tokens
 // of a share form a spatial grid cut into 8 x 8 square blocks; after each step
-// every block is scored by its cosine dissimilarity to its previous value, the
-// top-k blocks among those not yet visited in the current round are sent, and
-// the round restarts once every block has been visited. Here the previous
-// value of a block is the receiver's copy (ahat: the block as last sent), and
-// a sent block replaces that copy exactly, so in the residual framework of the
-// CompactFusion notes (Overall framework, Error feedback) the sender keeps
-// e = a_t - ahat on every block it did not send and e = 0 on the blocks it sent.
+// every block is scored by the cosine dissimilarity between its values at this
+// step and at the previous step, the top-k blocks among those not yet visited
+// in the current round are sent, and the round restarts once every block has
+// been visited. A sent block replaces the receiver's copy exactly, so in the
+// residual framework of the CompactFusion notes (Overall framework, Error
+// feedback) the sender keeps e = a_t - ahat on every block it did not send and
+// e = 0 on the blocks it sent.
+//
+// The previous step's activation is kept by the plan (a copy of the last a_t,
+// in the input dtype), written by the score pass as it reads the new one. On
+// the first step after a reset there is no copy yet; there the sender's
+// reconstruction is the previous activation (the warm-up sends a_0 in full),
+// so the score pass compares with ahat. (Option: score against ahat, the
+// receiver's copy, on every step; then no copy is kept.)
 //
 // Sender, per step (three launches):
-//   bs_score_kernel  one workgroup per block row (8 tokens): streams a_t and
-//                    ahat once (4 consecutive channels per lane), writes
-//                    e = a_t - ahat everywhere, and reduces <a, ahat>, |a|^2,
-//                    |ahat|^2 in fp64 (exact fp32 products) for the row.
+//   bs_score_kernel  one workgroup per block row (8 tokens): streams a_t, ahat
+//                    and the previous activation once (4 consecutive channels
+//                    per lane), writes e = a_t - ahat everywhere and the new
+//                    previous activation, and reduces <a, p>, |a|^2, |p|^2 in
+//                    fp64 (exact fp32 products) for the row.
 //   bs_select_kernel one workgroup per tensor: sums each block's 8 row
-//                    partials, d = 1 - <a,ahat> / (|a| |ahat|) (both blocks
+//                    partials, d = 1 - <a,p> / (|a| |p|) (both blocks
 //                    zero -> 0, one zero -> 1), restarts the round if every
 //                    block was visited, ranks every unvisited block by
 //                    (d descending, index ascending), keeps ranks < k, marks
@@ -54,12 +62,16 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
 }
 
 // One workgroup per (block row, block, tensor): e = a - ahat over the row's 8
-// tokens x m channels, and the row's fp64 partial sums <a, ahat>, |a|^2,
-// |ahat|^2 into part[tensor][block][row][3].
-template <typename IN>
+// tokens x m channels, and the row's fp64 partial sums <a, p>, |a|^2, |p|^2
+// into part[tensor][block][row][3], where p is the previous step's activation
+// (PREV: the plan's copy, or ahat while have_prev[b] is 0; it is replaced by a)
+// or the receiver's copy ahat (!PREV).
+template <typename IN, bool PREV>
 __global__ __launch_bounds__(kBsThreads) void bs_score_kernel(const IN* __restrict__ a,
                                                               const float* __restrict__ ahat,
                                                               float* __restrict__ e,
+                                                              IN* __restrict__ prev,
+                                                              const uint8_t* __restrict__ have_prev,
                                                               double* __restrict__ part,
                                                               BlockSel S) {
   __shared__ double red[3][4];
@@ -67,19 +79,27 @@ __global__ __launch_bounds__(kBsThreads) void bs_score_kernel(const IN* __restri
   const int64_t m = S.cols;
   const int64_t seg = 8 * m;  // elements of one block row (8 tokens x m channels)
   const int64_t off0 = (int64_t)b * S.rows * m + bs_row_token(i, dy, S.grid_w) * m;
+  const bool from_copy = PREV && have_prev[b] != 0;
   double dot = 0.0, na = 0.0, nb = 0.0;
   for (int64_t c = 4 * threadIdx.x; c < seg; c += 4 * kBsThreads) {
     const f32x4 x = load4<IN>(a + off0 + c);
     const f32x4 h = load4<float>(ahat + off0 + c);
+    const f32x4 p = from_copy ? load4<IN>(prev + off0 + c) : h;
     f32x4 r;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       r[t] = x[t] - h[t];
-      dot += (double)x[t] * (double)h[t];
+      dot += (double)x[t] * (double)p[t];
       na += (double)x[t] * (double)x[t];
-      nb += (double)h[t] * (double)h[t];
+      nb += (double)p[t] * (double)p[t];
     }
     store4(e + off0 + c, r);
+    if constexpr (PREV) {
+      if constexpr (sizeof(IN) == 2)
+        *reinterpret_cast<u32x2*>(prev + off0 + c) = *reinterpret_cast<const u32x2*>(a + off0 + c);
+      else
+        store4(reinterpret_cast<float*>(prev) + off0 + c, x);
+    }
   }
   dot = block_sum_f64(dot, red[0]);
   na = block_sum_f64(na, red[1]);
@@ -98,6 +118,7 @@ __global__ __launch_bounds__(kBsThreads) void bs_score_kernel(const IN* __restri
 // count, then block indices ascending.
 __global__ __launch_bounds__(kBsThreads) void bs_select_kernel(const double* __restrict__ part,
                                                                uint8_t* __restrict__ visited,
+                                                               uint8_t* __restrict__ have_prev,
                                                                uint8_t* __restrict__ packed,
                                                                BlockSel S) {
   __shared__ double sd[kBsMaxBlocks];
@@ -176,7 +197,10 @@ __global__ __launch_bounds__(kBsThreads) void bs_select_kernel(const double* __r
   }
   __syncthreads();
   const int count = wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
-  if (threadIdx.x == 0) head[0] = (uint32_t)count;
+  if (threadIdx.x == 0) {
+    head[0] = (uint32_t)count;
+    have_prev[b] = 1;  // the score pass has stored this step's activation
+  }
   for (int s = count + threadIdx.x; s < S.keep; s += kBsThreads) head[1 + s] = 0u;
 }
 
@@ -239,32 +263,38 @@ __global__ __launch_bounds__(kBsThreads) void bs_unpack_kernel(PeerSet peers, Bl
   }
 }
 
-// Round-robin state of every tensor back to "nothing visited" (a fill kernel,
-// so the call can sit in a captured graph).
-__global__ __launch_bounds__(kBsThreads) void bs_clear_kernel(uint8_t* __restrict__ visited, int64_t n) {
+// Round-robin state of every tensor back to "nothing visited", and no previous
+// activation (a fill kernel, so the call can sit in a captured graph).
+__global__ __launch_bounds__(kBsThreads) void bs_clear_kernel(uint8_t* __restrict__ visited, int64_t n,
+                                                              uint8_t* __restrict__ have_prev, int batch) {
   const int64_t i = (int64_t)blockIdx.x * kBsThreads + threadIdx.x;
   if (i < n) visited[i] = 0;
+  if (i < batch) have_prev[i] = 0;
+}
+
+template <typename IN>
+hipError_t bs_compress_t(const void* a, float* ahat, float* e, uint8_t* packed, int batch,
+                         const BlockSel& S, const BsState& st, hipStream_t s) {
+  const dim3 g_rows(S.nblocks * 8, batch), g_slots(S.keep * 8, batch);
+  const IN* x = static_cast<const IN*>(a);
+  IN* prev = static_cast<IN*>(st.prev);
+  if (prev)
+    hipLaunchKernelGGL((bs_score_kernel<IN, true>), g_rows, dim3(kBsThreads), 0, s, x, ahat, e, prev,
+                       st.have_prev, st.part, S);
+  else
+    hipLaunchKernelGGL((bs_score_kernel<IN, false>), g_rows, dim3(kBsThreads), 0, s, x, ahat, e, prev,
+                       st.have_prev, st.part, S);
+  hipLaunchKernelGGL(bs_select_kernel, dim3(batch), dim3(kBsThreads), 0, s, st.part, st.visited,
+                     st.have_prev, packed, S);
+  hipLaunchKernelGGL((bs_pack_kernel<IN>), g_slots, dim3(kBsThreads), 0, s, x, ahat, e, packed, S);
+  return hipGetLastError();
 }
 
 hipError_t launch_bs_compress(bool bf16_input, const void* a, float* ahat, float* e,
-                              uint8_t* packed, int batch, const BlockSel& S, double* part,
-                              uint8_t* visited, hipStream_t s) {
-  const dim3 g_rows(S.nblocks * 8, batch), g_slots(S.keep * 8, batch);
-  if (bf16_input) {
-    hipLaunchKernelGGL((bs_score_kernel<uint16_t>), g_rows, dim3(kBsThreads), 0, s,
-                       static_cast<const uint16_t*>(a), ahat, e, part, S);
-  } else {
-    hipLaunchKernelGGL((bs_score_kernel<float>), g_rows, dim3(kBsThreads), 0, s,
-                       static_cast<const float*>(a), ahat, e, part, S);
-  }
-  hipLaunchKernelGGL(bs_select_kernel, dim3(batch), dim3(kBsThreads), 0, s, part, visited, packed, S);
-  if (bf16_input)
-    hipLaunchKernelGGL((bs_pack_kernel<uint16_t>), g_slots, dim3(kBsThreads), 0, s,
-                       static_cast<const uint16_t*>(a), ahat, e, packed, S);
-  else
-    hipLaunchKernelGGL((bs_pack_kernel<float>), g_slots, dim3(kBsThreads), 0, s,
-                       static_cast<const float*>(a), ahat, e, packed, S);
-  return hipGetLastError();
+                              uint8_t* packed, int batch, const BlockSel& S, const BsState& st,
+                              hipStream_t s) {
+  return bf16_input ? bs_compress_t<uint16_t>(a, ahat, e, packed, batch, S, st, s)
+                    : bs_compress_t<float>(a, ahat, e, packed, batch, S, st, s);
 }
 
 hipError_t launch_bs_decompress(bool bf16_input, const PeerSet& peers, int batch, const BlockSel& S,
@@ -277,9 +307,9 @@ hipError_t launch_bs_decompress(bool bf16_input, const PeerSet& peers, int batch
   return hipGetLastError();
 }
 
-hipError_t launch_bs_reset(uint8_t* visited, int64_t n, hipStream_t s) {
+hipError_t launch_bs_reset(uint8_t* visited, int64_t n, uint8_t* have_prev, int batch, hipStream_t s) {
   hipLaunchKernelGGL(bs_clear_kernel, dim3((unsigned)((n + kBsThreads - 1) / kBsThreads)),
-                     dim3(kBsThreads), 0, s, visited, n);
+                     dim3(kBsThreads), 0, s, visited, n, have_prev, batch);
   return hipGetLastError();
 }
 

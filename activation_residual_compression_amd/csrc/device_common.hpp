@@ -67,6 +67,26 @@ __device__ __forceinline__ float group_max(float v) {
   if constexpr (L >= 32) v = fmaxf(v, __shfl_xor(v, 16));
   return v;
 }
+template <int L>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+  static_assert(L >= 1 && L <= 32 && (L & (L - 1)) == 0, "group of 1..32 lanes");
+  if constexpr (L >= 2) v = max(v, dpp_u32<kQuadXor1>(v));
+  if constexpr (L >= 4) v = max(v, dpp_u32<kQuadXor2>(v));
+  if constexpr (L >= 8) v = max(v, dpp_u32<kHalfMirror>(v));
+  if constexpr (L >= 16) v = max(v, dpp_u32<kRowMirror>(v));
+  if constexpr (L >= 32) v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+  return v;
+}
+template <int L>
+__device__ __forceinline__ uint32_t group_min_u32(uint32_t v) {
+  static_assert(L >= 1 && L <= 32 && (L & (L - 1)) == 0, "group of 1..32 lanes");
+  if constexpr (L >= 2) v = min(v, dpp_u32<kQuadXor1>(v));
+  if constexpr (L >= 4) v = min(v, dpp_u32<kQuadXor2>(v));
+  if constexpr (L >= 8) v = min(v, dpp_u32<kHalfMirror>(v));
+  if constexpr (L >= 16) v = min(v, dpp_u32<kRowMirror>(v));
+  if constexpr (L >= 32) v = min(v, (uint32_t)__shfl_xor((int)v, 16));
+  return v;
+}
 // Bitwise OR over aligned groups of L lanes (L = 1, 2, 4, 8).
 template <int L>
 __device__ __forceinline__ uint32_t group_or(uint32_t v) {

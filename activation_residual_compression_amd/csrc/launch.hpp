@@ -4,6 +4,8 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include "../../include/librescomp.h"
+
 namespace rc {
 
 // Per-tensor packed layout: up to 4 sections, each at a multiple of 256 bytes
@@ -57,7 +59,21 @@ struct LowRankWork {
   float* gsum = nullptr;     // summed Gram matrices [batch][rank][rank]
   float* linv = nullptr;     // inverse Cholesky factor, dead rows zeroed [batch][rank][rank]
   uint32_t* amax = nullptr;  // column absmax bits of U and V [batch][2][rank]
+  uint32_t* dead = nullptr;  // optional: count of dead Cholesky pivots (sent columns)
 };
+
+// Start matrices: Q0t bf16 [batch][rank][cols] (rows kp .. rank-1 zero) from a
+// device fp32 q0 [batch][cols][kp], or, when q0 is null, drawn from `seed`
+// (SplitMix64 + Box-Muller, as the public header defines).
+hipError_t launch_lr_q0(const float* q0, uint64_t seed, uint16_t* Q0t, int batch, int cols, int kp,
+                        int rank, hipStream_t s);
+
+// Host side (plan.cpp): request validation, packed layout, and the low-rank
+// workspace pieces placed from `base` on (null: sizes only); returns the bytes.
+rc_status_t validate(const rc_shape_t& sh, rc_dtype_t dtype, rc_scheme_t scheme, const rc_params_t* p);
+rc_status_t make_layout(const rc_shape_t& sh, rc_dtype_t dtype, rc_scheme_t scheme, const rc_params_t& p,
+                        Layout* L);
+int64_t carve_lowrank(LowRankWork* w, const rc_shape_t& shape, const rc_params_t& p, void* base);
 
 hipError_t launch_lr_compress(bool bf16_input, const void* a, float* ahat, float* e,
                               uint8_t* packed, int batch, const Layout& L, const LowRankWork& w,
@@ -65,6 +81,12 @@ hipError_t launch_lr_compress(bool bf16_input, const void* a, float* ahat, float
 // Receiver: every peer in one launch (the decode reads only the packed bytes).
 hipError_t launch_lr_decompress(const PeerSet& peers, int batch, const Layout& L,
                                 const LowRankWork& w, hipStream_t s);
+
+// Debug checks: count[0] += number of non-finite values in a [n] (bf16 or
+// fp32) and ahat [n] fp32; fill a u32 (kernels, so the calls can be captured).
+hipError_t launch_count_nonfinite(const void* a, bool bf16, const float* ahat, int64_t n,
+                                  uint32_t* count, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, hipStream_t s);
 
 // Otil-style block selection: tokens on a grid of grid_w columns, 8 x 8-token
 // blocks (nblocks per tensor, raster order), keep blocks sent per step.
@@ -74,13 +96,22 @@ struct BlockSel {
   int grid_w = 0, nblocks = 0, keep = 0;
   Layout L;
 };
-// part: fp64 [batch][nblocks][8][3] scratch (row partial sums); visited: u8
-// [batch][nblocks] round state.
+// Per-tensor state of a launch (pointers already offset to its first tensor):
+// part: fp64 [batch][nblocks][8][3] row partial sums (scratch); visited: u8
+// [batch][nblocks] round state; prev: the previous step's activation
+// [batch][rows][cols] in the input dtype, or null to score against ahat;
+// have_prev: u8 [batch], 0 until the tensor's prev holds an activation.
+struct BsState {
+  double* part = nullptr;
+  uint8_t* visited = nullptr;
+  void* prev = nullptr;
+  uint8_t* have_prev = nullptr;
+};
 hipError_t launch_bs_compress(bool bf16_input, const void* a, float* ahat, float* e,
-                              uint8_t* packed, int batch, const BlockSel& S, double* part,
-                              uint8_t* visited, hipStream_t s);
+                              uint8_t* packed, int batch, const BlockSel& S, const BsState& st,
+                              hipStream_t s);
 hipError_t launch_bs_decompress(bool bf16_input, const PeerSet& peers, int batch, const BlockSel& S,
                                 hipStream_t s);
-hipError_t launch_bs_reset(uint8_t* visited, int64_t n, hipStream_t s);
+hipError_t launch_bs_reset(uint8_t* visited, int64_t n, uint8_t* have_prev, int batch, hipStream_t s);
 
 }  // namespace rc

@@ -347,7 +347,8 @@ __device__ __forceinline__ float lane_f32(float v, int lane) {
 
 template <int K, int KP>
 __global__ __launch_bounds__(64) void lr_chol_kernel(const float* __restrict__ gsum,
-                                                     float* __restrict__ linv) {
+                                                     float* __restrict__ linv,
+                                                     uint32_t* __restrict__ dead) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const float* gs = gsum + (size_t)b * K * K;
@@ -379,6 +380,7 @@ __global__ __launch_bounds__(64) void lr_chol_kernel(const float* __restrict__ g
     L[j] = lane == j ? ljj : (lane > j && !dj ? s * inv : 0.f);
     y[j] = dj ? 0.f : t * inv;
     if (lane < K) out[(size_t)j * K] = y[j];  // stored here, so the chain is not deferred to the end
+    if (dead && dj && j < KP && lane == 0) atomicAdd(dead, 1u);  // debug report of sent columns
   }
 }
 
@@ -993,6 +995,53 @@ void launch_recon(const RcGrid& g, hipStream_t s, const IN* a, float* e, const P
                        peers, batch, L, g.chunk_rows);
 }
 
+// ---------------------------------------------------------------- start matrices
+// Q0t[b][j][c] = bf16(q0[b][c][j]) for j < kp, 0 for kp <= j < rank. One lane
+// per (tensor, column); from the caller's fp32 q0, or drawn from the seed as
+// the public header defines (SplitMix64 outputs, Box-Muller normals in fp64,
+// rounded to fp32 and then to bf16).
+__device__ __forceinline__ uint64_t sm64(uint64_t key, uint64_t i) {
+  uint64_t z = key + (i + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+__device__ __forceinline__ double sm64_unit(uint64_t key, uint64_t i) {
+  return ((double)(sm64(key, i) >> 11) + 0.5) * 0x1p-53;
+}
+
+__global__ __launch_bounds__(256) void lr_q0_kernel(const float* __restrict__ q0, uint64_t seed,
+                                                    uint16_t* __restrict__ Q0t, int batch, int cols,
+                                                    int kp, int rank) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)batch * cols) return;
+  const int b = (int)(idx / cols), c = (int)(idx % cols);
+  const uint64_t key = sm64(sm64(sm64(seed, 7), (uint64_t)b), 0);
+  uint16_t* dst = Q0t + (size_t)b * rank * cols + c;
+  for (int j = 0; j < rank; ++j) {
+    float v = 0.f;
+    if (j < kp) {
+      if (q0) {
+        v = q0[((size_t)b * cols + c) * kp + j];
+      } else {
+        const uint64_t i = (uint64_t)c * kp + j, p = i >> 1;
+        const double rad = sqrt(-2.0 * log(sm64_unit(key, 2 * p)));
+        const double ang = 6.283185307179586476925286766559 * sm64_unit(key, 2 * p + 1);
+        v = (float)((i & 1) ? rad * sin(ang) : rad * cos(ang));
+      }
+    }
+    dst[(size_t)j * cols] = (uint16_t)bf16_rne(v);
+  }
+}
+
+hipError_t launch_lr_q0(const float* q0, uint64_t seed, uint16_t* Q0t, int batch, int cols, int kp,
+                        int rank, hipStream_t s) {
+  const int64_t n = (int64_t)batch * cols;
+  hipLaunchKernelGGL(lr_q0_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, q0, seed, Q0t,
+                     batch, cols, kp, rank);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- launchers
 namespace {
 
@@ -1001,7 +1050,7 @@ void cqr_pass(const LowRankWork& w, int n, int B, bool final_pass, hipStream_t s
   const int nt = (int)w.ntiles, rp = (int)w.rows_pad;
   hipLaunchKernelGGL((lr_gram_reduce_kernel<K>), dim3((K * K + 255) / 256, B), dim3(256), 0, s,
                      w.gpart, w.gsum, nt);
-  hipLaunchKernelGGL((lr_chol_kernel<K, KP>), dim3(B), dim3(64), 0, s, w.gsum, w.linv);
+  hipLaunchKernelGGL((lr_chol_kernel<K, KP>), dim3(B), dim3(64), 0, s, w.gsum, w.linv, w.dead);
   if (final_pass)
     hipLaunchKernelGGL((lr_solve_kernel<K, false, true>), dim3(nt, B), dim3(256), 0, s, w.P, w.linv,
                        w.gpart, w.Pbt, w.amax, n, nt, rp);

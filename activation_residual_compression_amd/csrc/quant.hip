@@ -15,12 +15,24 @@
 // accumulates in one pass with the same lane layout.
 //
 // Arithmetic (fp32, one rounding per operation, no contraction):
-//   Q1: s = fp32(sum_fp64 |r| / G), bit = (r >= 0), c = bit ? s : -s
+//   Q1: s = the mean of |r| over the group rounded once to fp32 (nearest,
+//       ties to even), bit = (r >= 0), c = bit ? s : -s
 //   Q2: mn, mx = group min/max; d = (mx - mn) / 3 (zeros of mn and d stored
 //       as +0); if d >= FLT_MIN:
 //       inv = 1/d, q = min(3, rint_even((r - mn) * inv)) else q = 0;
 //       c = fma(q, d, mn)
 //   e = r - c; ahat = ahat + c   (the receiver applies the same c)
+//
+// The exact 1-bit mean. Each nonzero |r| is m * 2^(x - 150) with m < 2^24 and
+// x = max(exponent field, 1), an integer multiple of 2^(x_min - 150) for the
+// group's smallest x. When the group's exponents span at most 29 - log2(G)
+// binades, the sum is below 2^53 such units, so the fp64 sum is exact in any
+// order, and s = fp32(sum / G) rounds once (the common case: one fp64 sum over
+// the group's lanes). Otherwise (a term smaller than about 2^-22 of the
+// largest) the group takes an exact integer path: the magnitudes are added as
+// integers in units of 2^-149 into a 288-bit accumulator in LDS (64-bit words
+// of 32 live bits, so concurrent lane additions need no carry) and rounded to
+// fp32 from its bits.
 #include <float.h>
 
 #include "device_common.hpp"
@@ -29,6 +41,51 @@
 namespace rc {
 
 constexpr int kBlock = 256;
+constexpr int kQ1Words = 9;  // 288-bit exact |r| sum, 32 bits per 64-bit word
+
+// Exact mean of the group's |r| (slow path, see the file header). `acc` and
+// `nrm` are this group's kQ1Words-word LDS areas; every lane of the group
+// calls this with its 4 residuals and returns the same scale. LDS operations
+// of one wave complete in issue order, so the group needs no barrier.
+template <int LANES, int LOG2G>
+__device__ __forceinline__ float q1_exact_mean(f32x4 r, unsigned long long* acc, uint32_t* nrm) {
+  const int lig = threadIdx.x % LANES;  // lane in group
+  for (int k = lig; k < kQ1Words; k += LANES) acc[k] = 0ull;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t u = __float_as_uint(r[i]) & 0x7FFFFFFFu;
+    const uint32_t x = u >> 23;
+    if (u == 0u || x == 0xFFu) continue;
+    const uint32_t pos = (x ? x : 1u) - 1u;                     // lsb of m, in units of 2^-149
+    const uint64_t v = (uint64_t)(x ? ((u & 0x7FFFFFu) | 0x800000u) : u) << (pos & 31u);
+    atomicAdd(&acc[pos >> 5], v & 0xFFFFFFFFull);
+    atomicAdd(&acc[(pos >> 5) + 1], v >> 32);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  uint64_t carry = 0;
+  int top = -1;
+  for (int k = 0; k < kQ1Words; ++k) {
+    const uint64_t t = acc[k] + carry;
+    nrm[k] = (uint32_t)t;
+    carry = t >> 32;
+    if ((uint32_t)t) top = 32 * k + 31 - __clz((uint32_t)t);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  if (top < 0) return 0.0f;
+  // keep 24 significant bits, or the subnormal grid 2^-149 (2^LOG2G units)
+  const int drop = max(top - 23, LOG2G);
+  const int w0 = drop >> 5;
+  const uint64_t win = ((uint64_t)(w0 + 1 < kQ1Words ? nrm[w0 + 1] : 0u) << 32) | nrm[w0];
+  uint32_t q = (uint32_t)(win >> (drop & 31));
+  const int gp = drop - 1;  // the first dropped bit (drop >= LOG2G >= 1)
+  const uint32_t gw = nrm[gp >> 5];
+  const bool half = (gw >> (gp & 31)) & 1u;
+  bool sticky = (gw & ((1u << (gp & 31)) - 1u)) != 0u;
+  for (int k = 0; k < (gp >> 5); ++k) sticky |= nrm[k] != 0u;
+  if (half && (sticky || (q & 1u))) ++q;  // nearest, ties to even
+  return (float)ldexp((double)q, drop - 149 - LOG2G);  // exact: q <= 2^24
+}
 
 // Zero the gaps between sections (and after the last) of one tensor's packed
 // block, so the stream is fully defined. Each gap is below 256 bytes.
@@ -46,6 +103,11 @@ __global__ __launch_bounds__(kBlock) void q_compress_kernel(const IN* __restrict
                                                             float* __restrict__ e,
                                                             uint8_t* __restrict__ packed, Layout L) {
   constexpr int LANES = G / 4;  // lanes per group
+  constexpr int LOG2G = G == 32 ? 5 : (G == 64 ? 6 : 7);
+  static_assert(G == 32 || G == 64 || G == 128, "group");
+  // exact |r| sums of the 1-bit slow path, one area per group of the block
+  __shared__ unsigned long long q1_acc[BITS == 1 ? kBlock / LANES : 1][kQ1Words];
+  __shared__ uint32_t q1_nrm[BITS == 1 ? kBlock / LANES : 1][kQ1Words];
   const int b = blockIdx.y;
   const int64_t n4 = L.n / 4;
   const int64_t base = (int64_t)b * L.n;
@@ -75,10 +137,21 @@ __global__ __launch_bounds__(kBlock) void q_compress_kernel(const IN* __restrict
 
     if constexpr (BITS == 1) {
       double s = 0.0;
+      uint32_t xmax = 0u, xmin = 0xFFu;  // exponents of the nonzero |r| (subnormals: 1)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s += (double)fabsf(r[i]);
+      for (int i = 0; i < 4; ++i) {
+        s += (double)fabsf(r[i]);
+        const uint32_t u = __float_as_uint(r[i]) & 0x7FFFFFFFu;
+        const uint32_t x = max(u >> 23, 1u);
+        xmax = u ? max(xmax, x) : xmax;
+        xmin = u ? min(xmin, x) : xmin;
+      }
       s = group_sum_f64<LANES>(s);
-      const float scale = (float)(s * (1.0 / G));
+      xmax = group_max_u32<LANES>(xmax);
+      xmin = group_min_u32<LANES>(xmin);
+      float scale = (float)(s * (1.0 / G));
+      if (xmax > xmin + (29u - LOG2G))  // the fp64 sum may have rounded: exact path
+        scale = q1_exact_mean<LANES, LOG2G>(r, q1_acc[threadIdx.x / LANES], q1_nrm[threadIdx.x / LANES]);
       uint32_t nib = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -111,9 +184,13 @@ __global__ __launch_bounds__(kBlock) void q_compress_kernel(const IN* __restrict
       }
       // word w holds the codes of elements 16w .. 16w+15 (4 lanes)
       const uint32_t word = group_or<4>(code << (8 * (threadIdx.x & 3)));
-      if (valid) {
-        if ((threadIdx.x & 3) == 0) reinterpret_cast<uint32_t*>(pk)[c >> 2] = word;
-        if ((c % LANES) == 0) reinterpret_cast<float2*>(meta)[c / LANES] = make_float2(mn, d);
+      if (valid && (threadIdx.x & 3) == 0) reinterpret_cast<uint32_t*>(pk)[c >> 2] = word;
+      // mn and d are the same in every lane of the group: its first lane
+      // writes the minimum and its second the step, in one store instruction
+      const int gl = (int)(c % LANES);
+      if (valid && gl < 2) {
+        float* dst = reinterpret_cast<float*>(gl == 0 ? meta : pk + L.sec_off[2]);
+        dst[c / LANES] = gl == 0 ? mn : d;
       }
     }
 
@@ -167,9 +244,10 @@ __global__ __launch_bounds__(kBlock) void q_decompress_kernel(PeerSet peers, Lay
 #pragma unroll
       for (int i = 0; i < 4; ++i) h[i] = h[i] + (((nib >> i) & 1u) ? scale : -scale);
     } else {
-      const float2 md = reinterpret_cast<const float2*>(meta)[c / LANES];
+      const float mn = reinterpret_cast<const float*>(meta)[c / LANES];
+      const float d = reinterpret_cast<const float*>(pk + L.sec_off[2])[c / LANES];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) h[i] = h[i] + fmaf((float)((codes[j] >> (2 * i)) & 3u), md.y, md.x);
+      for (int i = 0; i < 4; ++i) h[i] = h[i] + fmaf((float)((codes[j] >> (2 * i)) & 3u), d, mn);
     }
     store4(ahat + base + c * 4, h);
   }

@@ -3,8 +3,9 @@
 Argument marshalling only: every step of the compression path runs in the HIP
 kernels of ``librescomp.so``. Functions keep the C names; a non-RC_OK status
 raises :class:`RcError`. Tensor arguments may be torch tensors (their
-``data_ptr()`` is passed), raw integer device addresses, or numpy arrays for the
-host-side start matrix ``q0``. Streams may be a ``torch.cuda.Stream``, a raw
+``data_ptr()`` is passed) or raw integer device addresses; the low-rank start
+matrices ``q0`` may also be a host numpy array, which ``Plan`` copies to the
+device for the plan's set-up. Streams may be a ``torch.cuda.Stream``, a raw
 ``hipStream_t`` integer, or None for torch's current stream.
 
 The library must be built first (``__graft_entry__.build()`` or
@@ -20,11 +21,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "librescomp.so")
 
 RC_OK, RC_ERR_INVALID_ARG, RC_ERR_UNSUPPORTED, RC_ERR_ALIGNMENT, RC_ERR_HIP = 0, 1, 2, 3, 4
+RC_ERR_NUMERIC, RC_ERR_NONFINITE = 5, 6
 RC_BF16, RC_F32 = 0, 1
 RC_Q1, RC_Q2, RC_NM, RC_LOWRANK, RC_BLOCKSEL = 0, 1, 2, 3, 4
 RC_MAX_PEERS = 8
 RC_LR_BF16_FACTORS = 1  # rc_params_t.flags, RC_LOWRANK only
 RC_LR_ONE_STREAM = 2    # rc_params_t.flags, RC_LOWRANK only: no second stream in rc_compress
+RC_BS_SCORE_LAST_SENT = 4  # rc_params_t.flags, RC_BLOCKSEL only: score against ahat
+RC_CHECK_FINITE = 8        # rc_params_t.flags, any scheme: reject NaN / Inf inputs (syncs)
+RC_LR_CHECK_NUMERIC = 16   # rc_params_t.flags, RC_LOWRANK only: report dead pivots (syncs)
 
 SCHEMES = {"q1": RC_Q1, "q2": RC_Q2, "nm": RC_NM, "lr": RC_LOWRANK, "bs": RC_BLOCKSEL}
 DTYPES = {"bf16": RC_BF16, "f32": RC_F32}
@@ -37,7 +42,8 @@ class rc_shape_t(ctypes.Structure):
 class rc_params_t(ctypes.Structure):
     _fields_ = [("group", ctypes.c_int32), ("nm_keep", ctypes.c_int32),
                 ("nm_block", ctypes.c_int32), ("rank", ctypes.c_int32),
-                ("iters", ctypes.c_int32), ("q0", ctypes.c_void_p), ("flags", ctypes.c_uint32),
+                ("iters", ctypes.c_int32), ("seed", ctypes.c_uint64), ("q0", ctypes.c_void_p),
+                ("flags", ctypes.c_uint32),
                 ("grid_w", ctypes.c_int32), ("keep_blocks", ctypes.c_int32)]
 
 
@@ -81,6 +87,8 @@ def _load():
     lib.rc_status_string.argtypes = [ctypes.c_int]
     lib.rcx_lowrank_workspace.restype = ctypes.c_int
     lib.rcx_lowrank_workspace.argtypes = [vp, ctypes.POINTER(vp), ctypes.c_int]
+    lib.rcx_device_to_host.restype = ctypes.c_int
+    lib.rcx_device_to_host.argtypes = [vp, vp, sz]
     lib.rcx_hbm_probe.restype = ctypes.c_int
     lib.rcx_hbm_probe.argtypes = [ctypes.c_int, vp, vp, vp, ctypes.c_int64, vp]
     return lib
@@ -204,17 +212,28 @@ def rc_workspace_bytes(plan) -> int:
     return int(_lib.rc_workspace_bytes(plan))
 
 
-def make_params(scheme, *, group=0, nm_keep=0, nm_block=0, rank=0, iters=0, q0=None, flags=0,
-                grid_w=0, keep_blocks=0):
-    """rc_params_t for a scheme; q0 (host fp32 [batch][cols][rank]) is referenced, not copied,
-    so keep it alive until rc_plan_create returns."""
-    p = rc_params_t(int(group), int(nm_keep), int(nm_block), int(rank), int(iters), _ptr(q0),
-                    int(flags), int(grid_w), int(keep_blocks))
+def make_params(scheme, *, group=0, nm_keep=0, nm_block=0, rank=0, iters=0, seed=0, q0=None,
+                flags=0, grid_w=0, keep_blocks=0):
+    """rc_params_t for a scheme; q0 (device fp32 [batch][cols][rank], or None to
+    draw the start matrices from `seed`) is referenced, not copied, so keep it
+    alive until rc_plan_create returns."""
+    p = rc_params_t(int(group), int(nm_keep), int(nm_block), int(rank), int(iters), int(seed),
+                    _ptr(q0), int(flags), int(grid_w), int(keep_blocks))
     p._q0_ref = q0
     return p
 
 
 RCX_PROBE_COPY, RCX_PROBE_READ, RCX_PROBE_WRITE, RCX_PROBE_SENDER_MIX, RCX_PROBE_RECEIVER_RMW = range(5)
+
+
+def rcx_device_to_host(src, nbytes):
+    """bytes at device address src, copied synchronously (librescomp_diag.h)."""
+    import numpy as np
+    out = np.empty(int(nbytes), np.uint8)
+    err = _lib.rcx_device_to_host(out.ctypes.data, _ptr(src), int(nbytes))
+    if err != 0:
+        raise RuntimeError("rcx_device_to_host: hipError %d" % err)
+    return out
 
 
 def rcx_hbm_probe(kind, a, b, c, n, stream=None):
@@ -234,15 +253,23 @@ class Plan:
         self.scheme = scheme
         q0 = params.get("q0")
         if q0 is not None:
-            import numpy as np
-            q0 = np.ascontiguousarray(q0, dtype=np.float32)
-            params["q0"] = q0
             want = self.shape[0] * self.shape[2] * int(params.get("rank", 0))
-            if SCHEMES.get(scheme, scheme) == RC_LOWRANK and q0.size != want:
+            size = q0.numel() if hasattr(q0, "numel") else int(getattr(q0, "size", -1))
+            if SCHEMES.get(scheme, scheme) == RC_LOWRANK and size != want:
                 # the library reads batch * cols * rank floats through the pointer
-                raise ValueError("q0 holds %d floats; [batch][cols][rank] needs %d" % (q0.size, want))
+                raise ValueError("q0 holds %d floats; [batch][cols][rank] needs %d" % (size, want))
+            if hasattr(q0, "data_ptr"):
+                if not (q0.is_cuda and q0.is_contiguous()) or str(q0.dtype) != "torch.float32":
+                    raise ValueError("q0 must be a contiguous fp32 device tensor")
+            else:  # host array: a device copy for the plan's set-up
+                import numpy as np
+                import torch
+                q0 = torch.from_numpy(np.ascontiguousarray(q0, dtype=np.float32)).to("cuda")
+                torch.cuda.synchronize()
+            params["q0"] = q0
         self._params = make_params(scheme, **params)
         self.handle = rc_plan_create(self.shape, dtype, scheme, self._params)
+        self._params._q0_ref = None  # the plan has its own copy of the start matrices
         self.packed_bytes = rc_packed_bytes(self.handle)
         self.tensor_packed_bytes = rc_tensor_packed_bytes(self.handle)
         self.workspace_bytes = rc_workspace_bytes(self.handle)
@@ -253,10 +280,20 @@ class Plan:
     def _in_bytes(self):
         return self._elems() * (2 if DTYPES.get(self.dtype, self.dtype) == RC_BF16 else 4)
 
+    def _input(self, a_t):
+        """a_t checked as _dev_buffer does, and for the plan's dtype (an fp32 tensor
+        given to a bf16 plan would otherwise be read as pairs of bf16 values)."""
+        if hasattr(a_t, "dtype") and hasattr(a_t, "data_ptr"):
+            want = "torch.bfloat16" if DTYPES.get(self.dtype, self.dtype) == RC_BF16 else "torch.float32"
+            if str(a_t.dtype) != want:
+                raise ValueError("a_t is %s, the plan takes %s" % (a_t.dtype, want))
+        return _dev_buffer(a_t, self._in_bytes(), "a_t")
+
     def compress(self, a_t, ahat, e, packed_out, stream=None):
+        a = self._input(a_t)
         st = rc_state_t(_dev_buffer(ahat, 4 * self._elems(), "ahat"),
                         _dev_buffer(e, 4 * self._elems(), "e"))
-        rc_compress(self.handle, stream, _dev_buffer(a_t, self._in_bytes(), "a_t"), st,
+        rc_compress(self.handle, stream, a, st,
                     _dev_buffer(packed_out, self.packed_bytes, "packed_out"))
 
     def decompress(self, packed_in, recon_state, stream=None):
@@ -264,10 +301,10 @@ class Plan:
                       _dev_buffer(recon_state, 4 * self._elems(), "recon_state"))
 
     def compress_send(self, a_t, ahat, e, packed_out, packed_dst, chunk, copy_stream, stream=None):
+        a = self._input(a_t)
         st = rc_state_t(_dev_buffer(ahat, 4 * self._elems(), "ahat"),
                         _dev_buffer(e, 4 * self._elems(), "e"))
-        rc_compress_send(self.handle, stream, copy_stream,
-                         _dev_buffer(a_t, self._in_bytes(), "a_t"), st,
+        rc_compress_send(self.handle, stream, copy_stream, a, st,
                          _dev_buffer(packed_out, self.packed_bytes, "packed_out"),
                          _sized(packed_dst, self.packed_bytes, "packed_dst"), chunk)
 

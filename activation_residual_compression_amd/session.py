@@ -79,7 +79,24 @@ class Session:
         self.sent_bytes = 0
 
     def step(self, a_t, stream=None):
-        """Advance one step; returns dict(t, kind, bytes)."""
+        """Advance one step; returns dict(t, kind, bytes).
+
+        Everything the step does -- the library calls and the copies and clears
+        of the state buffers around them -- is enqueued on `stream` (a
+        torch.cuda.Stream or a raw hipStream_t; None: torch's current stream),
+        in that order, so no update can overtake a kernel that reads the same
+        buffer. a_t must be ready on that stream."""
+        import torch
+        if stream is None:
+            s = torch.cuda.current_stream()
+        elif isinstance(stream, int):
+            s = torch.cuda.ExternalStream(stream)
+        else:
+            s = stream
+        with torch.cuda.stream(s):
+            return self._step(a_t, s)
+
+    def _step(self, a_t, stream):
         self.t += 1
         kind = self.schedule.at(self.t)
         if kind == "full":

@@ -180,10 +180,18 @@ class Workload:
 
     def q0(self, rank: int) -> np.ndarray:
         """Seeded N(0,1) start matrices, float32 [nb, m, rank]."""
-        out = np.empty((self.nb, self.m, rank), np.float32)
-        for i, b in enumerate(self.tensors):
-            _load().sg_q0(self.seed, b, self.m, rank, _p(out[i]))
-        return out
+        return start_matrices(self.seed, self.tensors, self.m, rank)
+
+
+def start_matrices(seed: int, tensors, m: int, rank: int) -> np.ndarray:
+    """N(0,1) start matrices of the subspace iteration for the given seed,
+    float32 [len(tensors), m, rank]: element (b, c, j) is the (c*rank + j)-th
+    normal of stream key(seed, 7, b, 0) (Workload.q0 is this with the workload's
+    seed)."""
+    out = np.empty((len(tensors), m, rank), np.float32)
+    for i, b in enumerate(tensors):
+        _load().sg_q0(int(seed), int(b), m, rank, _p(out[i]))
+    return out
 
 
 class WalkWorkload(Workload):
@@ -312,6 +320,6 @@ def sigma_ratio(a_prev: np.ndarray, a_next: np.ndarray) -> float:
     return float(d.std() / a_prev.astype(np.float64).std())
 
 
-__all__ = ["Workload", "WalkWorkload", "FluxWorkload", "VideoWorkload", "LatentWorkload", "CONFIGS", "make", "build",
+__all__ = ["start_matrices", "Workload", "WalkWorkload", "FluxWorkload", "VideoWorkload", "LatentWorkload", "CONFIGS", "make", "build",
            "normal", "uniform", "key", "to_bf16_bits", "bf16_bits_to_f32", "SEED_BASE",
            "sigma_ratio"]

@@ -107,11 +107,12 @@ def algorithmic_bytes(scheme, n_elem, in_bytes, group=None, rank=None, rows=None
     """Bytes each call must move at minimum (all tensors): compress and decompress."""
     N = n_elem
     if scheme == "bs":
-        # score pass reads a, ahat and writes e everywhere; the sent fraction of the
-        # blocks is copied into the packed stream and written to ahat (and e = 0);
-        # the receiver reads the sent blocks and writes them into its state
+        # score pass reads a, ahat and the previous activation, writes e and the
+        # new previous activation everywhere; the sent fraction of the blocks is
+        # copied into the packed stream and written to ahat (and e = 0); the
+        # receiver reads the sent blocks and writes them into its state
         frac = keep / (rows // 64)
-        return dict(compress=N * (in_bytes + 8) + N * frac * (2 * in_bytes + 8),
+        return dict(compress=N * (3 * in_bytes + 8) + N * frac * (2 * in_bytes + 8),
                     decompress=N * frac * (in_bytes + 4))
     if scheme == "q1":
         meta = N / 8 + 4 * N / group
@@ -217,7 +218,7 @@ def _ms(x):
 
 
 def measure(config, steps, warmup, max_frames, log, exchange_chunks=(), overlap=True,
-            lr_one_stream=False):
+            lr_one_stream=False, parity=True):
     import numpy as np
     import torch
 
@@ -341,6 +342,8 @@ def measure(config, steps, warmup, max_frames, log, exchange_chunks=(), overlap=
     if exchange_chunks:
         out["exchange"] = exchange_timing(plan, seq, ahat, e, packed, exchange_chunks)
         log("[bench] %s exchange: %s" % (config, json.dumps(out["exchange"])))
+    if parity:
+        out["parity"] = parity_sample(config, plan, seq[-1], ahat, e, recon, packed, log, q0=kw.get("q0"))
     # reference kernels on these very buffers, after the timed region (the state is
     # no longer needed): the HBM ceiling of the sender and receiver access patterns
     if wl.dtype == "bf16" and N % 8 == 0:
@@ -351,6 +354,33 @@ def measure(config, steps, warmup, max_frames, log, exchange_chunks=(), overlap=
     del frames, seq, ahat, recon, e, packed
     torch.cuda.empty_cache()
     return out
+
+
+def parity_summary(results):
+    """Totals of the per-workload sampled oracle checks."""
+    checks = {k: r["parity"] for k, r in results.items() if "parity" in r}
+    if not checks:
+        return None
+    exact = {k: p for k, p in checks.items() if "eps_gap_max" not in p}
+    lr = {k: p for k, p in checks.items() if "eps_gap_max" in p}
+    return dict(
+        workloads_checked=sorted(checks),
+        mismatched_packed_bytes=sum(p["mismatched_packed_bytes"] for p in exact.values()),
+        mismatched_state_elements=sum(p["mismatched_state_elements"] for p in exact.values()),
+        boundary_elements=sum(p["boundary_elements"] for p in exact.values()),
+        max_rel_err_state=max([p["max_rel_err_state"] for p in exact.values()] or [0.0]),
+        lowrank_eps_gap_max=max([p["eps_gap_max"] for p in lr.values()] or [0.0]),
+        receiver_equals_sender=all(p["receiver_equals_sender"] for p in checks.values()))
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(config, budget_s, log, ntensors=24):
@@ -366,12 +396,15 @@ def cpu_baseline(config, budget_s, log, ntensors=24):
     if spec["scheme"] == "lr":
         kw.update(rank=spec["rank"], iters=spec["iters"])
     oracle.build(force=False)
-    tensors = list(range(ntensors))
+    full = synth.make(config, tensors=[0])
+    tensors = list(range(min(ntensors, full.batch)))
     wl = synth.make(config, tensors=tensors)
     _, a0 = wl.next()
     f32 = lambda a: (a.astype(np.uint32) << 16).view(np.float32) if wl.dtype == "bf16" else a
     ahat = [f32(a0)[i].copy() for i in range(len(tensors))]
     recon = [x.copy() for x in ahat]
+    prev = [x.copy() for x in ahat]
+    visited = [np.zeros(wl.n // 64, bool) for _ in tensors]
     q0 = wl.q0(spec["rank"]) if spec["scheme"] == "lr" else None
     done, elapsed, t = 0, 0.0, 0
     log("[bench] cpu baseline: oracle %s" % config)
@@ -380,11 +413,18 @@ def cpu_baseline(config, budget_s, log, ntensors=24):
         t += 1
         af = f32(a)
         for i in range(len(tensors)):
-            extra = dict(q0=q0[i]) if q0 is not None else {}
             s = time.perf_counter()
-            o = oracle.compress_tensor(spec["scheme"], af[i], ahat[i], **kw, **extra)
-            recon[i] = oracle.decompress_tensor(spec["scheme"], o["packed"], recon[i],
-                                                group=kw.get("group"), rank=kw.get("rank"))
+            if spec["scheme"] == "bs":
+                o = oracle.bs_compress_tensor(af[i], ahat[i], grid_w=spec["grid_w"], keep=spec["keep_blocks"],
+                                              visited=visited[i], prev=prev[i], in_dtype=wl.dtype)
+                recon[i] = oracle.bs_decompress_tensor(o["packed"], recon[i], grid_w=spec["grid_w"],
+                                                       keep=spec["keep_blocks"], in_dtype=wl.dtype)
+                visited[i], prev[i] = o["visited"], af[i]
+            else:
+                extra = dict(q0=q0[i]) if q0 is not None else {}
+                o = oracle.compress_tensor(spec["scheme"], af[i], ahat[i], **kw, **extra)
+                recon[i] = oracle.decompress_tensor(spec["scheme"], o["packed"], recon[i],
+                                                    group=kw.get("group"), rank=kw.get("rank"))
             elapsed += time.perf_counter() - s
             ahat[i] = o["ahat"]
             done += 1
@@ -392,18 +432,95 @@ def cpu_baseline(config, budget_s, log, ntensors=24):
                 break
     in_bytes = 2 if wl.dtype == "bf16" else 4
     gbps = done * wl.n * wl.m * in_bytes / elapsed / 1e9
-    model = "unknown"
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    return dict(value=gbps, unit="GB/s", cores=1, kind="oracle", cpu_model=model,
+    return dict(value=gbps, unit="GB/s", cores=1, kind="oracle", cpu_model=_cpu_model(),
                 host_cpus=os.cpu_count(), tensors_per_s=done / elapsed,
                 sample="%s: %d tensor-steps of %dx%d (tensors 0-%d, steps 1-%d), compress+decompress, "
-                       "%.1f s single-threaded" % (config, done, wl.n, wl.m, ntensors - 1, t, elapsed))
+                       "%.1f s single-threaded" % (config, done, wl.n, wl.m, len(tensors) - 1, t, elapsed))
+
+
+def parity_sample(config, plan, frame, ahat, e, recon, packed, log, q0=None):
+    """One more step after the timed region, checked against the oracle on the
+    first and last tensor of the batch, teacher-forced (the oracle starts from
+    the GPU's state before the step). Bit-exact schemes: packed bytes, e and
+    ahat compared element by element; the count of elements within 1e-6
+    (relative) of a quantiser decision boundary is reported, as those are the
+    only ones where a code may differ. Low rank: the relative Frobenius error
+    of ahat, GPU against oracle. Block selection: the plan's round is restarted
+    first, so the oracle starts from an empty round too."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from activation_residual_compression_amd import synth
+
+    spec = synth.CONFIGS[config]
+    scheme = spec["scheme"]
+    B, n, m = plan.shape
+    bf16 = plan.dtype == "bf16"
+    f32 = lambda t: t.float().cpu().numpy()
+    checked = sorted({0, B - 1})
+    if scheme == "bs":
+        plan.reset_state()
+    recon.copy_(ahat)   # the receiver starts where the sender does (timing runs may have parted them)
+    before = ahat.cpu().numpy()
+    plan.compress(frame, ahat, e, packed)
+    plan.decompress(packed, recon)
+    torch.cuda.synchronize()
+    af, pk, ah, eh, rh = f32(frame), packed.cpu().numpy(), ahat.cpu().numpy(), e.cpu().numpy(), recon.cpu().numpy()
+    ts = plan.tensor_packed_bytes
+    out = dict(tensors_checked=checked, mismatched_packed_bytes=0, mismatched_state_elements=0,
+               max_rel_err_state=0.0, boundary_elements=0,
+               receiver_equals_sender=bool(np.array_equal(rh.view(np.uint32), ah.view(np.uint32))))
+    kw = {k: spec[k] for k in ("group",) if k in spec}
+    for b in checked:
+        r = (af[b] - before[b]).astype(np.float32)
+        if scheme == "lr":
+            o = oracle.compress_tensor("lr", af[b], before[b], rank=spec["rank"], iters=spec["iters"],
+                                       q0=q0[b])
+            eg = float(np.linalg.norm(af[b].astype(np.float64) - ah[b]) / np.linalg.norm(af[b]))
+            eo = float(np.linalg.norm(af[b].astype(np.float64) - o["ahat"]) / np.linalg.norm(af[b]))
+            out.setdefault("eps_gpu", []).append(eg)
+            out.setdefault("eps_oracle", []).append(eo)
+            out["eps_gap_max"] = max(out.get("eps_gap_max", 0.0), abs(eg - eo))
+            continue
+        if scheme == "bs":
+            o = oracle.bs_compress_tensor(af[b], before[b], grid_w=spec["grid_w"], keep=spec["keep_blocks"],
+                                          visited=np.zeros(n // 64, bool), in_dtype=plan.dtype)
+        else:
+            o = oracle.compress_tensor(scheme, af[b], before[b], **kw)
+        out["mismatched_packed_bytes"] += int(np.count_nonzero(pk[b * ts:(b + 1) * ts] != o["packed"]))
+        for g, w in ((ah[b], o["ahat"]), (eh[b], o["e"])):
+            out["mismatched_state_elements"] += int(np.count_nonzero(g.view(np.uint32) != w.view(np.uint32)))
+            den = max(float(np.abs(w).max()), 1e-30)
+            out["max_rel_err_state"] = max(out["max_rel_err_state"], float(np.abs(g.astype(np.float64) - w).max()) / den)
+        out["boundary_elements"] += boundary_count(scheme, r, o, n, m, kw)
+    log("[bench] %s parity sample: %s" % (config, json.dumps(out)))
+    return out
+
+
+def boundary_count(scheme, r, o, n, m, kw):
+    """Elements whose pre-quantisation value lies within 1e-6 (relative) of a
+    decision boundary of the oracle's encoding (where a code may flip)."""
+    import numpy as np
+
+    import oracle
+    if scheme == "q1":
+        s = oracle.unpack_fields("q1", o["packed"], n, m, group=kw["group"])["scale"]
+        s = np.repeat(s, kw["group"]).reshape(n, m)
+        return int(np.count_nonzero(np.abs(r) <= 1e-6 * s))
+    if scheme == "q2":
+        f = oracle.unpack_fields("q2", o["packed"], n, m, group=kw["group"])
+        mn = np.repeat(f["mn"], kw["group"]).reshape(n, m).astype(np.float64)
+        d = np.repeat(f["d"], kw["group"]).reshape(n, m).astype(np.float64)
+        cnt = 0
+        for k in range(3):
+            mid = mn + (k + 0.5) * d
+            cnt += int(np.count_nonzero((np.abs(r - mid) <= 1e-6 * np.maximum(np.abs(mid), 3 * d)) & (d > 0)))
+        return cnt
+    if scheme == "nm":
+        blk = np.sort(np.abs(r.reshape(-1, 16).astype(np.float64)), axis=1)[:, ::-1]
+        return int(np.count_nonzero(blk[:, 1] - blk[:, 2] <= 1e-6 * blk[:, 1]) * 2)
+    return 0
 
 
 def main():
@@ -412,14 +529,16 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="flux_q2")
-    ap.add_argument("--also", default="flux_nm,video_q1,flux_lr,video_lr,latent_bs",
+    ap.add_argument("--also", default="flux_nm,video_q1,flux_lr,video_lr,latent_bs,tiny_q1",
                     help="other workloads to measure ('' for none)")
     ap.add_argument("--also-frames", type=int, default=4,
                     help="distinct input frames for the other workloads (cycled)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--lr-cpu-budget", type=float, default=8.0,
-                    help="seconds of oracle time on the flux low-rank workload (reported "
-                         "under workloads.flux_lr.cpu_baseline; 0 to skip)")
+    ap.add_argument("--cpu-budget-each", type=float, default=4.0,
+                    help="seconds of oracle time on each of the other workloads (reported "
+                         "under workloads.<name>.cpu_baseline; 0 to skip)")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the sampled oracle check after each workload's timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-probe", action="store_true")
     ap.add_argument("--no-exchange", action="store_true",
@@ -465,7 +584,8 @@ def main():
     ceiling = None if args.no_hbm_probe else hbm_probe(_wl.batch * _wl.n * _wl.m, log)
     main_res = measure(args.workload, args.steps, args.warmup, 64, log,
                        exchange_chunks=() if args.no_exchange else (4, 8, 19),
-                       overlap=not args.no_exchange, lr_one_stream=args.lr_one_stream)
+                       overlap=not args.no_exchange, lr_one_stream=args.lr_one_stream,
+                       parity=not args.no_parity)
     log("[bench] %s: %.3f ms/step, %.1f GB/s input, compress %.3f ms (%.0f GB/s alg), "
         "graph replay %.3f ms/step, compress/decode overlapped %s ms/step" % (
             args.workload, main_res["ms_per_step"], main_res["input_GBps"], main_res["compress_ms"],
@@ -474,7 +594,8 @@ def main():
     for cfg in [c for c in args.also.split(",") if c and c != args.workload]:
         r = measure(cfg, args.steps, args.warmup, args.also_frames, log,
                     exchange_chunks=(8, 19) if (cfg == "flux_lr" and not args.no_exchange) else (),
-                    overlap=not args.no_exchange, lr_one_stream=args.lr_one_stream)
+                    overlap=not args.no_exchange, lr_one_stream=args.lr_one_stream,
+                    parity=not args.no_parity)
         log("[bench] %s: %.3f ms/step, %.1f GB/s input (graph replay %.3f, compress/decode "
             "overlapped %s ms/step)" % (cfg, r["ms_per_step"], r["input_GBps"],
                                        r["graph_ms_per_step"], _ms(r["overlapped_ms_per_step"])))
@@ -483,9 +604,11 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.workload, args.cpu_budget, log)
-        if "flux_lr" in others and args.lr_cpu_budget > 0:
-            others["flux_lr"]["cpu_baseline"] = cpu_baseline("flux_lr", args.lr_cpu_budget, log,
-                                                             ntensors=6)
+        main_res["cpu_baseline"] = cpu
+        if args.cpu_budget_each > 0:
+            for cfg, res in others.items():
+                res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget_each, log,
+                                                   ntensors=4 if res["scheme"] == "lr" else 8)
 
     ach = main_res["compress_GBps"]
     traffic = None
@@ -540,14 +663,20 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "%s: %d bf16 tensors [%d x %d] per step, scheme %s" % (
-            args.workload, *main_res["shape"], main_res["scheme"]),
+        "config": {"workload": "%s: %d %s tensors [%d x %d] per step, scheme %s" % (
+            args.workload, main_res["shape"][0], main_res["dtype"], *main_res["shape"][1:], main_res["scheme"]),
             "input_dtype": main_res["dtype"], "state_dtype": "f32",
-            "steps_per_sequence": 28, "parallelism": "single GPU"},
+            "steps_per_sequence": _synth.make(args.workload, tensors=[0]).steps,
+            "parallelism": "single GPU",
+            "headline": "the FLUX-like sequence-parallel share (2-bit), the first full-size "
+                        "setting of the metric; every other setting, the largest (video-like "
+                        "1-bit, 256 M elements per step) included, is measured in the same run "
+                        "under workloads"},
         "roofline": roof,
         "hbm_reference_kernels_GBps": ceiling,
         "hbm_frac_step": main_res["hbm_frac_step"],
         "cpu_baseline": cpu,
+        "parity": parity_summary({args.workload: main_res, **others}),
         "workloads": {args.workload: main_res, **others},
     }
     print(json.dumps(line))

@@ -30,10 +30,12 @@
  *     and block-selection schemes keep per-plan device workspace and state).
  *     Separate plans share nothing and may run concurrently on separate streams.
  *   - A rejected request (RC_ERR_INVALID_ARG, RC_ERR_UNSUPPORTED,
- *     RC_ERR_ALIGNMENT) launches nothing and touches no buffer. RC_ERR_HIP
- *     reports a failed HIP call or kernel launch; the outputs of that call are
- *     then unspecified.
- *   - Inputs holding NaN or Inf give unspecified (but memory-safe) results.
+ *     RC_ERR_ALIGNMENT, RC_ERR_NONFINITE) launches nothing and touches no
+ *     buffer. RC_ERR_HIP reports a failed HIP call or kernel launch; the
+ *     outputs of that call are then unspecified. RC_ERR_NUMERIC is a report
+ *     after a completed call (see RC_LR_CHECK_NUMERIC).
+ *   - Inputs holding NaN or Inf give unspecified (but memory-safe) results,
+ *     unless RC_CHECK_FINITE asks for them to be rejected.
  */
 #ifndef LIBRESCOMP_H
 #define LIBRESCOMP_H
@@ -55,6 +57,8 @@ typedef enum {
   RC_ERR_UNSUPPORTED = 2, /* valid request this library does not implement */
   RC_ERR_ALIGNMENT = 3,   /* a tensor pointer is not 16-byte aligned */
   RC_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  RC_ERR_NUMERIC = 5,     /* RC_LR_CHECK_NUMERIC: a Cholesky pivot broke down */
+  RC_ERR_NONFINITE = 6,   /* RC_CHECK_FINITE: NaN or Inf in the input */
 } rc_status_t;
 
 typedef enum { RC_BF16 = 0, RC_F32 = 1 } rc_dtype_t; /* dtype of a_t */
@@ -73,18 +77,38 @@ typedef struct {
   int32_t cols;  /* hidden size                                     */
 } rc_shape_t;
 
+/* Scheme parameters. The values the pages evaluate: 1-bit and 2-bit groups
+ * (Main experiment table: 1-bit 16x, 2-bit 8x; group 64 and 128 in this
+ * library's workloads), the 2:16 block sparsifier (Key designs / System
+ * co-design: N:M instead of TopK), and rank / iterations / INT4 factors of the
+ * subspace iteration (Key designs / Low-rank strategy for extreme compression;
+ * Main experiment table: low rank at about 100x). Unused fields must be 0. */
 typedef struct {
   int32_t group;    /* RC_Q1 / RC_Q2: group size along cols: 32, 64 or 128       */
   int32_t nm_keep;  /* RC_NM: kept per block, must be 2                           */
   int32_t nm_block; /* RC_NM: block size, must be 16                              */
   int32_t rank;     /* RC_LOWRANK: 8, 16, 32, 48 or 64, at most rows and cols     */
   int32_t iters;    /* RC_LOWRANK: subspace iterations, 1..16                     */
-  const float* q0;  /* RC_LOWRANK: HOST fp32 [batch][cols][rank] start matrices;  */
-                    /*   copied at plan creation and reused every step           */
-  uint32_t flags;   /* 0, or RC_LOWRANK: RC_LR_BF16_FACTORS | RC_LR_ONE_STREAM     */
+  uint64_t seed;    /* RC_LOWRANK with q0 == NULL: seed of the start matrices     */
+  const void* q0;   /* RC_LOWRANK, optional: DEVICE fp32 [batch][cols][rank]      */
+                    /*   start matrices (4-byte aligned), read by rc_plan_create  */
+                    /*   before it returns and reused every step. NULL: drawn     */
+                    /*   from `seed` (see RC_LOWRANK below).                      */
+  uint32_t flags;   /* 0 or an OR of the RC_* flags below allowed for the scheme  */
   int32_t grid_w;      /* RC_BLOCKSEL: tokens per row of the spatial token grid     */
   int32_t keep_blocks; /* RC_BLOCKSEL: blocks sent per tensor and step (k)          */
 } rc_params_t;
+
+/* Seeded start matrices (RC_LOWRANK, q0 == NULL). Element (b, c, j) of the
+ * [batch][cols][rank] start matrices is the (c * rank + j)-th value of the
+ * standard normal sequence of stream K_b, rounded to fp32, where
+ *   S(k, i) = i-th output of SplitMix64 seeded with k (Steele, Lea and Flood,
+ *             OOPSLA 2014): mix(k + (i + 1) * 0x9E3779B97F4A7C15),
+ *   K_b     = S(S(S(seed, 7), b), 0),
+ *   u(i)    = ((S(K_b, i) >> 11) + 0.5) * 2^-53, uniform in (0, 1),
+ *   normal element 2p / 2p + 1 = sqrt(-2 ln u(2p)) * cos / sin(2 pi u(2p + 1))
+ *             (Box-Muller, 1958).
+ * The start matrices are the subspace iteration's only random input. */
 
 /* rc_params_t.flags for RC_LOWRANK: send the factors as bf16 (round to nearest
  * even) instead of INT4 with per-column scales -- the factor-precision side of
@@ -101,6 +125,25 @@ typedef struct {
  * traces without overlapping kernels. */
 #define RC_LR_ONE_STREAM 2u
 
+/* rc_params_t.flags for RC_BLOCKSEL: score each block against the receiver's
+ * copy (ahat, the block as last sent) instead of the previous step's
+ * activation. An alternative to the page's rule; the plan then keeps no copy
+ * of the previous activation. */
+#define RC_BS_SCORE_LAST_SENT 4u
+
+/* rc_params_t.flags, any scheme (debugging): rc_compress and rc_compress_send
+ * first scan a_t and the sender's ahat and return RC_ERR_NONFINITE, launching
+ * nothing else, if either holds NaN or Inf. The call then waits for the scan
+ * (a host synchronisation on the stream; not for graph capture). */
+#define RC_CHECK_FINITE 8u
+
+/* rc_params_t.flags for RC_LOWRANK (debugging): rc_compress waits for its
+ * kernels and returns RC_ERR_NUMERIC if any Cholesky pivot of the CholeskyQR2
+ * passes fell under the dead-column threshold (a zero or rank-deficient
+ * residual, or a breakdown). The results are those of the default path, which
+ * zeroes such columns; the status only reports it. Not for graph capture. */
+#define RC_LR_CHECK_NUMERIC 16u
+
 typedef struct {
   float* ahat; /* sender's copy of the receiver reconstruction, fp32 [batch][rows][cols] */
   float* e;    /* error-feedback buffer, fp32 [batch][rows][cols] (written every step)  */
@@ -110,21 +153,30 @@ typedef struct {
  * Communication-Efficient Multi-GPU Parallelism", Key designs 1-3): the rows of
  * a tensor are tokens of a spatial grid with grid_w tokens per row (raster
  * order); the grid is cut into 8 x 8-token blocks (all channels), numbered in
- * raster order. Each step every block is scored by its cosine dissimilarity
- * 1 - <a, ahat> / (|a| |ahat|) to the receiver's copy (the block as last sent;
- * both zero -> 0, one zero -> 1), and the keep_blocks highest-scoring blocks
- * among those not yet sent in the current round (ties to the lower index) are
- * sent; the round restarts once every block has been sent, so every block is
- * sent once per round. Sent blocks carry the a_t values (input dtype) and
- * replace the receiver's copy: after the step ahat = a_t and e = 0 there, and
- * e = a_t - ahat on the other blocks. The round state lives in the plan
- * (rc_plan_reset_state clears it). Requirements: rows % (8 grid_w) == 0,
- * grid_w % 8 == 0, cols % 4 == 0, 1 <= keep_blocks <= blocks <= 4096. */
+ * raster order. Each step every block is scored by the cosine dissimilarity
+ * 1 - <a_t, a_{t-1}> / (|a_t| |a_{t-1}|) between its values at this step and
+ * at the previous step (Key design 2; both zero -> 0, one zero -> 1), and the
+ * keep_blocks highest-scoring blocks among those not yet sent in the current
+ * round (ties to the lower index) are sent; the round restarts once every block
+ * has been sent, so every block is sent once per round (Key design 3). Sent
+ * blocks carry the a_t values (input dtype) and replace the receiver's copy:
+ * after the step ahat = a_t and e = 0 there, and e = a_t - ahat on the other
+ * blocks. The plan keeps the round state and a copy of the previous a_t
+ * (rc_workspace_bytes counts it); on the first step after creation or
+ * rc_plan_reset_state it has none and compares with ahat, which the warm-up
+ * set to a_{t-1}. RC_BS_SCORE_LAST_SENT scores against ahat on every step.
+ * Requirements: rows % (8 grid_w) == 0, grid_w % 8 == 0, cols % 4 == 0,
+ * 1 <= keep_blocks <= blocks <= 4096. */
 
-/* Validate the request and build a plan. For RC_LOWRANK this allocates the
- * device workspace (rc_workspace_bytes) on the current device and uploads q0.
- * Cols must be a multiple of the group (Q1/Q2), of 16 (NM) or of 64 (LR);
- * LR rows at most 65535 * 32; rows*cols*batch must stay below 2^40. */
+/* Validate the request and build a plan. For RC_LOWRANK and RC_BLOCKSEL this
+ * allocates the device workspace (rc_workspace_bytes) on the current device;
+ * RC_LOWRANK also sets up the start matrices (from q0 or the seed) and waits
+ * for that. Cols must be a multiple of the group (Q1/Q2), of 16 (NM) or of 64
+ * (LR); LR rows at most 65535 * 32; rows*cols*batch must stay below 2^40.
+ * Errors: RC_ERR_INVALID_ARG (null params or out, bad shape, bad value, a flag
+ * the scheme does not take), RC_ERR_UNSUPPORTED (a valid value this library
+ * does not implement), RC_ERR_ALIGNMENT (q0 not 4-byte aligned), RC_ERR_HIP
+ * (allocation or launch failure; nothing is leaked). */
 rc_status_t rc_plan_create(rc_shape_t shape, rc_dtype_t dtype, rc_scheme_t scheme,
                            const rc_params_t* params, rc_plan_t* out);
 
@@ -176,8 +228,8 @@ rc_status_t rc_decompress_many(rc_plan_t plan, hipStream_t stream, const void* c
                                float* const* recon_states, int npeers);
 
 /* Clear the state a plan keeps across steps (RC_BLOCKSEL: the round of sent
- * blocks), for a new sequence; asynchronous on stream; no effect for the other
- * schemes. */
+ * blocks and the previous activation), for a new sequence; asynchronous on
+ * stream; no effect for the other schemes. */
 rc_status_t rc_plan_reset_state(rc_plan_t plan, hipStream_t stream);
 
 /* Free the plan and its workspace. Waits for nothing: the caller must make sure
@@ -188,7 +240,8 @@ rc_status_t rc_plan_destroy(rc_plan_t plan);
  * slice of it. Layout, per tensor, each section starting at a multiple of 256
  * bytes, tensors back to back (N = rows*cols, G = group):
  *   Q1: sign bits [N/8] (element k = bit k%8 of byte k/8) | scale f32 [N/G]
- *   Q2: codes [N/4] (element k = bits 2(k%4)..+1 of byte k/4) | {mn, step} f32 pairs [N/G]
+ *   Q2: codes [N/4] (element k = bits 2(k%4)..+1 of byte k/4) | group minimum mn f32 [N/G]
+ *       | group step d f32 [N/G]
  *   NM: {v_i0, v_i1} bf16 pairs [N/16] | index byte i0 | i1<<4 [N/16], i0 < i1
  *   LR: U nibbles [rows*rank/2] | V nibbles [cols*rank/2] | sU f32 [rank] | sV f32 [rank]
  *       (row-major INT4, element t in nibble t, even t low, two's complement);
@@ -200,7 +253,8 @@ rc_status_t rc_plan_destroy(rc_plan_t plan);
 size_t rc_packed_bytes(rc_plan_t plan);
 size_t rc_tensor_packed_bytes(rc_plan_t plan);
 
-/* Device workspace owned by the plan (0 for Q1, Q2, NM). */
+/* Device workspace owned by the plan (0 for Q1, Q2, NM; the debug flags add a
+ * 4-byte counter not counted here). */
 size_t rc_workspace_bytes(rc_plan_t plan);
 
 /* Static description of a status code. */

@@ -6,6 +6,7 @@
 #ifndef LIBRESCOMP_DIAG_H
 #define LIBRESCOMP_DIAG_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
@@ -40,6 +41,10 @@ int rcx_hbm_probe(int kind, const void* a, void* b, void* c, int64_t n, hipStrea
  * NULL plan, another scheme, or count < 8. The pieces are as wide as the
  * iteration: max(rank, 16) (rank 8 runs 16 wide with columns 8 .. 15 zero). */
 int rcx_lowrank_workspace(rc_plan_t plan, void** ptrs, int count);
+
+/* Synchronous copy of `bytes` bytes from device address src to host memory dst
+ * (for reading the workspace pieces above). Returns a hipError_t value. */
+int rcx_device_to_host(void* dst, const void* src, size_t bytes);
 
 #ifdef __cplusplus
 }

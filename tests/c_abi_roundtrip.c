@@ -148,15 +148,24 @@ int main(void) {
   p.nm_block = 16;
   failures += run_scheme("nm", RC_NM, shape, p);
 
+  /* start matrices given on the device, then drawn from a seed */
   const int rank = 16;
-  float* q0 = (float*)malloc(sizeof(float) * shape.batch * shape.cols * rank);
+  const size_t q0_bytes = sizeof(float) * shape.batch * shape.cols * rank;
+  float* q0 = (float*)malloc(q0_bytes);
   for (int i = 0; i < shape.batch * shape.cols * rank; ++i) q0[i] = uniform();
+  void* d_q0;
+  CHECK_HIP(hipMalloc(&d_q0, q0_bytes));
+  CHECK_HIP(hipMemcpy(d_q0, q0, q0_bytes, hipMemcpyHostToDevice));
   memset(&p, 0, sizeof p);
   p.rank = rank;
   p.iters = 2;
-  p.q0 = q0;
+  p.q0 = d_q0;
   failures += run_scheme("lowrank", RC_LOWRANK, shape, p);
+  CHECK_HIP(hipFree(d_q0));
   free(q0);
+  p.q0 = NULL;
+  p.seed = 12345;
+  failures += run_scheme("lowrank seeded", RC_LOWRANK, shape, p);
 
   memset(&p, 0, sizeof p);
   p.grid_w = 16; /* 128 tokens = 8 rows of 16: one row of two 8 x 8 blocks */

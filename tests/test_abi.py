@@ -37,7 +37,7 @@ def test_exports_every_declared_function(rc):
 
 
 def test_status_strings(rc):
-    for s in range(5):
+    for s in range(7):
         assert rc.rc_status_string(s).startswith("RC_")
     assert "unknown" in rc.rc_status_string(99)
 
@@ -48,19 +48,19 @@ def test_status_strings(rc):
     ("q2", dict(group=128), dict(group=7)),
     ("nm", dict(nm_keep=2, nm_block=16), dict(nm_keep=4)),
     ("nm", dict(nm_keep=2, nm_block=16), dict(nm_block=1)),
-    ("lr", dict(rank=32, iters=2), dict(q0=None)),
+    ("lr", dict(rank=32, iters=2), dict(iters=17)),
     ("lr", dict(rank=32, iters=2), dict(rank=24)),
     ("lr", dict(rank=32, iters=2), dict(rank=4)),
     ("lr", dict(rank=32, iters=2), dict(rank=80)),
     ("lr", dict(rank=32, iters=2), dict(iters=0)),
-    ("lr", dict(rank=32, iters=2), dict(flags=4)),                # unknown flag
+    ("lr", dict(rank=32, iters=2), dict(flags=4)),                # a block-selection flag
+    ("lr", dict(rank=32, iters=2), dict(flags=32)),               # unknown flag
+    ("bs", dict(grid_w=16, keep_blocks=1), dict(flags=1)),        # a low-rank flag
     ("q2", dict(group=128), dict(flags=2)),                       # a low-rank flag
 ])
 def test_plan_validation(rc, scheme, kw, bad):
     kw = dict(kw)
     kw.update(bad)
-    if scheme == "lr" and "q0" not in bad:  # start matrices of the rank asked for
-        kw["q0"] = np.zeros((2, 256, max(kw["rank"], 1)), np.float32)
     with pytest.raises(rc.RcError) as ei:
         rc.Plan((2, 128, 256), "bf16", scheme, **kw)
     assert ei.value.status in (rc.RC_ERR_INVALID_ARG, rc.RC_ERR_UNSUPPORTED)
@@ -99,12 +99,11 @@ def test_packed_sizes_match_oracle_layout(rc, scheme, kw, shape):
 def test_lowrank_rank8_rejected_above_rows(rc):
     # rank 8 is accepted (the GPU parity tests run it) but, as every rank,
     # never above the rows or columns of the tensor; checked before allocating
-    q0 = np.zeros((2, 256, 8), np.float32)
     with pytest.raises(rc.RcError) as ei:
-        rc.Plan((2, 6, 256), "bf16", "lr", rank=8, iters=2, q0=q0)   # rank > rows
+        rc.Plan((2, 6, 256), "bf16", "lr", rank=8, iters=2)   # rank > rows
     assert ei.value.status == rc.RC_ERR_INVALID_ARG
-    with pytest.raises(rc.RcError) as ei:                            # reconstruct grid limit
-        rc.Plan((1, 65535 * 32 + 1, 64), "bf16", "lr", rank=8, iters=2, q0=q0[:1, :64])
+    with pytest.raises(rc.RcError) as ei:                     # reconstruct grid limit
+        rc.Plan((1, 65535 * 32 + 1, 64), "bf16", "lr", rank=8, iters=2)
     assert ei.value.status == rc.RC_ERR_UNSUPPORTED
 
 
@@ -188,3 +187,34 @@ def test_binding_refuses_host_or_short_tensors(rc):
             p.compress(a, st, st.clone(), pk)
         with pytest.raises(ValueError, match="device tensor"):
             p.decompress(pk, st)
+
+
+def test_binding_refuses_input_of_the_other_dtype(rc):
+    # an fp32 a_t given to a bf16 plan is twice as long as needed, so the size
+    # check alone would pass it and the kernels would read it as bf16 pairs
+    import torch
+    with rc.Plan((2, 8, 128), "bf16", "q2", group=128) as p:
+        st = torch.zeros(2, 8, 128)
+        pk = torch.zeros(p.packed_bytes, dtype=torch.uint8)
+        with pytest.raises(ValueError, match="plan takes torch.bfloat16"):
+            p.compress(torch.zeros(2, 8, 128), st, st.clone(), pk)
+        with pytest.raises(ValueError, match="plan takes torch.bfloat16"):
+            p.compress_send(torch.zeros(2, 8, 128), st, st.clone(), pk, pk.clone(), 1, None)
+    with rc.Plan((2, 8, 128), "f32", "q1", group=64) as p:
+        st = torch.zeros(2, 8, 128)
+        pk = torch.zeros(p.packed_bytes, dtype=torch.uint8)
+        with pytest.raises(ValueError, match="plan takes torch.float32"):
+            p.compress(torch.zeros(2, 8, 128, dtype=torch.bfloat16), st, st.clone(), pk)
+
+
+def test_debug_flags_are_per_scheme(rc):
+    # RC_CHECK_FINITE is taken by every scheme, RC_LR_CHECK_NUMERIC only by low
+    # rank, RC_BS_SCORE_LAST_SENT only by block selection (checked before any
+    # device work, so these plans fail or pass validation without a GPU)
+    for scheme, kw in (("q2", dict(group=128)), ("nm", dict(nm_keep=2, nm_block=16))):
+        with pytest.raises(rc.RcError) as ei:
+            rc.Plan((2, 8, 128), "bf16", scheme, flags=rc.RC_LR_CHECK_NUMERIC, **kw)
+        assert ei.value.status == rc.RC_ERR_INVALID_ARG
+        with pytest.raises(rc.RcError) as ei:
+            rc.Plan((2, 8, 128), "bf16", scheme, flags=rc.RC_BS_SCORE_LAST_SENT, **kw)
+        assert ei.value.status == rc.RC_ERR_INVALID_ARG

@@ -1,8 +1,11 @@
 """GPU parity of Otil-style block selection (RC_BLOCKSEL) against the CPU oracle.
 
 Page: "Otil: Accelerating Diffusion Model Inference via Communication-Efficient
-Multi-GPU Parallelism", Key designs 1-3. Every step is teacher-forced (the
-oracle starts from the GPU's previous ahat and round state). The choice of
+Multi-GPU Parallelism", Key designs 1-3: blocks are scored against the same
+block at the previous step (the plan keeps that activation); the option
+RC_BS_SCORE_LAST_SENT scores against the receiver's copy instead, and both are
+checked. Every step is teacher-forced (the oracle starts from the GPU's
+previous ahat and round state). The choice of
 blocks rests on fp64 cosine scores whose last bits depend on summation order,
 so the selection is checked for what is unique: if it equals the oracle's it
 must match exactly; otherwise it must still be a valid top-k of the oracle's
@@ -31,11 +34,13 @@ def _valid_topk(sel, d, visited, keep, tol=1e-12):
     return rest.size == 0 or d[sel].min() >= d[rest].max() - tol
 
 
-def _run(wl, grid_w, keep, steps, check=None, zero_step=False):
+def _run(wl, grid_w, keep, steps, check=None, zero_step=False, last_sent=False):
     B, n, m, dtype = wl.nb, wl.n, wl.m, wl.dtype
     K = n // 64
     in_dtype = "bf16" if dtype == "bf16" else "f32"
-    with rc.Plan((B, n, m), dtype, "bs", grid_w=grid_w, keep_blocks=keep) as plan:
+    score = "last_sent" if last_sent else "prev"
+    flags = rc.RC_BS_SCORE_LAST_SENT if last_sent else 0
+    with rc.Plan((B, n, m), dtype, "bs", grid_w=grid_w, keep_blocks=keep, flags=flags) as plan:
         assert plan.tensor_packed_bytes == oracle.tensor_bytes(
             "bs", n, m, keep=keep, in_bytes=2 if dtype == "bf16" else 4)
         _, a0 = wl.next()
@@ -44,7 +49,8 @@ def _run(wl, grid_w, keep, steps, check=None, zero_step=False):
         recon = ahat.clone()
         e = torch.zeros_like(ahat)
         packed = torch.empty(plan.packed_bytes, dtype=torch.uint8, device=DEV)
-        prev = lib_view_f32(a0, dtype).copy()
+        prev = lib_view_f32(a0, dtype).copy()      # sender state (GPU's ahat)
+        prev_a = lib_view_f32(a0, dtype).copy()    # the previous step's activation
         visited = [np.zeros(K, bool) for _ in range(B)]
         sent = [np.zeros(K, int) for _ in range(B)]
         tb = plan.tensor_packed_bytes
@@ -66,34 +72,71 @@ def _run(wl, grid_w, keep, steps, check=None, zero_step=False):
                 head = tp[:4 * (1 + keep)].view(np.uint32)
                 gsel = head[1:1 + head[0]].astype(np.int64)
                 o = oracle.bs_compress_tensor(af[b], prev[b], grid_w=grid_w, keep=keep,
-                                              visited=visited[b], in_dtype=in_dtype)
+                                              visited=visited[b], prev=prev_a[b], score=score,
+                                              in_dtype=in_dtype)
                 same = np.array_equal(gsel, o["selected"])
-                say("[gpu] bs t=%d b=%d sent %d blocks, same as oracle: %s" % (t, b, gsel.size, same))
+                say("[gpu] bs %s t=%d b=%d sent %d blocks, same as oracle: %s" % (score, t, b, gsel.size, same))
                 if not same:
                     assert _valid_topk(gsel, o["scores"], visited[b], keep)
                     o = oracle.bs_compress_tensor(af[b], prev[b], grid_w=grid_w, keep=keep,
-                                                  visited=visited[b], in_dtype=in_dtype, selected=gsel)
+                                                  visited=visited[b], prev=prev_a[b], score=score,
+                                                  in_dtype=in_dtype, selected=gsel)
                 assert np.array_equal(tp, o["packed"])
                 assert np.array_equal(bits(eh[b]), bits(o["e"]))
                 assert np.array_equal(bits(ah[b]), bits(o["ahat"]))
                 visited[b] = o["visited"]
                 sent[b][gsel] += 1
             prev = ah
+            prev_a = af
         return sent
 
 
-def test_latent_rounds_every_block_once():
+@pytest.mark.parametrize("last_sent", [False, True])
+def test_latent_rounds_every_block_once(last_sent):
     wl = synth.LatentWorkload(batch=2, height=32, width=64, m=64, steps=10)
     K, keep = 32, 8
-    sent = _run(wl, 64, keep, steps=9)   # 8 compressed steps = 2 full rounds
+    sent = _run(wl, 64, keep, steps=9, last_sent=last_sent)   # 8 compressed steps = 2 full rounds
     for s in sent:
         assert np.all(s == 2)
 
 
 @pytest.mark.parametrize("keep", [1, 5, 32])
-def test_latent_keep_sizes(keep):
+@pytest.mark.parametrize("last_sent", [False, True])
+def test_latent_keep_sizes(keep, last_sent):
     wl = synth.LatentWorkload(batch=2, height=32, width=64, m=64, steps=5)
-    _run(wl, 64, keep, steps=5)
+    _run(wl, 64, keep, steps=5, last_sent=last_sent)
+
+
+def test_page_rule_and_last_sent_copy_pick_different_blocks():
+    """The hand-built two-step case of the oracle pins (one block flips and is
+    sent, one turns by 90 degrees and is not, then a third turns by 45 degrees):
+    the page's rule sends the third block at step 2, the last-sent option the
+    second; the GPU follows each rule."""
+    gw, m = 24, 8
+    n = 8 * gw
+    tok = [oracle.bs_block_tokens(i, gw) for i in range(3)]
+    u, w = np.zeros(m, np.float32), np.zeros(m, np.float32)
+    u[0], w[1] = 1.0, 1.0
+    a0 = np.zeros((n, m), np.float32)
+    for i in range(3):
+        a0[tok[i]] = u
+    a1 = a0.copy()
+    a1[tok[0]] = w
+    a1[tok[2]] = -u
+    a2 = a1.copy()
+    a2[tok[1]] = u + w
+    for flags, want in ((0, 1), (rc.RC_BS_SCORE_LAST_SENT, 0)):
+        with rc.Plan((1, n, m), "f32", "bs", grid_w=gw, keep_blocks=1, flags=flags) as plan:
+            ahat = to_device(a0[None], "f32")
+            e = torch.zeros_like(ahat)
+            packed = torch.empty(plan.packed_bytes, dtype=torch.uint8, device=DEV)
+            heads = []
+            for a in (a1, a2):
+                plan.compress(to_device(a[None], "f32"), ahat, e, packed)
+                torch.cuda.synchronize()
+                heads.append(packed.cpu().numpy()[:8].view(np.uint32).tolist())
+            say("[gpu] bs two-step case flags %d: %s" % (flags, heads))
+            assert heads == [[1, 2], [1, want]]
 
 
 @pytest.mark.parametrize("n,m,grid_w,keep", [(64, 4, 8, 1), (128, 8, 16, 1), (128, 4, 8, 2)])

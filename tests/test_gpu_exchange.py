@@ -5,17 +5,23 @@ chunk's packed bytes on a second stream while the next chunk is compressed
 (CompactFusion notes, Key designs / System co-design: compression overlapped
 with communication). Its packed stream, the copy at the destination (device
 buffer or pinned host memory) and the sender state must equal those of one
-rc_compress call bit for bit, whatever the chunk size.
+rc_compress call bit for bit, whatever the chunk size, and every tensor must
+match the CPU oracle: bit for bit for 1-bit, 2-bit and 2:16 (packed bytes, e,
+ahat); for low rank, the relative error of ahat within 1e-3 of the oracle's
+and e, ahat within the decode bound of the oracle's decoder applied to the
+GPU's factors.
 
 rc_decompress_many decodes several peers' packed streams into their receiver
 states (Overall framework: each GPU rebuilds every peer's activation); it must
-equal one rc_decompress per peer bit for bit.
+equal one rc_decompress per peer bit for bit, and each peer's state must equal
+the oracle's decoder applied to that peer's packed stream (bit for bit, or
+within the reconstruction bound for low rank).
 """
 import numpy as np
 import pytest
 import torch
 
-from gpu_harness import DEV, lib_view_f32, say, to_device
+from gpu_harness import DEV, bits, lib_view_f32, oracle, relF, say, to_device
 from activation_residual_compression_amd import librescomp as rc
 from activation_residual_compression_amd import synth
 
@@ -39,6 +45,51 @@ def _inputs(scheme, dtype, kw, B, n, m, seed_tensors=None):
 
 def _bits(t):
     return t.detach().cpu().numpy().view(np.uint8)
+
+
+def _okw(scheme, kw):
+    if scheme in ("q1", "q2"):
+        return dict(group=kw["group"])
+    if scheme == "lr":
+        return dict(rank=kw["rank"], iters=kw["iters"])
+    return {}
+
+
+def _lr_bound(c_src, prev, got, rank, extra=None):
+    """|got - fl(prev + c)| within the fp32 reconstruct's rounding (rank terms),
+    c from the oracle's decoder applied to the GPU's own factors."""
+    c, mag = c_src
+    want = (prev.astype(np.float64) + (c if extra is None else extra)).astype(np.float32)
+    tol = rank * 2.0 ** -23 * mag + np.spacing(np.abs(want)).astype(np.float64)
+    return np.all(np.abs(got.astype(np.float64) - want) <= tol)
+
+
+def _lr_decode(packed_t, n, m, rank):
+    f = oracle.unpack_fields("lr", packed_t, n, m, rank=rank)
+    U = f["qu"].astype(np.float64) * f["su"].astype(np.float64)
+    V = f["qv"].astype(np.float64) * f["sv"].astype(np.float64)
+    return U @ V.T, np.abs(U) @ np.abs(V).T
+
+
+def _check_sender_vs_oracle(scheme, kw, params, a_f, start_f, packed, ahat, e, ts):
+    """Every tensor of one compress against the oracle from the same state."""
+    B = a_f.shape[0]
+    n, m = a_f.shape[1:]
+    for b in range(B):
+        gp = packed[b * ts:(b + 1) * ts]
+        if scheme == "lr":
+            o = oracle.compress_tensor("lr", a_f[b], start_f[b], q0=params["q0"][b], **_okw(scheme, kw))
+            eg, eo = relF(a_f[b], ahat[b]), relF(a_f[b], o["ahat"])
+            assert abs(eg - eo) <= 1e-3, (b, eg, eo)
+            c, mag = _lr_decode(gp, n, m, kw["rank"])
+            r = (a_f[b] - start_f[b]).astype(np.float32)
+            assert _lr_bound((c, mag), start_f[b], ahat[b], kw["rank"])
+            assert _lr_bound((c, mag), r, e[b], kw["rank"], extra=-c)
+        else:
+            o = oracle.compress_tensor(scheme, a_f[b], start_f[b], **_okw(scheme, kw))
+            assert np.array_equal(gp, o["packed"]), b
+            assert np.array_equal(bits(ahat[b]), bits(o["ahat"])), b
+            assert np.array_equal(bits(e[b]), bits(o["e"])), b
 
 
 @pytest.mark.parametrize("scheme,dtype,kw", SCHEMES)
@@ -70,6 +121,11 @@ def test_compress_send_equals_compress(scheme, dtype, kw, chunk, dest):
         assert np.array_equal(packed_dst.cpu().numpy(), ref)
         assert np.array_equal(_bits(ahat_s), _bits(ahat_ref))
         assert np.array_equal(_bits(e_s), _bits(e_ref))
+        # and each tensor against the oracle, from the same start state
+        a_f = lib_view_f32(a1, "bf16") if dtype == "bf16" else np.asarray(a1, np.float32)
+        start_f = start.cpu().numpy()
+        _check_sender_vs_oracle(scheme, kw, params, a_f, start_f, packed_dst.cpu().numpy(),
+                                ahat_s.cpu().numpy(), e_s.cpu().numpy(), plan.tensor_packed_bytes)
 
 
 @pytest.mark.parametrize("scheme,dtype,kw", SCHEMES)
@@ -98,6 +154,19 @@ def test_decompress_many_equals_one_call_per_peer(scheme, dtype, kw, npeers):
             plan.decompress(packed[p], seq[p])
         plan.decompress_many(packed, many)
         torch.cuda.synchronize()
+        ts = plan.tensor_packed_bytes
         for p in range(npeers):
             assert np.array_equal(_bits(many[p]), _bits(seq[p])), p
             assert not np.array_equal(_bits(many[p]), _bits(states[p])), p  # something was applied
+            # the oracle's receiver applied to this peer's packed stream
+            pk = packed[p].cpu().numpy()
+            st0 = states[p].cpu().numpy()
+            got = many[p].cpu().numpy()
+            for b in range(B):
+                if scheme == "lr":
+                    c, mag = _lr_decode(pk[b * ts:(b + 1) * ts], n, m, kw["rank"])
+                    assert _lr_bound((c, mag), st0[b], got[b], kw["rank"]), (p, b)
+                else:
+                    want = oracle.decompress_tensor(scheme, pk[b * ts:(b + 1) * ts], st0[b],
+                                                    **_okw(scheme, kw))
+                    assert np.array_equal(bits(got[b]), bits(want)), (p, b)

@@ -12,11 +12,14 @@ GPU, fp64 in the oracle), so parity is by tolerance on what the method fixes:
   * INT4 codes of U mostly identical to the oracle's (basis fixed by CQR2);
   * degenerate residuals (zero, rank-deficient) give finite, exact-zero updates.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
 
-from gpu_harness import GpuRun, lib_view_f32, oracle, relF, say, synth, bits
+from gpu_harness import GpuRun, bits, lib_view_f32, oracle, relF, say, synth, to_device
 from activation_residual_compression_amd import librescomp as rc
 
 pytestmark = pytest.mark.gpu
@@ -183,6 +186,21 @@ def test_lr_free_running_trajectory_matches_oracle():
         run.close()
 
 
+SENSITIVITY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                           "lr_free_running_sensitivity.json")
+
+
+def _sensitivity_bounds():
+    """Per-step and second-half-mean bounds on the relative gap of the relative
+    error, from two free-running oracle runs that differ by one rounding-sized
+    perturbation (tests/golden/make_lr_sensitivity.py): twice the largest gap
+    seen there, since the GPU's own differences enter at every step."""
+    d = json.load(open(SENSITIVITY))
+    runs = [r[k] for r in d["tensors"].values() for k in ("input", "state")]
+    return (2 * max(r["max_rel_gap"] for r in runs),
+            2 * max(r["second_half_mean_rel_gap"] for r in runs))
+
+
 def test_lr_free_running_flux_shape_half_sequence():
     """Free-running at the flux tensor shape (1152 x 3072, rank 32, 2 iterations)
     over the first half of a 28-step sequence, the GPU and the oracle each
@@ -191,12 +209,12 @@ def test_lr_free_running_flux_shape_half_sequence():
     Per step, from the same state, the two agree on the relative error of the
     reconstruction within 1e-3 (the teacher-forced tests). Free-running, the
     tiny per-step differences (fp32 against fp64 factors) feed back through the
-    residual and the subspace iteration, whose rank-32 subspace is poorly fixed
-    where the residual's trailing singular values are nearly equal, so the two
-    trajectories part slowly, as two runs of the method from perturbed inputs
-    would. What must hold is that neither drifts away: the relative error of
-    each step within 5 % of the oracle's, and its mean over the second half
-    within 2 %."""
+    residual and the subspace iteration. The method itself is that sensitive:
+    two oracle runs whose inputs differ by one bf16 ulp in one element, or whose
+    state differs by one fp32 ulp, part by up to 3.5-5 % per step and 1-3 % on
+    the second-half means at this shape (the committed sensitivity fixture).
+    The GPU must stay within twice that of the oracle."""
+    step_bound, mean_bound = _sensitivity_bounds()
     steps = 14
     wl = synth.FluxWorkload(batch=2, n=1152, m=3072, steps=steps + 1)
     q0 = wl.q0(32)
@@ -220,11 +238,11 @@ def test_lr_free_running_flux_shape_half_sequence():
     finally:
         run.close()
     for (t, b, eg), (_, _, eo) in zip(eps_g, eps_o):
-        assert abs(eg - eo) <= 0.05 * eo, (t, b, eg, eo)
+        assert abs(eg - eo) <= step_bound * eo, (t, b, eg, eo, step_bound)
     for b in range(2):
         g = np.mean([e for t, bb, e in eps_g if bb == b and t > steps // 2])
         o = np.mean([e for t, bb, e in eps_o if bb == b and t > steps // 2])
-        assert abs(g - o) <= 0.02 * o, (b, g, o)
+        assert abs(g - o) <= mean_bound * o, (b, g, o, mean_bound)
 
 
 @pytest.mark.parametrize("config,check", [("flux_lr", [0, 56]), ("video_lr", [0])])
@@ -233,3 +251,138 @@ def test_lr_full_size_sampled_tensors(config, check):
     wl = synth.make(config, steps=2)
     _run_lr(wl, spec["rank"], spec["iters"], check=check)
     torch.cuda.empty_cache()
+
+
+# Exact agreement of factor codes is a sanity check only: the factors are an
+# orthonormal basis of the dominant subspace, which fp32 and fp64 arithmetic fix
+# only up to small rotations among directions of nearly equal singular values,
+# and every further iteration carries those rounding differences along. At 3-4
+# iterations 78-89 % of the bf16 factor entries agree exactly (against 95 % at
+# 1-2); the parity criterion is the relative error of ahat, within 1e-3.
+MORE_ITERS_BF16_AGREE = 0.7
+
+
+@pytest.mark.parametrize("iters", [3, 4])
+@pytest.mark.parametrize("factors", ["int4", "bf16"])
+def test_lr_more_iterations_small(iters, factors):
+    wl = synth.FluxWorkload(batch=2, n=100, m=192, steps=3)
+    _run_lr(wl, 16, iters, check=[0, 1], factors=factors,
+            code_agree=MORE_ITERS_BF16_AGREE if factors == "bf16" else 0.8)
+
+
+@pytest.mark.parametrize("shape,rank,iters,factors", [
+    ((2, 1152, 3072), 32, 3, "int4"), ((2, 1152, 3072), 32, 4, "bf16"),
+    ((1, 4444, 1920), 48, 3, "bf16"), ((1, 4444, 1920), 48, 4, "int4")])
+def test_lr_more_iterations_full_shapes(shape, rank, iters, factors):
+    """Iteration counts 3 and 4 (the sweep's) at the flux and video tensor
+    shapes, teacher-forced against the oracle."""
+    B, n, m = shape
+    if n == 1152:
+        wl = synth.FluxWorkload(batch=B, steps=2)
+    else:
+        wl = synth.VideoWorkload(batch=B, steps=2)
+    _run_lr(wl, rank, iters, check=[0], factors=factors,
+            code_agree=MORE_ITERS_BF16_AGREE if factors == "bf16" else 0.8)
+    torch.cuda.empty_cache()
+
+
+def test_lr_seeded_start_matrices_equal_the_generator():
+    """q0 = NULL: the plan draws its start matrices from the seed (SplitMix64 and
+    Box-Muller as the header defines them). They must be the input generator's
+    draw for that seed -- each implementation's own code for the published
+    generators -- and a seeded plan then gives the same bytes as a plan handed
+    those matrices."""
+    B, n, m, k = 3, 100, 320, 16
+    seed = 0x5EED0001
+    want = synth.start_matrices(seed, range(B), m, k)
+    want_bits = oracle.bf16_bits(want)   # [B][m][k] -> the plan keeps bf16 Q0^T
+    wl = synth.FluxWorkload(batch=B, n=n, m=m, steps=2)
+    _, a0 = wl.next()
+    _, a1 = wl.next()
+    with rc.Plan((B, n, m), "bf16", "lr", rank=k, iters=2, seed=seed) as ps, \
+            rc.Plan((B, n, m), "bf16", "lr", rank=k, iters=2, q0=want) as pg:
+        ptrs, _ = ps.lowrank_workspace()
+        torch.cuda.synchronize()
+        got = rc.rcx_device_to_host(ptrs[4], B * k * m * 2).view(np.uint16).reshape(B, k, m)
+        mismatch = np.count_nonzero(got != want_bits.transpose(0, 2, 1))
+        say("[gpu] seeded start matrices: %d of %d bf16 entries differ" % (mismatch, got.size))
+        assert mismatch <= got.size // 100000
+        outs = []
+        for p in (ps, pg):
+            a = to_device(a1, "bf16")
+            ahat = to_device(a0, "bf16").float()
+            e = torch.zeros_like(ahat)
+            pk = torch.empty(p.packed_bytes, dtype=torch.uint8, device="cuda")
+            p.compress(a, ahat, e, pk)
+            torch.cuda.synchronize()
+            outs.append(pk.cpu().numpy())
+        if mismatch == 0:
+            assert np.array_equal(outs[0], outs[1])
+
+
+def test_lr_check_numeric_reports_dead_pivots():
+    """RC_LR_CHECK_NUMERIC: a zero residual makes every pivot dead and the call
+    returns RC_ERR_NUMERIC (with the default path's results: zero factors, no
+    update); a generic residual passes, with the same results as without the
+    flag."""
+    wl = synth.FluxWorkload(batch=2, n=100, m=192, steps=2)
+    _, a0 = wl.next()
+    _, a1 = wl.next()
+    q0 = wl.q0(16)
+    res = {}
+    for flags in (0, rc.RC_LR_CHECK_NUMERIC):
+        with rc.Plan((2, 100, 192), "bf16", "lr", rank=16, iters=2, q0=q0,
+                     flags=flags | rc.RC_LR_ONE_STREAM) as p:
+            a = to_device(a1, "bf16")
+            ahat = to_device(a0, "bf16").float()
+            e = torch.zeros_like(ahat)
+            pk = torch.empty(p.packed_bytes, dtype=torch.uint8, device="cuda")
+            p.compress(a, ahat, e, pk)
+            torch.cuda.synchronize()
+            res[flags] = (pk.cpu().numpy(), ahat.cpu().numpy(), e.cpu().numpy())
+            if flags:
+                z = to_device(a0, "bf16")
+                ahat0 = z.float().clone()
+                with pytest.raises(rc.RcError) as ei:
+                    p.compress(z, ahat0, e, pk)
+                assert ei.value.status == rc.RC_ERR_NUMERIC
+                torch.cuda.synchronize()
+                assert np.array_equal(bits(ahat0.cpu().numpy()), bits(lib_view_f32(a0, "bf16")))
+    for x, y in zip(res[0], res[rc.RC_LR_CHECK_NUMERIC]):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+@pytest.mark.parametrize("scheme,kw", [("q1", dict(group=64)), ("lr", dict(rank=16, iters=2))])
+def test_check_finite_rejects_nan_before_launching(scheme, kw):
+    wl = synth.FluxWorkload(batch=2, n=100, m=192, steps=2)
+    _, a0 = wl.next()
+    _, a1 = wl.next()
+    with rc.Plan((2, 100, 192), "bf16", scheme, flags=rc.RC_CHECK_FINITE, **kw) as p, \
+            rc.Plan((2, 100, 192), "bf16", scheme, **kw) as ref:
+        a = to_device(a1, "bf16")
+        outs = []
+        for plan in (p, ref):
+            ahat = to_device(a0, "bf16").float()
+            e = torch.zeros_like(ahat)
+            pk = torch.zeros(plan.packed_bytes, dtype=torch.uint8, device="cuda")
+            plan.compress(a, ahat, e, pk)
+            torch.cuda.synchronize()
+            outs.append((pk.cpu().numpy(), ahat.cpu().numpy(), e.cpu().numpy()))
+        for x, y in zip(*outs):
+            assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+        bad = a.clone()
+        bad[1, 7, 5] = float("nan")
+        ahat = to_device(a0, "bf16").float()
+        e = torch.full_like(ahat, 3.0)
+        pk = torch.full((p.packed_bytes,), 0x5A, dtype=torch.uint8, device="cuda")
+        with pytest.raises(rc.RcError) as ei:
+            p.compress(bad, ahat, e, pk)
+        assert ei.value.status == rc.RC_ERR_NONFINITE
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(ahat.cpu().numpy()), bits(lib_view_f32(a0, "bf16")))
+        assert bool((e == 3.0).all()) and bool((pk == 0x5A).all())
+        inf_state = to_device(a0, "bf16").float()
+        inf_state[0, 3, 3] = float("inf")
+        with pytest.raises(rc.RcError) as ei:
+            p.compress(a, inf_state, e, pk)
+        assert ei.value.status == rc.RC_ERR_NONFINITE

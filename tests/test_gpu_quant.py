@@ -138,9 +138,10 @@ def _q1_order_sensitive_groups(n, m, group, seed):
 
 @pytest.mark.parametrize("group", [32, 64, 128])
 def test_q1_summation_order_sensitive_groups(group):
-    """The 1-bit scale is an fp64 sum in a fixed order (runs of 4, then a
-    pairwise tree); on groups where that order decides the fp32 scale the GPU
-    must still match the oracle bit for bit."""
+    """The 1-bit scale is the exactly rounded mean of |r| (the oracle adds the
+    magnitudes as integers). On groups where any floating-point summation
+    order decides the last bit, the kernel (exact fp64 sum when the exponents
+    span few binades, an exact integer sum otherwise) must match bit for bit."""
     n, m = 48, 512
     a = _q1_order_sensitive_groups(n, m, group, seed=11)
     ahat = np.zeros((n, m), np.float32)
@@ -153,6 +154,30 @@ def test_q1_summation_order_sensitive_groups(group):
     try:
         run.set_state(ahat[None])
         say("[gpu] q1 order-sensitive groups, group %d" % group)
+        run.step(a[None])
+        packed, e, ahat_g, recon = run.fetch()
+        check_exact_step(run, 0, a, ahat, packed, e, ahat_g, recon, dict(group=group))
+    finally:
+        run.close()
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_q1_wide_magnitude_spans_exact_path(group):
+    """Residuals whose magnitudes span the whole fp32 range (subnormals, the
+    largest normals, zeros) in every group: the exact integer path of the
+    kernel against the oracle's exact mean, bit for bit, packed bytes and
+    state included; plus groups mixing both paths within one wave."""
+    n, m = 24, 512
+    rng = np.random.default_rng(group)
+    ex = rng.integers(-149, 127, (n, m))
+    a = (np.ldexp(rng.uniform(1.0, 2.0, (n, m)), ex) * rng.choice([-1.0, 1.0], (n, m))).astype(np.float32)
+    a[rng.random((n, m)) < 0.05] = 0.0
+    a[::3] = rng.standard_normal((len(a[::3]), m)).astype(np.float32)   # fast-path rows between
+    ahat = np.zeros((n, m), np.float32)
+    run = GpuRun((1, n, m), "f32", "q1", group=group)
+    try:
+        run.set_state(ahat[None])
+        say("[gpu] q1 wide spans, group %d" % group)
         run.step(a[None])
         packed, e, ahat_g, recon = run.fetch()
         check_exact_step(run, 0, a, ahat, packed, e, ahat_g, recon, dict(group=group))

@@ -101,3 +101,58 @@ def test_schedule_switch_keeps_receiver_equal():
                                                **({"group": 64} if info["kind"] == "q1" else {}))
                     assert np.array_equal(bits(ah[b]), bits(o["ahat"])), (t, b)
             prev = ah
+
+
+@pytest.mark.parametrize("mode", ["noef", "direct"])
+def test_lowrank_ablation_modes_match_oracle_trajectory(mode):
+    """Low rank in the two ablation modes against oracle.run_trajectory. The
+    compression input of both modes does not depend on the state (noef: the
+    step change a_t - a_{t-1}; direct: a_t), so the GPU and the oracle compress
+    the same residuals every step and the relative errors of the receiver
+    state agree within the per-step 1e-3."""
+    wl = synth.FluxWorkload(batch=2, n=96, m=256, steps=6)
+    frames = _frames(wl)
+    q0 = wl.q0(16)
+    schemes = {"lr": ("lr", dict(rank=16, iters=2, q0=q0))}
+    with Session((2, 96, 256), "bf16", schemes, Schedule([(1, "lr")]), mode=mode) as s:
+        gpu = []
+        for a in frames:
+            s.step(to_device(a, "bf16"))
+            torch.cuda.synchronize()
+            gpu.append(s.recon.cpu().numpy())
+    for b in range(2):
+        fr = [lib_view_f32(f[b], "bf16") for f in frames]
+        ref = oracle.run_trajectory(mode, "lr", fr, rank=16, iters=2, q0=q0[b])
+        for t in range(1, len(frames)):
+            eg, eo = relF(fr[t], gpu[t][b]), relF(fr[t], ref[t])
+            say("[gpu] lr %s t=%d b=%d eps gpu %.5f oracle %.5f" % (mode, t, b, eg, eo))
+            assert abs(eg - eo) <= 1e-3, (t, b, eg, eo)
+
+
+@pytest.mark.parametrize("scheme,params", [("q2", dict(group=128)), ("bs", dict(grid_w=32, keep_blocks=4))])
+@pytest.mark.parametrize("mode", ["closed", "noef", "direct"])
+def test_session_on_a_side_stream_equals_current_stream(scheme, params, mode):
+    """Session.step(stream=s) with s not the current stream: the state updates
+    around the library calls run on s too, so the results equal those of the
+    same steps on the current stream bit for bit."""
+    if scheme == "bs":
+        wl = synth.LatentWorkload(batch=2, height=16, width=32, m=64, steps=6)
+    else:
+        wl = synth.FluxWorkload(batch=2, n=48, m=256, steps=6)
+    frames = _frames(wl)
+    sched = Schedule([(1, scheme)], full_steps=1)
+    out = []
+    for use_side in (False, True):
+        side = torch.cuda.Stream() if use_side else None
+        with Session((2, wl.n, wl.m), "bf16", {scheme: (scheme, params)}, sched, mode=mode) as s:
+            inputs = []   # kept alive until the side stream has read them
+            for a in frames:
+                inputs.append(to_device(a, "bf16"))
+                if side is not None:
+                    side.wait_stream(torch.cuda.current_stream())
+                s.step(inputs[-1], stream=side)
+            torch.cuda.synchronize()
+            out.append((s.recon.cpu().numpy(), s.ahat.cpu().numpy(), s.e.cpu().numpy()))
+    for x, y in zip(out[0], out[1]):
+        assert np.array_equal(bits(x), bits(y))
+    say("[gpu] session %s %s on a side stream: identical" % (scheme, mode))
