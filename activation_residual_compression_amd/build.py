@@ -23,7 +23,7 @@ LIB = os.path.join(HERE, "lib", "librescomp.so")
 RESOURCES = os.path.join(HERE, "lib", "kernel_resources.json")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["quant.hip", "nm.hip", "lowrank.hip", "blocksel.hip", "checks.hip", "probe.hip", "plan.cpp"]
+SOURCES = ["quant.hip", "nm.hip", "lowrank.hip", "blocksel.hip", "checks.hip", "noalloc.hip", "probe.hip", "plan.cpp"]
 ARCH = os.environ.get("RC_OFFLOAD_ARCH", "gfx950")
 FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

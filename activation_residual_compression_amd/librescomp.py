@@ -70,6 +70,9 @@ def _load():
                                    ctypes.POINTER(rc_params_t), ctypes.POINTER(vp)]
     lib.rc_compress.restype = st
     lib.rc_compress.argtypes = [vp, vp, vp, ctypes.POINTER(rc_state_t), vp]
+    lib.rc_compress_lowrank_noalloc.restype = st
+    lib.rc_compress_lowrank_noalloc.argtypes = [rc_shape_t, ctypes.c_int, ctypes.POINTER(rc_params_t),
+                                                vp, vp, ctypes.POINTER(rc_state_t), vp]
     lib.rc_decompress.restype = st
     lib.rc_decompress.argtypes = [vp, vp, vp, vp]
     lib.rc_compress_send.restype = st
@@ -168,6 +171,19 @@ def rc_plan_create(shape, dtype, scheme, params: rc_params_t):
 def rc_compress(plan, stream, a_t, state: rc_state_t, packed_out):
     _check(_lib.rc_compress(plan, _stream(stream), _ptr(a_t), ctypes.byref(state), _ptr(packed_out)),
            "rc_compress")
+
+
+RC_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def rc_compress_lowrank_noalloc(shape, dtype, params: rc_params_t, stream, a_t, state: rc_state_t,
+                                packed_out):
+    """The plan-free, allocation-free low-rank sender step (librescomp.h)."""
+    if not isinstance(shape, rc_shape_t):
+        shape = rc_shape_t(*shape)
+    _check(_lib.rc_compress_lowrank_noalloc(shape, int(DTYPES.get(dtype, dtype)), ctypes.byref(params),
+                                            _stream(stream), _ptr(a_t), ctypes.byref(state),
+                                            _ptr(packed_out)), "rc_compress_lowrank_noalloc")
 
 
 def rc_decompress(plan, stream, packed_in, recon_state):

@@ -232,6 +232,26 @@ rc_status_t rc_decompress_many(rc_plan_t plan, hipStream_t stream, const void* c
  * stream; no effect for the other schemes. */
 rc_status_t rc_plan_reset_state(rc_plan_t plan, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the RC_LOWRANK sender
+ * step of rc_compress without a plan. It validates shape, dtype and params as
+ * rc_plan_create does (flags: 0 or RC_LR_BF16_FACTORS), sets up the start
+ * matrices (from params->q0, a device pointer, or params->seed) and runs the
+ * plan's kernels on `stream` alone; a_t, state and packed_out are as for
+ * rc_compress (packed_out: the bytes rc_packed_bytes of such a plan reports),
+ * and the results equal rc_compress's bit for bit. It allocates nothing: the
+ * workspace is a fixed device array of RC_NOALLOC_SCRATCH_BYTES held by every
+ * GPU the library runs on until the process ends, so shapes whose workspace
+ * (rc_workspace_bytes of the equivalent plan) is larger are rejected with
+ * RC_ERR_UNSUPPORTED before anything is launched. All calls on one GPU share
+ * that array: calls that overlap in time on one GPU (other streams, other
+ * threads) race and must be serialised by the caller. A receiver decodes the
+ * output with rc_decompress on a plan with the same parameters. */
+#define RC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+rc_status_t rc_compress_lowrank_noalloc(rc_shape_t shape, rc_dtype_t dtype, const rc_params_t* params,
+                                        hipStream_t stream, const void* a_t, const rc_state_t* state,
+                                        void* packed_out);
+
 /* Free the plan and its workspace. Waits for nothing: the caller must make sure
  * no launched work still uses the plan. NULL is accepted. */
 rc_status_t rc_plan_destroy(rc_plan_t plan);
