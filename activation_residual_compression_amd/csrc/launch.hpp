@@ -51,10 +51,10 @@ struct LowRankWork {
   int64_t ntiles = 0, rows_pad = 0;
   uint16_t* R = nullptr;     // bf16 residual: 64 x 128 tiles, column chunk, then tensor, then band (per launch)
   float* P = nullptr;        // fp32 panel [batch][rows][rank]
-  uint16_t* Pbt = nullptr;   // bf16 orthonormal panel, transposed [batch][rank][rows_pad]
+  uint16_t* Pbt = nullptr;   // bf16 orthonormal panel, transposed [batch][rank][rows_pad] in 32-row groups
   float* Qt = nullptr;       // fp32 Q^T [batch][rank][cols]
-  uint16_t* Q0t = nullptr;   // bf16 start matrix, transposed [batch][rank][cols]
-  uint16_t* Qtb = nullptr;   // bf16 Q^T for the next product [batch][rank][cols]
+  uint16_t* Q0t = nullptr;   // bf16 start matrix, transposed [batch][rank][cols] in 32-column groups
+  uint16_t* Qtb = nullptr;   // bf16 Q^T for the next product [batch][rank][cols] in 32-column groups
   float* gpart = nullptr;    // per-64-row-tile Gram partials [batch][ntiles][rank][rank]
   float* gsum = nullptr;     // summed Gram matrices [batch][rank][rank]
   float* linv = nullptr;     // inverse Cholesky factor, dead rows zeroed [batch][rank][rank]

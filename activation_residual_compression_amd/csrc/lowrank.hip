@@ -104,6 +104,15 @@ __device__ __forceinline__ int xcd_contiguous(int L, int N) {
   return x * q + min(x, r) + i;
 }
 
+// The bf16 operands of the products -- Q^T (start matrix and later iterations)
+// and P^T -- are [K][cols] matrices stored as 32-column groups: group c/32
+// holds its K rows of 32 consecutive columns contiguously (K x 64 bytes). A
+// step of either product reads one or four whole groups, so its operand loads
+// are contiguous runs instead of K separate 64-byte pieces.
+__device__ __forceinline__ size_t g32(int j, int c, int K) {
+  return ((size_t)(c >> 5) * K + j) * 32 + (c & 31);
+}
+
 // R, the bf16 residual the products share, lives in the library's own
 // workspace in 64 x 128 tiles, each a contiguous 16 KiB row-major block (one
 // step of one band of the R*Q pass; its halves are the 32-row steps of the
@@ -202,7 +211,10 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
           x = S.x[i];
         v.x = bf16_rne(x[0] - S.h[i][0]) | (bf16_rne(x[1] - S.h[i][1]) << 16);
         v.y = bf16_rne(x[2] - S.h[i][2]) | (bf16_rne(x[3] - S.h[i][3]) << 16);
-        if (col_ok && row0 + srow + 2 * i < n) *reinterpret_cast<u32x2*>(R + roff(c0, i)) = v;
+        // non-temporal: R is read again three times, and the later passes read
+        // it half as fast when its lines are still dirty in the caches
+        if (col_ok && row0 + srow + 2 * i < n)
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(R + roff(c0, i)));
       } else {
         v = S.r[i];
       }
@@ -228,7 +240,7 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
     const int kc = c0 + 32 * w < m ? c0 + 32 * w : 0;
 #pragma unroll
     for (int g = 0; g < NT; ++g)
-      B[g] = *reinterpret_cast<const u32x4*>(Qb + (size_t)(16 * g + lr) * m + kc + 8 * lk);
+      B[g] = *reinterpret_cast<const u32x4*>(Qb + g32(16 * g + lr, kc + 8 * lk, K));
   };
   Stage S;
   auto step = [&](int c0, auto prefetch) {
@@ -462,9 +474,9 @@ __global__ __launch_bounds__(256) void lr_solve_kernel(float* __restrict__ P,
     // lane = row of the tile (rows past n are zero in X); wave w writes
     // columns w, w + 4, ...
     const int row = row0 + lane;
-    uint16_t* dst = Pbt + (size_t)b * K * rows_pad + row;
+    uint16_t* dst = Pbt + (size_t)b * K * rows_pad;
 #pragma unroll
-    for (int j = w; j < K; j += 4) dst[(size_t)j * rows_pad] = (uint16_t)bf16_rne(T[lane * LD + j]);
+    for (int j = w; j < K; j += 4) dst[g32(j, row, K)] = (uint16_t)bf16_rne(T[lane * LD + j]);
     __shared__ float cm[4 * K];
     if (lane < K) {
       float mx = 0.f;
@@ -549,7 +561,7 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
     st.r1 = *reinterpret_cast<const u32x4*>(R + r_index(b, row1, col, batch, bands));
     // lanes past the P^T chunk count reread chunk 0 and never store it
     const int t = threadIdx.x < PCH ? threadIdx.x : 0;
-    st.p = *reinterpret_cast<const u32x4*>(Pb + (size_t)(t >> 2) * rows_pad + i0 + 8 * (t & 3));
+    st.p = *reinterpret_cast<const u32x4*>(Pb + g32(t >> 2, i0 + 8 * (t & 3), K));
     return st;
   };
   f32x4 acc[2][NT];
@@ -622,7 +634,7 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
           uint2 hb;
           hb.x = bf16_rne(v.x) | (bf16_rne(v.y) << 16);
           hb.y = bf16_rne(v.z) | (bf16_rne(v.w) << 16);
-          *reinterpret_cast<uint2*>(Qtb + o) = hb;
+          *reinterpret_cast<uint2*>(Qtb + (size_t)b * K * m + g32(16 * g + lr, c, K)) = hb;
         }
       }
     }
@@ -1017,7 +1029,7 @@ __global__ __launch_bounds__(256) void lr_q0_kernel(const float* __restrict__ q0
   if (idx >= (int64_t)batch * cols) return;
   const int b = (int)(idx / cols), c = (int)(idx % cols);
   const uint64_t key = sm64(sm64(sm64(seed, 7), (uint64_t)b), 0);
-  uint16_t* dst = Q0t + (size_t)b * rank * cols + c;
+  uint16_t* dst = Q0t + (size_t)b * rank * cols;
   for (int j = 0; j < rank; ++j) {
     float v = 0.f;
     if (j < kp) {
@@ -1030,7 +1042,7 @@ __global__ __launch_bounds__(256) void lr_q0_kernel(const float* __restrict__ q0
         v = (float)((i & 1) ? rad * sin(ang) : rad * cos(ang));
       }
     }
-    dst[(size_t)j * cols] = (uint16_t)bf16_rne(v);
+    dst[g32(j, c, rank)] = (uint16_t)bf16_rne(v);
   }
 }
 
