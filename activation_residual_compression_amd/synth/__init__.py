@@ -16,6 +16,9 @@ prompts and datasets are not used, the activations are synthetic stand-ins):
 * ``flux``  : 57 bf16 tensors [1152 tokens x 3072 hidden], 28 steps;
   s_c ~ LogNormal(0,1) with 1% outlier channels x20; step change of std 0.1*s_c
   split equally between white noise and a persistent rank-8 drift.
+* ``flux_sched``: the flux shape whose white step change follows a noise
+  schedule, 20x larger at step 1 and decaying with time constant 1.5 steps
+  (NoiseScheduleWorkload).
 * ``video`` : 30 bf16 tensors [4444 tokens x 1920 hidden], 50 steps; share 0 of a
   226-text + 13x30x45-patch token sequence split 4 ways; AR(1) with rho = 0.98
   and Gaussian-blurred (sigma = 2 tokens) spatial noise.
@@ -76,6 +79,7 @@ def _load():
         lib.sg_walk_step.argtypes = [u64, i32, i32, i32, i32, dbl, vp, vp]
         lib.sg_flux_init.argtypes = [u64, i32, i32, i32, i32, dbl, i32, vp, vp, vp, vp]
         lib.sg_flux_step.argtypes = [u64, i32, i32, i32, i32, dbl, i32, vp, vp, vp, vp]
+        lib.sg_flux_step_mix.argtypes = [u64, i32, i32, i32, i32, dbl, dbl, i32, vp, vp, vp, vp]
         lib.sg_video_init.argtypes = [u64, i32, ctypes.POINTER(_VideoGeom), i32, vp, vp]
         lib.sg_video_step.argtypes = [u64, i32, i32, ctypes.POINTER(_VideoGeom), i32, dbl, vp, vp, vp]
         lib.sg_q0.argtypes = [u64, i32, i32, i32, vp]
@@ -240,6 +244,38 @@ class FluxWorkload(Workload):
                              _p(self._sc[i]), _p(self._A[i]), _p(self._B[i]), _p(self._state[i]))
 
 
+class NoiseScheduleWorkload(FluxWorkload):
+    """The FLUX-like share whose step change follows a noise schedule.
+
+    The page "Accelerating Parallel Diffusion Model Serving with Residual
+    Compression" (CompactFusion notes, Limitations) names the steps where the
+    noise level changes sharply, such as the first few, as those where extreme
+    low-rank compression may fail. Here the white (full-rank) part of the step
+    change has std
+        white(t) = sigma / sqrt(2) * (1 + (early_ratio - 1) * exp(-(t - 1) / tau))
+    times s_c, so step 1 moves the activation by about its own size (early_ratio
+    20: 1.4 s_c) and the change decays to the FLUX-like white part within about
+    six steps; the persistent rank-8 drift keeps std sigma / sqrt(2) throughout.
+    Scales, outliers and a_0 are drawn as in FluxWorkload.
+    """
+
+    def __init__(self, name="flux_sched", batch=57, n=1152, m=3072, steps=28,
+                 seed=SEED_BASE + 6, early_ratio=20.0, tau=1.5, **kw):
+        self.early_ratio, self.tau = float(early_ratio), float(tau)
+        super().__init__(name=name, batch=batch, n=n, m=m, steps=steps, seed=seed, **kw)
+
+    def white(self, t: int) -> float:
+        """Std of the white part of the step change at step t >= 1, in units of s_c."""
+        return self.sigma / math.sqrt(2.0) * (1.0 + (self.early_ratio - 1.0) * math.exp(-(t - 1) / self.tau))
+
+    def _step(self, t):
+        lib = _load()
+        for i, b in enumerate(self.tensors):
+            lib.sg_flux_step_mix(self.seed, b, t, self.n, self.m, self.white(t),
+                                 self.sigma / math.sqrt(2.0), self.drift_rank, _p(self._sc[i]),
+                                 _p(self._A[i]), _p(self._B[i]), _p(self._state[i]))
+
+
 class VideoWorkload(Workload):
     def __init__(self, name="video", batch=30, m=1920, steps=50, seed=SEED_BASE + 4, share=0,
                  n_shares=4, n_text=226, frames=13, height=30, width=45, blur_sigma=2.0, rho=0.98,
@@ -320,6 +356,7 @@ def sigma_ratio(a_prev: np.ndarray, a_next: np.ndarray) -> float:
     return float(d.std() / a_prev.astype(np.float64).std())
 
 
-__all__ = ["start_matrices", "Workload", "WalkWorkload", "FluxWorkload", "VideoWorkload", "LatentWorkload", "CONFIGS", "make", "build",
+__all__ = ["start_matrices", "Workload", "WalkWorkload", "FluxWorkload", "NoiseScheduleWorkload",
+           "VideoWorkload", "LatentWorkload", "CONFIGS", "make", "build",
            "normal", "uniform", "key", "to_bf16_bits", "bf16_bits_to_f32", "SEED_BASE",
            "sigma_ratio"]

@@ -201,6 +201,31 @@ void sg_flux_step(uint64_t seed, int tensor, int t, int n, int m, double sigma, 
   }
 }
 
+/* The FLUX-like step with the white and drift parts scaled separately:      */
+/*   a += (amp_white z + amp_drift (A B^T)[i][j] / sqrt(r)) s_c               */
+/* (the noise-schedule workload varies amp_white from step to step).         */
+void sg_flux_step_mix(uint64_t seed, int tensor, int t, int n, int m, double amp_white,
+                      double amp_drift, int rank_drift, const float* sc, const float* A,
+                      const float* B, float* a) {
+  const uint64_t k = sg_key(seed, ROLE_STEP, tensor, t);
+  const double inv_sqrt_r = 1.0 / sqrt((double)rank_drift);
+  const int64_t N = (int64_t)n * m;
+#pragma omp parallel for schedule(static)
+  for (int64_t p = 0; p < (N + 1) / 2; ++p) {
+    double z[2];
+    sm_normal_pair(k, p, &z[0], &z[1]);
+    for (int q = 0; q < 2; ++q) {
+      const int64_t idx = 2 * p + q;
+      if (idx >= N) break;
+      const int64_t i = idx / m, j = idx % m;
+      double d = 0.0;
+      for (int r = 0; r < rank_drift; ++r) d += (double)A[i * rank_drift + r] * (double)B[j * rank_drift + r];
+      d *= inv_sqrt_r;
+      a[idx] = (float)((double)a[idx] + (amp_white * z[q] + amp_drift * d) * (double)sc[j]);
+    }
+  }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Video-like share (CogVideoX-2b-shaped): the token sequence is n_text text */
 /* tokens followed by frames x height x width patch tokens; share s of       */

@@ -529,6 +529,32 @@ def compress_values(scheme, x, *, group=None, rank=None, iters=None, q0=None, fa
     raise ValueError(scheme)
 
 
+def run_schedule(frames, kinds):
+    """Closed-loop sequence of one tensor with a scheme chosen per step.
+
+    CompactFusion notes, Limitations: step 0 has no history and is sent in full,
+    and the steps where the noise level changes sharply (the first few) may be
+    sent in full or with a finer scheme before the cheap one takes over.
+    kinds[t] is None for a step sent in full (both copies become a_t, the
+    carried residual is dropped) or (scheme, params) for a compressed step of
+    the closed loop (Overall framework / Error feedback), params as for
+    compress_tensor. kinds[0] must be None. Returns ahat_t for every step.
+    """
+    if kinds[0] is not None:
+        raise ValueError("step 0 is sent in full")
+    out = []
+    ahat = None
+    for a, kind in zip(frames, kinds):
+        a = _f32(a)
+        if kind is None:
+            ahat = a.copy()
+        else:
+            scheme, params = kind
+            ahat = compress_tensor(scheme, a, ahat, **params)["ahat"]
+        out.append(ahat.copy())
+    return out
+
+
 def run_trajectory(mode, scheme, frames, **kw):
     """Free-running sequence of one tensor through the scheme.
 
