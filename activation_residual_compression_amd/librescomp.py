@@ -18,7 +18,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "lib", "librescomp.so")
+# LIBRESCOMP_LIB names another build of the library (the CPU sanitizer build
+# of the host code); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("LIBRESCOMP_LIB") or os.path.join(_HERE, "lib", "librescomp.so")
 
 RC_OK, RC_ERR_INVALID_ARG, RC_ERR_UNSUPPORTED, RC_ERR_ALIGNMENT, RC_ERR_HIP = 0, 1, 2, 3, 4
 RC_ERR_NUMERIC, RC_ERR_NONFINITE = 5, 6

@@ -51,7 +51,17 @@ extern "C" {
 
 typedef struct rc_plan* rc_plan_t; /* opaque; created and owned by the library */
 
-typedef enum {
+/* The enumerations are int-sized in C and C++ alike. In C++ they are given int
+ * as their fixed underlying type, so that any int a C caller passes for one
+ * (an invalid value included, which the library rejects) is a value of the
+ * type on the C++ side too. */
+#ifdef __cplusplus
+#define RC_ENUM enum : int
+#else
+#define RC_ENUM enum
+#endif
+
+typedef RC_ENUM {
   RC_OK = 0,
   RC_ERR_INVALID_ARG = 1, /* null pointer, bad shape, bad parameter value */
   RC_ERR_UNSUPPORTED = 2, /* valid request this library does not implement */
@@ -61,9 +71,9 @@ typedef enum {
   RC_ERR_NONFINITE = 6,   /* RC_CHECK_FINITE: NaN or Inf in the input */
 } rc_status_t;
 
-typedef enum { RC_BF16 = 0, RC_F32 = 1 } rc_dtype_t; /* dtype of a_t */
+typedef RC_ENUM { RC_BF16 = 0, RC_F32 = 1 } rc_dtype_t; /* dtype of a_t */
 
-typedef enum {
+typedef RC_ENUM {
   RC_Q1 = 0,      /* 1-bit signs + per-group fp32 mean|r|                 */
   RC_Q2 = 1,      /* 2-bit uniform levels + per-group fp32 (min, step)   */
   RC_NM = 2,      /* keep 2 of every 16, bf16 values + 4-bit indices     */
@@ -277,7 +287,8 @@ size_t rc_tensor_packed_bytes(rc_plan_t plan);
  * 4-byte counter not counted here). */
 size_t rc_workspace_bytes(rc_plan_t plan);
 
-/* Static description of a status code. */
+/* Static description of a status code ("unknown rc_status_t" for a value that
+ * is none). */
 const char* rc_status_string(rc_status_t status);
 
 #ifdef __cplusplus

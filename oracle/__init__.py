@@ -35,12 +35,20 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math"]
 
 
-def build(force: bool = True) -> str:
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+# AddressSanitizer + UndefinedBehaviorSanitizer build (a CPU check of the C
+# code; the library is then loaded with the sanitizer runtimes preloaded and
+# ORACLE_LIB naming it).
+SAN_CFLAGS = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+              "-fno-sanitize-recover=all"]
+
+
+def build(force: bool = True, sanitize: bool = False, out: str = None) -> str:
+    out = out or _LIB
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, *(SAN_CFLAGS if sanitize else []), _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, out)
+    return out
 
 
 _lib = None
@@ -49,9 +57,10 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        path = os.environ.get("ORACLE_LIB") or _LIB
+        if path == _LIB and not os.path.exists(_LIB):
             build(force=False)
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(path)
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
         lib.orc_bf16_bits.restype = ctypes.c_uint16
         lib.orc_bf16_bits.argtypes = [ctypes.c_float]
