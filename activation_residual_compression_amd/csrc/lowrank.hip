@@ -494,14 +494,20 @@ __global__ __launch_bounds__(256) void lr_solve_kernel(float* __restrict__ P,
 }
 
 // ---------------------------------------------------------------- Q = R^T P
-// Block: 128 columns of one tensor over all of its rows; wave w owns columns
-// 32w .. 32w+31 (two 16-column MFMA tiles). Per step of 32 rows the R tile
-// [32 x 128] and the matching P^T chunk [K x 32] are staged through LDS
-// (double buffered, one barrier per step). R is read back transposed with
-// ds_read_b64_tr_b16 (A[c][i] = R[i][c]); each P^T fragment read from LDS
-// feeds both column tiles of the wave. A last block of 64 columns (cols % 128
-// == 64) computes its missing half from reread valid columns and stores only
-// the valid ones.
+// Block: 128 columns of one tensor over all of its rows, in two halves of 4
+// waves: half h walks rows [h * rows_pad/2, (h+1) * rows_pad/2), and at the end
+// half 1's sums are added to half 0's through LDS (one fixed order). Within a
+// half, wave w owns columns 32w .. 32w+31 (two 16-column MFMA tiles). Per step
+// of 32 rows the R tile [32 x 128] and the matching P^T chunk [K x 32] are
+// staged through LDS (double buffered per half, one barrier per step). R is
+// read back transposed with ds_read_b64_tr_b16 (A[c][i] = R[i][c]); each P^T
+// fragment read from LDS feeds both column tiles of the wave. A last block of
+// 64 columns (cols % 128 == 64) computes its missing half from reread valid
+// columns and stores only the valid ones.
+// The two halves matter where the grid is small: the video-like share has 15
+// column blocks per tensor and 30 tensors, 450 blocks on 256 CUs, and twice
+// the waves per block run it 5 % faster (the flux-like grid, 1368 blocks, is
+// unchanged).
 // The block writes its columns of Q^T itself. Before the last iteration Q is
 // needed only as the bf16 operand of the next product (Qtb); after it, only as
 // V: Qt in fp32 and the column absmax of V folded into amax[b][1][j] (FINAL).
@@ -511,9 +517,10 @@ __global__ __launch_bounds__(256) void lr_solve_kernel(float* __restrict__ P,
 constexpr int kRtpCols = 128;
 constexpr int kRtpLd = kRtpCols + 8;  // bf16 per staged R row (272 B)
 constexpr int kRtpPld = 32 + 8;       // bf16 per staged P^T row (80 B)
+constexpr int kRtpHalves = 2;         // row halves per block, 256 threads each
 
 template <int K, bool FINAL>
-__global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict__ R,
+__global__ __launch_bounds__(256 * kRtpHalves) void lr_rtp_kernel(const uint16_t* __restrict__ R,
                                                      const uint16_t* __restrict__ Pbt,
                                                      float* __restrict__ Qt,
                                                      uint16_t* __restrict__ Qtb,
@@ -521,8 +528,11 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
                                                      int rows_pad) {
   constexpr int NT = K / 16;
   constexpr int PCH = K * 4;  // 16-byte chunks of a [K x 32] bf16 P^T block
-  __shared__ __attribute__((aligned(16))) uint16_t sR[2][32 * kRtpLd];
-  __shared__ __attribute__((aligned(16))) uint16_t sP[2][K * kRtpPld];
+  __shared__ __attribute__((aligned(16))) uint16_t sRh[kRtpHalves][2][32 * kRtpLd];
+  __shared__ __attribute__((aligned(16))) uint16_t sPh[kRtpHalves][2][K * kRtpPld];
+  const int tid = threadIdx.x & 255, half = threadIdx.x >> 8;
+  auto sR = sRh[half];
+  auto sP = sPh[half];
   // Logical blocks (column block fastest, then tensor) are spread over the
   // XCDs in contiguous ranges, so the column blocks that share a P^T chunk
   // share an L2. Tensors are taken in the reverse of that order: every XCD's
@@ -534,12 +544,15 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
   const int cb = lin % gridDim.x;
   const int b = gridDim.y - 1 - lin / gridDim.x;
   const int c0 = cb * kRtpCols;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
+  const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lk = lane >> 4;
   // R staging: each wave-wide load covers 4 whole 256-byte row pieces (16 lanes
   // x 16 bytes per row); loads q = 0, 1 take rows ld_row and ld_row + 16
-  const int ld_row = threadIdx.x >> 4, ld_col = (threadIdx.x & 15) * 8;
+  const int ld_row = tid >> 4, ld_col = (tid & 15) * 8;
   const bool col_ok = c0 + ld_col < m;
-  const int i_end = rows_pad;
+  // this half's rows (rows_pad is a multiple of 64, so both halves hold the
+  // same whole number of 32-row steps and meet every barrier together)
+  const int i_begin = half * (rows_pad / kRtpHalves);
+  const int i_end = i_begin + rows_pad / kRtpHalves;
   const int batch = gridDim.y, bands = rows_pad >> 6;
   const uint16_t* Pb = Pbt + (size_t)b * K * rows_pad;
   const int tr_off = (8 * lk + (lr >> 2)) * kRtpLd + 32 * w + 4 * (lr & 3);
@@ -560,7 +573,7 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
     st.r0 = *reinterpret_cast<const u32x4*>(R + r_index(b, row0, col, batch, bands));
     st.r1 = *reinterpret_cast<const u32x4*>(R + r_index(b, row1, col, batch, bands));
     // lanes past the P^T chunk count reread chunk 0 and never store it
-    const int t = threadIdx.x < PCH ? threadIdx.x : 0;
+    const int t = tid < PCH ? tid : 0;
     st.p = *reinterpret_cast<const u32x4*>(Pb + g32(t >> 2, i0 + 8 * (t & 3), K));
     return st;
   };
@@ -573,8 +586,8 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
   auto put = [&](const Stage& st, int buf) {
     *reinterpret_cast<u32x4*>(&sR[buf][ld_row * kRtpLd + ld_col]) = st.r0;
     *reinterpret_cast<u32x4*>(&sR[buf][(ld_row + 16) * kRtpLd + ld_col]) = st.r1;
-    if (threadIdx.x < PCH)
-      *reinterpret_cast<u32x4*>(&sP[buf][(threadIdx.x >> 2) * kRtpPld + 8 * (threadIdx.x & 3)]) = st.p;
+    if (tid < PCH)
+      *reinterpret_cast<u32x4*>(&sP[buf][(tid >> 2) * kRtpPld + 8 * (tid & 3)]) = st.p;
   };
   auto compute = [&](int buf) {
     u32x4 A[2];
@@ -598,8 +611,8 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
 
   // LDS double buffer, one barrier per step: a buffer is refilled two steps
   // after it was read, and every wave has passed the barrier in between.
-  Stage s0 = gload(0), s1 = gload(32);
-  int i0 = 0;
+  Stage s0 = gload(i_begin), s1 = gload(i_begin + 32);
+  int i0 = i_begin;
   for (; i0 + 32 < i_end; i0 += 64) {
     put(s0, 0);
     __syncthreads();
@@ -615,14 +628,33 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
     __syncthreads();
     compute(0);
   }
-  // D[c][j]: lane holds c = c0 + 32w + 16ct + 4lk + t, j = 16g + lr
+  // half 1's sums into half 0's (the staging buffers are free after the barrier)
+  static_assert(2 * (K / 16) * 256 * 16 <= sizeof(sRh), "R staging too small for the half sums");
+  __syncthreads();
+  f32x4* hsum = reinterpret_cast<f32x4*>(&sRh[0][0][0]);
+  if (half == 1)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int g = 0; g < NT; ++g) hsum[(ct * NT + g) * 256 + tid] = acc[ct][g];
+  __syncthreads();
+  if (half == 0)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int g = 0; g < NT; ++g) {
+        const f32x4 o = hsum[(ct * NT + g) * 256 + tid];
+        acc[ct][g] = f32x4{acc[ct][g].x + o.x, acc[ct][g].y + o.y, acc[ct][g].z + o.z,
+                           acc[ct][g].w + o.w};
+      }
+  // D[c][j]: lane holds c = c0 + 32w + 16ct + 4lk + t, j = 16g + lr (half 0 stores)
   float mx[NT];
 #pragma unroll
   for (int g = 0; g < NT; ++g) mx[g] = 0.f;
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int c = c0 + 32 * w + 16 * ct + 4 * lk;
-    if (c < m) {
+    if (c < m && half == 0) {
 #pragma unroll
       for (int g = 0; g < NT; ++g) {
         const f32x4 v = acc[ct][g];
@@ -646,7 +678,7 @@ __global__ __launch_bounds__(256) void lr_rtp_kernel(const uint16_t* __restrict_
     for (int g = 0; g < NT; ++g) {
       mx[g] = fmaxf(mx[g], __shfl_xor(mx[g], 16));
       mx[g] = fmaxf(mx[g], __shfl_xor(mx[g], 32));
-      if (lk == 0) cm[w * K + 16 * g + lr] = mx[g];
+      if (lk == 0 && half == 0) cm[w * K + 16 * g + lr] = mx[g];
     }
     __syncthreads();
     const int j = threadIdx.x;
@@ -1096,10 +1128,10 @@ hipError_t lr_compress_k(bool bf16, const void* a, float* ahat, float* e, uint8_
     cqr_pass<K, KP>(w, n, B, true, s);
     const dim3 rtp_grid((m + kRtpCols - 1) / kRtpCols, B);
     if (it + 1 == w.iters)
-      hipLaunchKernelGGL((lr_rtp_kernel<K, true>), rtp_grid, dim3(256), 0, s, w.R, w.Pbt, w.Qt,
+      hipLaunchKernelGGL((lr_rtp_kernel<K, true>), rtp_grid, dim3(256 * kRtpHalves), 0, s, w.R, w.Pbt, w.Qt,
                          w.Qtb, w.amax, n, m, rp);
     else
-      hipLaunchKernelGGL((lr_rtp_kernel<K, false>), rtp_grid, dim3(256), 0, s, w.R, w.Pbt, w.Qt,
+      hipLaunchKernelGGL((lr_rtp_kernel<K, false>), rtp_grid, dim3(256 * kRtpHalves), 0, s, w.R, w.Pbt, w.Qt,
                          w.Qtb, w.amax, n, m, rp);
   }
   if (w.bf16_factors)
