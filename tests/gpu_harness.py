@@ -34,7 +34,7 @@ def lib_view_f32(a_np, dtype):
     return np.asarray(a_np, np.float32)
 
 
-class GpuRun:
+class DeviceRun:
     """Sender state (ahat, e), receiver state (recon) and one plan on cuda:0."""
 
     def __init__(self, shape, dtype, scheme, **params):
@@ -112,5 +112,5 @@ def relF(a, ahat):
     return float(np.linalg.norm(a64 - np.asarray(ahat, np.float64)) / np.linalg.norm(a64))
 
 
-__all__ = ["GpuRun", "check_exact_step", "relF", "bits", "max_rel", "lib_view_f32", "say", "synth",
+__all__ = ["DeviceRun", "check_exact_step", "relF", "bits", "max_rel", "lib_view_f32", "say", "synth",
            "oracle", "rc", "DEV"]

@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_harness import GpuRun, bits, lib_view_f32, oracle, relF, say, synth, to_device
+from gpu_harness import DeviceRun, bits, lib_view_f32, oracle, relF, say, synth, to_device
 from activation_residual_compression_amd import librescomp as rc
 
 pytestmark = pytest.mark.gpu
@@ -51,7 +51,7 @@ def _decode_bound_check(run, b, packed, a_f, ahat_prev, e, ahat, rank, factors="
 def _run_lr(wl, rank, iters, check, steps=None, code_agree=0.8, factors="int4"):
     q0 = wl.q0(rank)
     flags = rc.RC_LR_BF16_FACTORS if factors == "bf16" else 0
-    run = GpuRun((wl.nb, wl.n, wl.m), wl.dtype, "lr", rank=rank, iters=iters, q0=q0, flags=flags)
+    run = DeviceRun((wl.nb, wl.n, wl.m), wl.dtype, "lr", rank=rank, iters=iters, q0=q0, flags=flags)
     assert run.plan.tensor_packed_bytes == oracle.tensor_bytes("lr", wl.n, wl.m, rank=rank,
                                                                factors=factors)
     try:
@@ -152,7 +152,7 @@ def test_lr_zero_and_rank_deficient_residuals():
     exact = (a[1].astype(np.float64) - ahat[1]) == ((A @ B.T) * 0.25)
     assert exact.all()
     q0 = rng.standard_normal((2, m, k)).astype(np.float32)
-    run = GpuRun((2, n, m), "f32", "lr", rank=k, iters=2, q0=q0)
+    run = DeviceRun((2, n, m), "f32", "lr", rank=k, iters=2, q0=q0)
     try:
         run.set_state(ahat)
         say("[gpu] lr degenerate")
@@ -180,7 +180,7 @@ def test_lr_free_running_trajectory_matches_oracle():
     frames = []
     for _ in range(6):
         frames.append(wl.next()[1])
-    run = GpuRun((1, 96, 256), "bf16", "lr", rank=16, iters=2, q0=q0)
+    run = DeviceRun((1, 96, 256), "bf16", "lr", rank=16, iters=2, q0=q0)
     try:
         run.warmup(frames[0])
         ahat_o = lib_view_f32(frames[0], "bf16")[0].copy()
@@ -228,7 +228,7 @@ def test_lr_free_running_flux_shape_half_sequence():
     wl = synth.FluxWorkload(batch=2, n=1152, m=3072, steps=steps + 1)
     q0 = wl.q0(32)
     frames = [wl.next()[1] for _ in range(steps + 1)]
-    run = GpuRun((2, 1152, 3072), "bf16", "lr", rank=32, iters=2, q0=q0)
+    run = DeviceRun((2, 1152, 3072), "bf16", "lr", rank=32, iters=2, q0=q0)
     eps_g, eps_o = [], []
     try:
         run.warmup(frames[0])

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_harness import GpuRun, check_exact_step, lib_view_f32, oracle, say, synth
+from gpu_harness import DeviceRun, check_exact_step, lib_view_f32, oracle, say, synth
 
 pytestmark = pytest.mark.gpu
 
@@ -24,7 +24,7 @@ def _kw(scheme, group):
 
 def _run_sequence(wl, scheme, group, tensors_checked=None, steps=None):
     plan_kw, orc_kw = _kw(scheme, group)
-    run = GpuRun((wl.nb, wl.n, wl.m), wl.dtype, scheme, **plan_kw)
+    run = DeviceRun((wl.nb, wl.n, wl.m), wl.dtype, scheme, **plan_kw)
     try:
         _, a0 = wl.next()
         run.warmup(a0)
@@ -102,7 +102,7 @@ def test_crafted_edge_cases(scheme, group):
     n, m = 6, 256
     a, ahat = _crafted(n, m, seed=3)
     plan_kw, orc_kw = _kw(scheme, group)
-    run = GpuRun((1, n, m), "f32", scheme, **plan_kw)
+    run = DeviceRun((1, n, m), "f32", scheme, **plan_kw)
     try:
         run.set_state(ahat[None])
         say("[gpu] crafted %s" % scheme)
@@ -150,7 +150,7 @@ def test_q1_summation_order_sensitive_groups(group):
                     for row in a.reshape(-1, group)], np.float32)
     _, want = oracle.q1_encode(a.reshape(-1), group)
     assert np.all(seq.view(np.uint32) != want.view(np.uint32))
-    run = GpuRun((1, n, m), "f32", "q1", group=group)
+    run = DeviceRun((1, n, m), "f32", "q1", group=group)
     try:
         run.set_state(ahat[None])
         say("[gpu] q1 order-sensitive groups, group %d" % group)
@@ -174,7 +174,7 @@ def test_q1_wide_magnitude_spans_exact_path(group):
     a[rng.random((n, m)) < 0.05] = 0.0
     a[::3] = rng.standard_normal((len(a[::3]), m)).astype(np.float32)   # fast-path rows between
     ahat = np.zeros((n, m), np.float32)
-    run = GpuRun((1, n, m), "f32", "q1", group=group)
+    run = DeviceRun((1, n, m), "f32", "q1", group=group)
     try:
         run.set_state(ahat[None])
         say("[gpu] q1 wide spans, group %d" % group)
@@ -190,7 +190,7 @@ def test_zero_residual_everywhere(scheme, group):
     wl = synth.FluxWorkload(batch=2, n=33, m=256, steps=1)
     _, a0 = wl.next()
     plan_kw, orc_kw = _kw(scheme, group)
-    run = GpuRun((2, 33, 256), "bf16", scheme, **plan_kw)
+    run = DeviceRun((2, 33, 256), "bf16", scheme, **plan_kw)
     try:
         run.warmup(a0)
         run.step(a0)   # a_t == ahat: r = 0
