@@ -511,6 +511,14 @@ int rcx_lowrank_workspace(rc_plan_t pl, void** ptrs, int count) {
   return (int)w.rows_pad;
 }
 
+int rcx_lowrank_r_probe(rc_plan_t pl, int pattern, hipStream_t stream) {
+  if (!pl || pl->scheme != RC_LOWRANK) return -1;
+  const rc::LowRankWork& w = pl->lr;
+  // the sink is a piece of the workspace the probes never write (never = 0)
+  return (int)rc::launch_r_probe(pattern, w.R, (int)pl->shape.rows, (int)pl->shape.cols, (int)pl->shape.batch,
+                                 (int)w.ntiles, (int)w.rows_pad, reinterpret_cast<uint32_t*>(w.gsum), stream);
+}
+
 int rcx_device_to_host(void* dst, const void* src, size_t bytes) {
   if (!dst || !src) return (int)hipErrorInvalidValue;
   return (int)hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost);

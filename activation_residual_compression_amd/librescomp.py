@@ -91,6 +91,8 @@ def _load():
     lib.rc_status_string.restype = ctypes.c_char_p
     lib.rc_status_string.argtypes = [ctypes.c_int]
     lib.rcx_lowrank_workspace.restype = ctypes.c_int
+    lib.rcx_lowrank_r_probe.restype = ctypes.c_int
+    lib.rcx_lowrank_r_probe.argtypes = [vp, ctypes.c_int, vp]
     lib.rcx_lowrank_workspace.argtypes = [vp, ctypes.POINTER(vp), ctypes.c_int]
     lib.rcx_device_to_host.restype = ctypes.c_int
     lib.rcx_device_to_host.argtypes = [vp, vp, sz]
@@ -242,6 +244,7 @@ def make_params(scheme, *, group=0, nm_keep=0, nm_block=0, rank=0, iters=0, seed
 
 
 RCX_PROBE_COPY, RCX_PROBE_READ, RCX_PROBE_WRITE, RCX_PROBE_SENDER_MIX, RCX_PROBE_RECEIVER_RMW = range(5)
+RCX_R_PROBE_RQ, RCX_R_PROBE_RTP = 0, 1
 
 
 def rcx_device_to_host(src, nbytes):
@@ -333,6 +336,13 @@ class Plan:
 
     def reset_state(self, stream=None):
         rc_plan_reset_state(self.handle, stream)
+
+    def r_probe(self, pattern, stream=None):
+        """Read this low-rank plan's R in the pattern of its R*Q (RCX_R_PROBE_RQ)
+        or R^T*P (RCX_R_PROBE_RTP) pass and nothing else (librescomp_diag.h)."""
+        err = _lib.rcx_lowrank_r_probe(self.handle, int(pattern), _stream(stream))
+        if err != 0:
+            raise RuntimeError("rcx_lowrank_r_probe: %d" % err)
 
     def lowrank_workspace(self):
         """Device pointers (R, P, Pbt, Qt, Q0t, Qtb, gsum, linv) and rows_pad (diagnostics)."""

@@ -153,6 +153,21 @@ def _probe_on(kind, a, b, c, n, reps=5):
     return e0.elapsed_time(e1) / reps
 
 
+def _r_probe_on(plan, pattern, reps=5):
+    """ms per read of a low-rank plan's R in one product's pattern (after two
+    untimed reads, so R's lines are clean, as for the later passes)."""
+    import torch
+    for _ in range(2):
+        plan.r_probe(pattern)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        plan.r_probe(pattern)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def exchange_timing(plan, seq, ahat, e, packed, chunks, reps=7):
     """Sender step plus hand-off of the packed stream (rc_compress_send): compress
     alone, copy alone, both in sequence, and the chunked pipeline, to a device
@@ -350,6 +365,12 @@ def measure(config, steps, warmup, max_frames, log, exchange_chunks=(), overlap=
         from activation_residual_compression_amd import librescomp as rc
         out["ref_sender_mix_GBps"] = 14.0 * N / (_probe_on(rc.RCX_PROBE_SENDER_MIX, seq[0], ahat, e, N) * 1e6)
         out["ref_receiver_rmw_GBps"] = 8.0 * N / (_probe_on(rc.RCX_PROBE_RECEIVER_RMW, None, recon, None, N) * 1e6)
+    if spec["scheme"] == "lr":
+        # the passes that read R alone: R's bytes in each product's pattern
+        from activation_residual_compression_amd import librescomp as rc
+        out["ref_r_read_GBps"] = {
+            "rq_pattern": 2.0 * N / (_r_probe_on(plan, rc.RCX_R_PROBE_RQ) * 1e6),
+            "rtp_pattern": 2.0 * N / (_r_probe_on(plan, rc.RCX_R_PROBE_RTP) * 1e6)}
     plan.close()
     del frames, seq, ahat, recon, e, packed
     torch.cuda.empty_cache()
@@ -634,15 +655,25 @@ def main():
             # algorithmic bytes per element x elements / average duration
             B, n, m = res["shape"]
             k = int(ks[0][0].split(",")[-1].strip(" >"))
-            passes = {"first_product": ("lr_rq_kernel<unsigned short, true, %d>" % k, 8),
-                      "reconstruct_sender": ("lr_recon_kernel<unsigned short, true, %d, %d, false," % (k, k), 14),
-                      "reconstruct_receiver": ("lr_recon_kernel<float, false, %d, %d, false," % (k, k), 8)}
-            frac = {}
-            for name, (prefix, bpe) in passes.items():
+            passes = {"first_product": ("lr_rq_kernel<unsigned short, true, %d>" % k, 8, None),
+                      "reconstruct_sender": ("lr_recon_kernel<unsigned short, true, %d, %d, false," % (k, k), 14,
+                                             None),
+                      "reconstruct_receiver": ("lr_recon_kernel<float, false, %d, %d, false," % (k, k), 8, None),
+                      "r_only_rq": ("lr_rq_kernel<unsigned short, false, %d>" % k, 2, "rq_pattern"),
+                      "r_only_rtp_first": ("lr_rtp_kernel<%d, false>" % k, 2, "rtp_pattern"),
+                      "r_only_rtp_last": ("lr_rtp_kernel<%d, true>" % k, 2, "rtp_pattern")}
+            frac, of_probe = {}, {}
+            ref = res.get("ref_r_read_GBps") or {}
+            for name, (prefix, bpe, pat) in passes.items():
                 hits = [v for kn, v in trace["kernels"].items() if kn.startswith(prefix)]
                 if len(hits) == 1:
-                    frac[name] = bpe * B * n * m / (hits[0]["avg_us"] * 1e3) / HBM_PEAK_GBS
+                    gbs = bpe * B * n * m / (hits[0]["avg_us"] * 1e3)
+                    frac[name] = gbs / HBM_PEAK_GBS
+                    if pat in ref:
+                        of_probe[name] = gbs / ref[pat]
             res["streaming_pass_hbm_frac"] = frac
+            if of_probe:
+                res["r_only_pass_frac_of_r_probe"] = of_probe
     roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
             "kernel": kname or ((prefix + " ...>") if prefix else "sender kernel (rc_compress)"),

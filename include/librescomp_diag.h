@@ -45,6 +45,17 @@ int rcx_hbm_probe(int kind, const void* a, void* b, void* c, int64_t n, hipStrea
  * contiguously. */
 int rcx_lowrank_workspace(rc_plan_t plan, void** ptrs, int count);
 
+/* Reads the R workspace of a low-rank plan (bf16, batch x rows x cols) in the
+ * access pattern of one of its products, with that product's grid, and does
+ * nothing else: the measured ceiling of the passes that read R alone.
+ *   RCX_R_PROBE_RQ   the R*Q pass (64-row bands walking 128-column chunks)
+ *   RCX_R_PROBE_RTP  the R^T*P pass (128-column blocks walking 32-row steps)
+ * Reads batch * rows * cols * 2 bytes; writes nothing. Launches asynchronously
+ * on `stream`. Returns a hipError_t value, or -1 for a NULL plan or another
+ * scheme. */
+enum { RCX_R_PROBE_RQ = 0, RCX_R_PROBE_RTP = 1 };
+int rcx_lowrank_r_probe(rc_plan_t plan, int pattern, hipStream_t stream);
+
 /* Synchronous copy of `bytes` bytes from device address src to host memory dst
  * (for reading the workspace pieces above). Returns a hipError_t value. */
 int rcx_device_to_host(void* dst, const void* src, size_t bytes);

@@ -397,3 +397,26 @@ def test_check_finite_rejects_nan_before_launching(scheme, kw):
         with pytest.raises(rc.RcError) as ei:
             p.compress(a, inf_state, e, pk)
         assert ei.value.status == rc.RC_ERR_NONFINITE
+
+
+def test_r_probe_reads_r_and_writes_nothing():
+    """The R-pattern reference reads (diagnostics) leave the workspace as it was."""
+    wl = synth.FluxWorkload(batch=2, n=100, m=192, steps=2)
+    run = DeviceRun((2, 100, 192), "bf16", "lr", rank=16, iters=2, q0=wl.q0(16))
+    try:
+        _, a0 = wl.next()
+        _, a1 = wl.next()
+        run.warmup(a0)
+        run.step(a1)
+        ptrs, rows_pad = run.plan.lowrank_workspace()
+        r_bytes = 2 * rows_pad * 256 * 2          # R: batch x rows_pad x (cols padded to 128) bf16
+        before = rc.rcx_device_to_host(ptrs[0], r_bytes), rc.rcx_device_to_host(ptrs[6], 4 * 16 * 16 * 2)
+        for pattern in (rc.RCX_R_PROBE_RQ, rc.RCX_R_PROBE_RTP):
+            run.plan.r_probe(pattern)
+        torch.cuda.synchronize()
+        after = rc.rcx_device_to_host(ptrs[0], r_bytes), rc.rcx_device_to_host(ptrs[6], 4 * 16 * 16 * 2)
+        assert np.array_equal(before[0], after[0]) and np.array_equal(before[1], after[1])
+        with pytest.raises(RuntimeError):
+            run.plan.r_probe(7)
+    finally:
+        run.close()
