@@ -30,8 +30,8 @@
  *     and block-selection schemes keep per-plan device workspace and state).
  *     Separate plans share nothing and may run concurrently on separate streams.
  *   - A rejected request (RC_ERR_INVALID_ARG, RC_ERR_UNSUPPORTED,
- *     RC_ERR_ALIGNMENT, RC_ERR_NONFINITE) launches nothing and touches no
- *     buffer. RC_ERR_HIP reports a failed HIP call or kernel launch; the
+ *     RC_ERR_ALIGNMENT, RC_ERR_NONFINITE) writes no buffer and launches
+ *     nothing (RC_ERR_NONFINITE: nothing but the input scan that found it). RC_ERR_HIP reports a failed HIP call or kernel launch; the
  *     outputs of that call are then unspecified. RC_ERR_NUMERIC is a report
  *     after a completed call (see RC_LR_CHECK_NUMERIC).
  *   - Inputs holding NaN or Inf give unspecified (but memory-safe) results,
