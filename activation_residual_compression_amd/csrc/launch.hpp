@@ -62,13 +62,14 @@ struct LowRankWork {
   uint32_t* dead = nullptr;  // optional: count of dead Cholesky pivots (sent columns)
 };
 
-// Start matrices: Q0t bf16 [batch][rank][cols] (rows kp .. rank-1 zero) from a
-// device fp32 q0 [batch][cols][kp], or, when q0 is null, drawn from `seed`
-// (SplitMix64 + Box-Muller, as the public header defines).
 // Reads of a low-rank plan's R in the pattern of its R*Q pass (0) or R^T*P
 // pass (1), nothing else (diagnostics; sink is never written).
 hipError_t launch_r_probe(int pattern, const uint16_t* R, int n, int m, int batch, int ntiles, int rows_pad,
                           uint32_t* sink, hipStream_t s);
+
+// Start matrices: Q0t bf16 [batch][rank][cols] (rows kp .. rank-1 zero) from a
+// device fp32 q0 [batch][cols][kp], or, when q0 is null, drawn from `seed`
+// (SplitMix64 + Box-Muller, as the public header defines).
 hipError_t launch_lr_q0(const float* q0, uint64_t seed, uint16_t* Q0t, int batch, int cols, int kp,
                         int rank, hipStream_t s);
 
