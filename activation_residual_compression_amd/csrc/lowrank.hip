@@ -539,8 +539,15 @@ __global__ __launch_bounds__(256 * kRtpHalves) void lr_rtp_kernel(const uint16_t
     // columns past m reread column c0; output row c of the product depends on
     // column c of R alone, and rows past m are never stored
     const int col = c0 + (col_ok ? ld_col : 0);
-    st.r0 = *reinterpret_cast<const u32x4*>(R + r_index(b, row0, col, batch, bands));
-    st.r1 = *reinterpret_cast<const u32x4*>(R + r_index(b, row1, col, batch, bands));
+    // R is read non-temporally here and with ordinary loads in R*Q. An R*Q
+    // pass leaves the part of R it read last in the device's last-level
+    // cache, where the R^T*P pass after it still finds it, and non-temporal
+    // reads keep this pass from displacing other cached data: the three passes
+    // that read R alone took 242 / 311 us together this way against 254 / 333
+    // us with ordinary loads in all of them (flux / video, one stream). The
+    // cache policy changes no value.
+    st.r0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(R + r_index(b, row0, col, batch, bands)));
+    st.r1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(R + r_index(b, row1, col, batch, bands)));
     // lanes past the P^T chunk count reread chunk 0 and never store it
     const int t = tid < PCH ? tid : 0;
     st.p = *reinterpret_cast<const u32x4*>(Pb + g32(t >> 2, i0 + 8 * (t & 3), K));
