@@ -71,12 +71,19 @@ __device__ __forceinline__ void tile_gram(const float* T, float* out, int nwaves
   for (int ta = 0; ta < NT; ++ta)
     for (int tb = ta; tb < NT; ++tb, ++pair) {
       if (pair % nwaves != w) continue;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      // every operand is read from LDS before the first MFMA, so the chain of
+      // 16 MFMAs waits for the reads once instead of after each pair of them
+      float va[kTile / 4], vb[kTile / 4];
 #pragma unroll
       for (int s = 0; s < kTile / 4; ++s) {
         const float* row = T + (4 * s + lk) * LD;
-        acc = mfma_f32(row[16 * ta + lr], row[16 * tb + lr], acc);
+        va[s] = row[16 * ta + lr];
+        vb[s] = row[16 * tb + lr];
       }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < kTile / 4; ++s) acc = mfma_f32(va[s], vb[s], acc);
 #pragma unroll
       for (int t = 0; t < 4; ++t) out[(16 * ta + 4 * lk + t) * K + 16 * tb + lr] = acc[t];
     }
@@ -277,9 +284,21 @@ __global__ __launch_bounds__(256) void lr_rq_kernel(const IN* __restrict__ a,
   }
   __syncthreads();
   const float* T = red1;
-  for (int idx = threadIdx.x; idx < kTile * K; idx += blockDim.x) {
-    const int r = idx / K, j = idx % K;
-    if (row0 + r < n) P[((size_t)b * n + row0 + r) * K + j] = T[r * LD + j];
+  // P rows of the tile: 4 consecutive entries per lane and pass, all LDS reads
+  // of the lane before its stores
+  constexpr int kPIt = kTile * K / 4 / 256;
+  static_assert(kTile * K % (4 * 256) == 0, "P tile must split evenly over the block");
+  f32x4 pv[kPIt];
+#pragma unroll
+  for (int it = 0; it < kPIt; ++it) {
+    const int q = it * 256 + (int)threadIdx.x, r = (4 * q) / K, j = (4 * q) % K;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pv[it][t] = T[r * LD + j + t];
+  }
+#pragma unroll
+  for (int it = 0; it < kPIt; ++it) {
+    const int q = it * 256 + (int)threadIdx.x, r = (4 * q) / K, j = (4 * q) % K;
+    if (row0 + r < n) *reinterpret_cast<f32x4*>(P + ((size_t)b * n + row0 + r) * K + j) = pv[it];
   }
   tile_gram<K, LD>(T, gpart + ((size_t)b * ntiles + tile) * K * K, 4);
 }
