@@ -49,3 +49,16 @@ def test_profile_freshness_is_per_kernel_source(tmp_path, monkeypatch):
     assert bench._fresh_profile("p.json", "nm_compress_kernel<unsigned short,") is not None
     assert bench._fresh_profile("p.json", "unknown_kernel") is None
     assert bench._fresh_profile("missing.json", q) is None
+
+
+def test_more_than_one_gpu_is_refused_before_touching_a_gpu():
+    """The path has no inter-GPU step: --gpus N > 1 (or a launcher's
+    WORLD_SIZE > 1) ends with exit status 2 and a message, before any GPU or
+    library call."""
+    import subprocess
+    import sys
+    for args, env in ((["--gpus", "2"], {}), (["--gpus", "1"], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True,
+                           text=True, timeout=120, env=dict(os.environ, **env))
+        assert r.returncode == 2, (args, r.returncode, r.stderr[-500:])
+        assert "one GPU" in r.stderr and r.stdout == ""
